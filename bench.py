@@ -1,0 +1,233 @@
+"""Benchmark of the TC layer hot path on one MI355X.
+
+Headline (the JSON line's "value"): prefill tokens/s of tc_forward on the
+training-shape workload B=8 H=8 D=64 T=1024 W=256 C=64 bf16 (B*T tokens per
+call, inputs resident in HBM).  The same line carries the decode rate of the
+serving workload (64 streams x 32 heads, D=128, W=4096: tc_decode_step calls
+per second), the long-context prefill and the backward, each with its
+roofline, plus the CPU oracle timed on the host.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--legs prefill,decode,long,backward]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2500.0  # TFLOP/s, MI355X dense bf16 MFMA
+PEAK_HBM = 8000.0   # GB/s, MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fwd_flops(B, H, T, D, W, C):
+    """Algorithmic forward FLOPs: band QK^T+PV (4D per pair) plus the memory
+    write (2D^2), read (2D^2) and intra-chunk triangle (2D(C+1)) per evicted
+    query."""
+    P = W * (W + 1) // 2 + (T - W) * W if T >= W else T * (T + 1) // 2
+    E = max(T - W, 0)
+    return B * H * (4 * D * P + E * (4 * D * D + 2 * D * (C + 1)))
+
+
+def fwd_bytes(B, H, T, D, e_in=2, e_out=2):
+    return B * H * (T * D * (3 * e_in + e_out) + 4 * D * D + 4 * T)
+
+
+def bwd_flops(B, H, T, D, W, C):
+    P = W * (W + 1) // 2 + (T - W) * W if T >= W else T * (T + 1) // 2
+    E = max(T - W, 0)
+    return B * H * (10 * D * P + E * (10 * D * D + 4 * D * (C + 1)))
+
+
+def decode_bytes(S, H, D, W, e=2):
+    return S * H * (2 * W * D * e + 2 * D * e + 8 * D * D + 4 * D * e)
+
+
+def time_calls(fn, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(steps):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per call
+
+
+def prefill_leg(cfg_id, steps, warmup):
+    import torch
+
+    import eviction_fed_weight_amd as tc
+    import tc_inputs
+
+    cfg = tc_inputs.CONFIGS[cfg_id]
+    d = tc_inputs.prefill_inputs(cfg_id)
+    dv = torch.device("cuda")
+    q, k, v = (torch.from_numpy(d[x]).to(dv).to(torch.bfloat16).contiguous() for x in ("q", "k", "v"))
+    lam, eta, g = (torch.from_numpy(d[x]).to(dv) for x in ("lam", "eta", "gate"))
+    y = torch.empty_like(q)
+    A = torch.empty((cfg.B, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dv)
+    lse = torch.empty((cfg.B, cfg.H, cfg.T), dtype=torch.float32, device=dv)
+    shape = tc.make_shape(cfg.B, cfg.H, cfg.T, cfg.D, cfg.W, cfg.C)
+    ws = torch.empty(max(tc.tc_forward_workspace_size(shape), 1), dtype=torch.uint8, device=dv)
+
+    def call():
+        tc.tc_forward(q, k, v, lam, eta, g, cfg.W, cfg.C, y=y, A_final=A, lse=lse, ws=ws)
+
+    ms = time_calls(call, steps, warmup)
+    fl = fwd_flops(cfg.B, cfg.H, cfg.T, cfg.D, cfg.W, cfg.C)
+    by = fwd_bytes(cfg.B, cfg.H, cfg.T, cfg.D)
+    tflops = fl / (ms * 1e-3) / 1e12
+    return dict(
+        workload="prefill B=%d H=%d D=%d T=%d W=%d C=%d bf16" % (cfg.B, cfg.H, cfg.D, cfg.T, cfg.W, cfg.C),
+        ms_per_call=ms, tokens_per_s=cfg.B * cfg.T / (ms * 1e-3), flops=fl, bytes=by,
+        roofline=dict(bound="mfma", achieved=tflops, peak=PEAK_BF16, unit="TFLOP/s", frac=tflops / PEAK_BF16,
+                      traffic=None, kernel="tc_forward (seg_state + seg_chain + fwd kernels)"),
+        hbm_gbs=by / (ms * 1e-3) / 1e9,
+    )
+
+
+def decode_leg(steps, warmup):
+    """Serving decode: 64 streams x 32 heads, D=128, W=4096.  The start state
+    (ring of the last 4,096 pairs, A after 8,192 prior evictions) is built on
+    the device from seeded draws, A with the library's own forward pass."""
+    import torch
+
+    import eviction_fed_weight_amd as tc
+    import tc_inputs
+
+    cfg = tc_inputs.CONFIGS[4]
+    S, H, D, W = cfg.S, cfg.H, cfg.D, cfg.W
+    dv = torch.device("cuda")
+    lam, eta, g = (torch.from_numpy(x).to(dv) for x in tc_inputs.decode_params(4, H))
+    gen = torch.Generator(device=dv)
+    gen.manual_seed(4)
+    bf = torch.bfloat16
+    # A after `prior` evictions = the state tc_forward reaches with W=1 over prior+1 tokens
+    pk = torch.randn((S, H, cfg.prior + 1, D), generator=gen, device=dv).to(bf)
+    pv = torch.randn((S, H, cfg.prior + 1, D), generator=gen, device=dv).to(bf)
+    pq = torch.zeros_like(pk)
+    _, A, _ = tc.tc_forward(pq.view(S, H, -1, D), pk, pv, lam, eta, g, 1, 64, want_lse=False)
+    del pk, pv, pq
+    kr = torch.randn((S, H, W, D), generator=gen, device=dv).to(bf)
+    vr = torch.randn((S, H, W, D), generator=gen, device=dv).to(bf)
+    n = cfg.steps
+    qs = torch.randn((n, S, H, D), generator=gen, device=dv).to(bf)
+    ks = torch.randn((n, S, H, D), generator=gen, device=dv).to(bf)
+    vs = torch.randn((n, S, H, D), generator=gen, device=dv).to(bf)
+    pos = torch.full((S,), cfg.prior + W, dtype=torch.int64, device=dv)
+    y = torch.empty((S, H, D), dtype=bf, device=dv)
+    kr0, vr0, A0 = kr.clone(), vr.clone(), A.clone()
+    for i in range(min(warmup, n)):
+        tc.tc_decode_step(qs[i], ks[i], vs[i], kr, vr, A, pos, lam, eta, g, y=y)
+    torch.cuda.synchronize()
+    kr.copy_(kr0)
+    vr.copy_(vr0)
+    A.copy_(A0)
+    pos.fill_(cfg.prior + W)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(n):
+        tc.tc_decode_step(qs[i], ks[i], vs[i], kr, vr, A, pos, lam, eta, g, y=y)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    by = decode_bytes(S, H, D, W)
+    gbs = by / (ms * 1e-3) / 1e9
+    return dict(workload="decode S=%d H=%d D=%d W=%d bf16, %d consecutive steps" % (S, H, D, W, n),
+                ms_per_step=ms, steps_per_s=1e3 / ms, tokens_per_s=S * 1e3 / ms, bytes=by,
+                roofline=dict(bound="hbm", achieved=gbs, peak=PEAK_HBM, unit="GB/s", frac=gbs / PEAK_HBM,
+                              traffic=None, kernel="decode_kernel + pos_advance_kernel"))
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle (unmodified) on the prefill workload, on the host cores."""
+    import numpy as np
+
+    import oracle
+    import tc_inputs
+
+    cfg = tc_inputs.CONFIGS[2]
+    d = tc_inputs.prefill_inputs(2)
+    times = []
+    t_start = time.time()
+    while time.time() - t_start < budget_s and len(times) < 40:
+        t = time.time()
+        oracle.forward(d["q"], d["k"], d["v"], d["lam"], d["eta"], d["gate"], cfg.W)
+        times.append(time.time() - t)
+    sec = float(np.median(times))
+    return dict(value=cfg.B * cfg.T / sec, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample="full prefill batch (B=8 H=8 T=1024 W=256 D=64), float64 per-token recurrence, "
+                       "median of %d runs" % len(times), seconds_per_batch=sec)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--legs", default="prefill,decode,long")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the TC hot path has no multi-GPU mode in this build "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    legs = args.legs.split(",")
+    log("prefill leg ...")
+    pre = prefill_leg(2, args.steps, args.warmup)
+    log("  prefill", json.dumps(pre))
+    out = {
+        "metric": "TC-layer prefill tokens/s (training-shape prefill, tc_forward)",
+        "value": pre["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms_per_call"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": pre["workload"], "B": 8, "H": 8, "D": 64, "T": 1024, "W": 256, "C": 64},
+        "roofline": pre["roofline"],
+    }
+    if "decode" in legs:
+        log("decode leg ...")
+        dec = decode_leg(args.steps, args.warmup)
+        log("  decode", json.dumps(dec))
+        out["decode"] = dec
+    if "long" in legs:
+        log("long prefill leg ...")
+        lp = prefill_leg(3, max(3, args.steps // 5), 2)
+        log("  long", json.dumps(lp))
+        out["long_prefill"] = lp
+    if not args.no_cpu:
+        log("cpu baseline ...")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+"""Python binding of the TC C ABI (include/tc.h) -- argument marshalling only.
+
+Every step of the layer runs in the HIP kernels of ``libtc.so``; this module
+only checks tensor metadata, allocates outputs/workspaces with torch (device
+memory plumbing) and passes raw device pointers plus the current HIP stream.
+If the library has not been built it raises; there is no fallback.
+
+Entry points mirror the C names: ``tc_forward``, ``tc_decode_step``,
+``tc_backward``, ``tc_forward_workspace_size``, ``tc_backward_workspace_size``,
+``tc_status_string``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtc.so")
+
+TC_OK, TC_ERR_INVALID_ARGUMENT, TC_ERR_UNSUPPORTED, TC_ERR_WORKSPACE, TC_ERR_HIP = range(5)
+TC_F32, TC_BF16 = 0, 1
+
+
+class TCError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s failed: %s (status %d)" % (what, tc_status_string(status), status))
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("W", ctypes.c_int32), ("C", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class DecodeShape(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("W", ctypes.c_int32), ("scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtc.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libtc.so is not built (run: python -m eviction_fed_weight_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.tc_forward_workspace_size.argtypes = [ctypes.POINTER(Shape)]
+        L.tc_forward_workspace_size.restype = _sz
+        L.tc_backward_workspace_size.argtypes = [ctypes.POINTER(Shape)]
+        L.tc_backward_workspace_size.restype = _sz
+        L.tc_forward.argtypes = [ctypes.POINTER(Shape)] + [_vp] * 10 + [_sz, _vp]
+        L.tc_forward.restype = ctypes.c_int
+        L.tc_decode_step.argtypes = [ctypes.POINTER(DecodeShape)] + [_vp] * 12
+        L.tc_decode_step.restype = ctypes.c_int
+        L.tc_backward.argtypes = [ctypes.POINTER(Shape)] + [_vp] * 16 + [_sz, _vp]
+        L.tc_backward.restype = ctypes.c_int
+        L.tc_status_string.argtypes = [ctypes.c_int]
+        L.tc_status_string.restype = ctypes.c_char_p
+        L.tc_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def tc_status_string(status: int) -> str:
+    return lib().tc_status_string(int(status)).decode()
+
+
+def tc_version() -> str:
+    return lib().tc_version().decode()
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return TC_BF16
+    if t.dtype == torch.float32:
+        return TC_F32
+    raise TypeError("q/k/v must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device=None):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def make_shape(B, H, T, D, W, C=64, scale=0.0, dtype=TC_BF16) -> Shape:
+    return Shape(int(B), int(H), int(T), int(D), int(W), int(C), float(scale), int(dtype))
+
+
+def tc_forward_workspace_size(shape: Shape) -> int:
+    return int(lib().tc_forward_workspace_size(ctypes.byref(shape)))
+
+
+def tc_backward_workspace_size(shape: Shape) -> int:
+    return int(lib().tc_backward_workspace_size(ctypes.byref(shape)))
+
+
+def _workspace(nbytes, device, ws):
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError("workspace too small: %d < %d bytes" % (ws.numel() * ws.element_size(), nbytes))
+    return ws, ws.numel() * ws.element_size()
+
+
+def tc_forward(q, k, v, lam, eta, gate, W: int, C: int = 64, scale: float = 0.0, *,
+               want_state: bool = True, want_lse: bool = True, y=None, A_final=None, lse=None,
+               ws=None):
+    """Prefill/training forward.  q, k, v: [B,H,T,D] (bf16 or fp32, CUDA);
+    lam, eta, gate: [H] float32.  Returns (y, A_final or None, lse or None)."""
+    torch = _torch()
+    B, H, T, D = q.shape
+    shape = make_shape(B, H, T, D, W, C, scale, _dtype_code(q))
+    dev = q.device
+    if y is None:
+        y = torch.empty_like(q)
+    if want_state and A_final is None:
+        A_final = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(tc_forward_workspace_size(shape), dev, ws)
+    st = lib().tc_forward(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(eta),
+                          _ptr(gate), _ptr(y), _ptr(A_final) if want_state else None,
+                          _ptr(lse) if want_lse else None, _ptr(ws) if ws is not None else None,
+                          wsb, _stream(dev))
+    if st != TC_OK:
+        raise TCError(st, "tc_forward")
+    return y, (A_final if want_state else None), (lse if want_lse else None)
+
+
+def tc_decode_step(q, k, v, k_ring, v_ring, A, pos, lam, eta, gate, scale: float = 0.0, *, y=None):
+    """One decode step for S streams.  q, k, v: [S,H,D]; rings [S,H,W,D]
+    (updated in place); A [S,H,D,D] float32 (in place); pos [S] int64 (+1).
+    Returns y [S,H,D]."""
+    torch = _torch()
+    S, H, D = q.shape
+    W = k_ring.shape[2]
+    shape = DecodeShape(S, H, D, W, float(scale), _dtype_code(q))
+    if y is None:
+        y = torch.empty_like(q)
+    st = lib().tc_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(k_ring),
+                              _ptr(v_ring), _ptr(A), _ptr(pos), _ptr(lam), _ptr(eta), _ptr(gate),
+                              _ptr(y), _stream(q.device))
+    if st != TC_OK:
+        raise TCError(st, "tc_decode_step")
+    return y
+
+
+def tc_backward(q, k, v, y, dy, lse, lam, eta, gate, W: int, C: int = 64, scale: float = 0.0, *,
+                dq=None, dk=None, dv=None, ws=None):
+    """Gradients of sum <dy, y>.  Returns dq, dk, dv, dlam, deta, dgate."""
+    torch = _torch()
+    B, H, T, D = q.shape
+    shape = make_shape(B, H, T, D, W, C, scale, _dtype_code(q))
+    dev = q.device
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    dl = torch.empty(H, dtype=torch.float32, device=dev)
+    de = torch.empty(H, dtype=torch.float32, device=dev)
+    dg = torch.empty(H, dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(tc_backward_workspace_size(shape), dev, ws)
+    st = lib().tc_backward(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(dy),
+                           _ptr(lse), _ptr(lam), _ptr(eta), _ptr(gate), _ptr(dq), _ptr(dk), _ptr(dv),
+                           _ptr(dl), _ptr(de), _ptr(dg), _ptr(ws) if ws is not None else None, wsb,
+                           _stream(dev))
+    if st != TC_OK:
+        raise TCError(st, "tc_backward")
+    return dq, dk, dv, dl, de, dg

@@ -1,0 +1,206 @@
+// C ABI of the TC layer: host-side validation, workspace planning and
+// dispatch to the gfx950 kernels.  No allocation, no synchronisation, no
+// global mutable state.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/tc.h"
+#include "tc_launch.h"
+
+namespace {
+
+constexpr int kBlock = 64;  // query rows per block = tokens per scan chunk
+
+bool supported_d(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
+
+size_t elem_size(int32_t dtype) { return dtype == TC_BF16 ? 2 : 4; }
+
+bool valid_dtype(int32_t dtype) { return dtype == TC_F32 || dtype == TC_BF16; }
+
+// Byte ranges [p, p + n) overlap?
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+struct Plan {
+  int nblk, G, nseg;
+  size_t state_bytes;  // one [BH][nseg][D*D] float block
+};
+
+// Blocks per segment: enough segments to give ~1024 workgroups, few enough
+// that the chain over segments stays short.
+Plan plan_for(const tc_shape_t& s) {
+  Plan p;
+  const long long BH = (long long)s.B * s.H;
+  p.nblk = (s.T + kBlock - 1) / kBlock;
+  long long G = (BH * p.nblk + 1023) / 1024;
+  if (G < 1) G = 1;
+  if (G > p.nblk) G = p.nblk;
+  p.G = (int)G;
+  p.nseg = (p.nblk + p.G - 1) / p.G;
+  p.state_bytes = (size_t)BH * p.nseg * s.D * s.D * sizeof(float);
+  return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+tc_status_t check_shape(const tc_shape_t* s) {
+  if (!s) return TC_ERR_INVALID_ARGUMENT;
+  if (s->B < 1 || s->H < 1 || s->T < 1 || s->W < 1 || s->C < 1 || s->D < 1)
+    return TC_ERR_INVALID_ARGUMENT;
+  if (!valid_dtype(s->dtype)) return TC_ERR_UNSUPPORTED;
+  if (!supported_d(s->D)) return TC_ERR_UNSUPPORTED;
+  if (!(s->scale == s->scale)) return TC_ERR_INVALID_ARGUMENT;  // NaN scale
+  // index arithmetic is 32-bit inside a (b,h) sequence and 64-bit across
+  if ((long long)s->T * s->D > (1LL << 31) - 1) return TC_ERR_UNSUPPORTED;
+  if ((long long)s->B * s->H > (1LL << 24)) return TC_ERR_UNSUPPORTED;
+  return TC_OK;
+}
+
+float scale_of(float scale, int D) { return scale > 0.0f ? scale : 1.0f / sqrtf((float)D); }
+
+}  // namespace
+
+extern "C" {
+
+const char* tc_status_string(tc_status_t st) {
+  switch (st) {
+    case TC_OK: return "ok";
+    case TC_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case TC_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case TC_ERR_WORKSPACE: return "workspace missing or too small";
+    case TC_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* tc_version(void) { return "0.1.0"; }
+
+size_t tc_forward_workspace_size(const tc_shape_t* s) {
+  if (check_shape(s) != TC_OK) return 0;
+  return align256(plan_for(*s).state_bytes);
+}
+
+tc_status_t tc_forward(const tc_shape_t* s, const void* q, const void* k, const void* v,
+                       const float* lambda, const float* eta, const float* gate, void* y,
+                       float* A_final, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const tc_status_t st = check_shape(s);
+  if (st != TC_OK) return st;
+  if (!q || !k || !v || !lambda || !eta || !gate || !y) return TC_ERR_INVALID_ARGUMENT;
+  const size_t n = (size_t)s->B * s->H * s->T * s->D * elem_size(s->dtype);
+  const size_t na = A_final ? (size_t)s->B * s->H * s->D * s->D * 4 : 0;
+  const size_t nl = lse ? (size_t)s->B * s->H * s->T * 4 : 0;
+  const size_t nh = (size_t)s->H * 4;
+  const void* ins[6] = {q, k, v, lambda, eta, gate};
+  const size_t insz[6] = {n, n, n, nh, nh, nh};
+  void* outs[3] = {y, A_final, lse};
+  const size_t outsz[3] = {n, na, nl};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 6; ++i)
+      if (overlap(outs[o], outsz[o], ins[i], insz[i])) return TC_ERR_INVALID_ARGUMENT;
+    for (int p = o + 1; p < 3; ++p)
+      if (overlap(outs[o], outsz[o], outs[p], outsz[p])) return TC_ERR_INVALID_ARGUMENT;
+  }
+  const Plan p = plan_for(*s);
+  const size_t need = align256(p.state_bytes);
+  if (p.nseg > 1 && (!ws || ws_bytes < need)) return TC_ERR_WORKSPACE;
+  if (ws && ws_bytes >= need) {
+    for (int o = 0; o < 3; ++o)
+      if (overlap(ws, need, outs[o], outsz[o])) return TC_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i < 6; ++i)
+      if (overlap(ws, need, ins[i], insz[i])) return TC_ERR_INVALID_ARGUMENT;
+  }
+  tck::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.lam = lambda;
+  a.eta = eta;
+  a.gate = gate;
+  a.y = y;
+  a.A_final = A_final;
+  a.lse = lse;
+  a.seg_state = (float*)ws;
+  a.B = s->B;
+  a.H = s->H;
+  a.T = s->T;
+  a.W = s->W;
+  a.nblk = p.nblk;
+  a.G = p.G;
+  a.nseg = p.nseg;
+  a.scale = scale_of(s->scale, s->D);
+  const hipError_t e = tck::launch_forward(a, s->D, s->dtype == TC_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? TC_OK : TC_ERR_HIP;
+}
+
+tc_status_t tc_decode_step(const tc_decode_shape_t* s, const void* q, const void* k, const void* v,
+                           void* k_ring, void* v_ring, float* A, int64_t* pos, const float* lambda,
+                           const float* eta, const float* gate, void* y, void* stream) {
+  if (!s) return TC_ERR_INVALID_ARGUMENT;
+  if (s->S < 1 || s->H < 1 || s->W < 1 || s->D < 1) return TC_ERR_INVALID_ARGUMENT;
+  if (!valid_dtype(s->dtype) || !supported_d(s->D)) return TC_ERR_UNSUPPORTED;
+  if (!(s->scale == s->scale)) return TC_ERR_INVALID_ARGUMENT;
+  if ((long long)s->S * s->H > (1LL << 30)) return TC_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !k_ring || !v_ring || !A || !pos || !lambda || !eta || !gate || !y)
+    return TC_ERR_INVALID_ARGUMENT;
+  const size_t es = elem_size(s->dtype);
+  const size_t nt = (size_t)s->S * s->H * s->D * es;
+  const size_t nr = (size_t)s->S * s->H * s->W * s->D * es;
+  const size_t na = (size_t)s->S * s->H * s->D * s->D * 4;
+  const size_t np = (size_t)s->S * 8;
+  const size_t nh = (size_t)s->H * 4;
+  const void* ins[6] = {q, k, v, lambda, eta, gate};
+  const size_t insz[6] = {nt, nt, nt, nh, nh, nh};
+  void* outs[5] = {k_ring, v_ring, A, pos, y};
+  const size_t outsz[5] = {nr, nr, na, np, nt};
+  for (int o = 0; o < 5; ++o) {
+    for (int i = 0; i < 6; ++i)
+      if (overlap(outs[o], outsz[o], ins[i], insz[i])) return TC_ERR_INVALID_ARGUMENT;
+    for (int p = o + 1; p < 5; ++p)
+      if (overlap(outs[o], outsz[o], outs[p], outsz[p])) return TC_ERR_INVALID_ARGUMENT;
+  }
+  tck::DecArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.k_ring = k_ring;
+  a.v_ring = v_ring;
+  a.A = A;
+  a.pos = pos;
+  a.lam = lambda;
+  a.eta = eta;
+  a.gate = gate;
+  a.y = y;
+  a.S = s->S;
+  a.H = s->H;
+  a.W = s->W;
+  a.scale = scale_of(s->scale, s->D);
+  const hipError_t e = tck::launch_decode(a, s->D, s->dtype == TC_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? TC_OK : TC_ERR_HIP;
+}
+
+size_t tc_backward_workspace_size(const tc_shape_t* s) {
+  if (check_shape(s) != TC_OK) return 0;
+  return 0;
+}
+
+tc_status_t tc_backward(const tc_shape_t* s, const void* q, const void* k, const void* v,
+                        const void* y, const void* dy, const float* lse, const float* lambda,
+                        const float* eta, const float* gate, void* dq, void* dk, void* dv,
+                        float* dlambda, float* deta, float* dgate, void* ws, size_t ws_bytes,
+                        void* stream) {
+  (void)q; (void)k; (void)v; (void)y; (void)dy; (void)lse; (void)lambda; (void)eta; (void)gate;
+  (void)dq; (void)dk; (void)dv; (void)dlambda; (void)deta; (void)dgate; (void)ws; (void)ws_bytes;
+  (void)stream;
+  const tc_status_t st = check_shape(s);
+  if (st != TC_OK) return st;
+  if (!q || !k || !v || !y || !dy || !lse || !lambda || !eta || !gate || !dq || !dk || !dv ||
+      !dlambda || !deta || !dgate)
+    return TC_ERR_INVALID_ARGUMENT;
+  return TC_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Internal kernel-argument blocks and launchers (host side of the kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tck {
+
+// Forward: segment walk over 64-row query blocks.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* lam;
+  const float* eta;
+  const float* gate;
+  void* y;
+  float* A_final;  // nullable
+  float* lse;      // nullable
+  float* seg_state;  // [B*H][nseg][D*D] segment-start states (eta factored out)
+  int B, H, T, W;
+  int nblk;  // ceil(T / 64)
+  int G;     // blocks per segment
+  int nseg;  // ceil(nblk / G)
+  float scale;
+};
+
+// Decode: one step for S streams x H heads.
+struct DecArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* k_ring;
+  void* v_ring;
+  float* A;
+  int64_t* pos;
+  const float* lam;
+  const float* eta;
+  const float* gate;
+  void* y;
+  int S, H, W;
+  float scale;
+};
+
+// Backward (see tc_backward.hip for the workspace plan).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* y;
+  const void* dy;
+  const float* lse;
+  const float* lam;
+  const float* eta;
+  const float* gate;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dlam;
+  float* deta;
+  float* dgate;
+  float* fstate;   // forward segment states  [BH][nseg][D*D]  (S, eta-free)
+  float* tstate;   // forward tangent states  [BH][nseg][D*D]  (dS/dlambda)
+  float* rstate;   // reverse adjoint states  [BH][nseg][D*D]
+  float* delta;    // [BH][T] rowwise <dy, y_local>
+  float* part;     // [BH][nblk][4] per-block partial sums (dlam, eta*deta_free, <dy,m>)
+  int B, H, T, W;
+  int nblk, G, nseg;
+  float scale;
+};
+
+hipError_t launch_forward(const FwdArgs& a, int D, bool is_bf16, hipStream_t s);
+hipError_t launch_decode(const DecArgs& a, int D, bool is_bf16, hipStream_t s);
+hipError_t launch_backward(const BwdArgs& a, int D, bool is_bf16, hipStream_t s);
+
+}  // namespace tck

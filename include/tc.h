@@ -1,0 +1,149 @@
+/*
+ * tc.h -- C ABI of the Tensor Cache (TC) layer on AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the one described in "Tensor Cache: Eviction-conditioned
+ * Associative Memory for Transformers" (Swain, Han, Weidele, Martino,
+ * Torralba, 2026):
+ *   L1 (Section 3.1, Eq. 1): exact causal softmax attention of q_t over the W
+ *       most recent keys/values, i.e. keys max(0, t-W+1) .. t.
+ *   L2 (Section 3.2, Figure 2 step 3): a per-head D x D matrix A, A_0 = 0,
+ *       written only when a pair leaves the window:
+ *       A_t = lambda_h * A_{t-1} + eta_h * k_{t-W} (outer) v_{t-W}   (t >= W)
+ *       A[a][c] accumulates k[a]*v[c].
+ *   Read + fuse (Figure 2 step 5): m_t = q_t A_t (no normaliser),
+ *       y_t = y_local,t + sigmoid(g_h) * m_t.
+ *   Prefill/training computes A with the exact parallel weighted-sum scan of
+ *   the abstract (equal to per-token writes up to float rounding), never the
+ *   chunk-mean shortcut.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major and contiguous.
+ *     The caller owns every buffer; the library allocates nothing.
+ *   - q, k, v, y, dy, dq, dk, dv and the rings share the element type
+ *     `dtype` (TC_F32 or TC_BF16).  lambda, eta, gate, A, lse and the
+ *     parameter gradients are float32.  pos is int64.
+ *   - Arithmetic is float32 (bf16 operands on the matrix cores, float32
+ *     accumulation, float32 softmax and state); bf16 outputs are rounded to
+ *     nearest even.
+ *   - Supported head dims: D in {16, 32, 64, 128}; anything else returns
+ *     TC_ERR_UNSUPPORTED.  Any T >= 1, W >= 1, C >= 1.
+ *   - Device-side preconditions that are NOT checked (checking would need a
+ *     synchronisation): lambda in [0,1], eta >= 0, finite inputs, pos >= 0.
+ *     NaN/Inf inputs propagate to the outputs.
+ *   - All argument checks run on the host before any HIP call; a failed check
+ *     returns TC_ERR_INVALID_ARGUMENT / TC_ERR_UNSUPPORTED / TC_ERR_WORKSPACE
+ *     and writes nothing.  A failed kernel launch returns TC_ERR_HIP.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Nothing synchronises.  The library keeps no global
+ *     mutable state; calls on different streams with disjoint buffers may run
+ *     concurrently.  Results are deterministic (no floating-point atomics).
+ */
+#ifndef TC_H_
+#define TC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TC_OK = 0,
+  TC_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, aliased output */
+  TC_ERR_UNSUPPORTED = 2,      /* head dim or dtype not built */
+  TC_ERR_WORKSPACE = 3,        /* workspace missing or too small */
+  TC_ERR_HIP = 4               /* a HIP launch failed */
+} tc_status_t;
+
+typedef enum { TC_F32 = 0, TC_BF16 = 1 } tc_dtype_t;
+
+/* Prefill / training shapes.  scale <= 0 selects 1/sqrt(D) (the standard
+ * scaled dot product; the pages do not state the scale).  C is the chunk
+ * length of the weighted-sum scan; exact results do not depend on it (only
+ * float rounding does), and the GPU path tiles the scan in 64-token chunks
+ * for every C. */
+typedef struct {
+  int32_t B, H, T, D, W, C;
+  float scale;
+  int32_t dtype; /* tc_dtype_t */
+} tc_shape_t;
+
+/* Decode shapes: S independent streams of H heads, ring of W slots. */
+typedef struct {
+  int32_t S, H, D, W;
+  float scale;
+  int32_t dtype; /* tc_dtype_t */
+} tc_decode_shape_t;
+
+/* Bytes of device workspace tc_forward / tc_backward need for `shape`
+ * (0 if the shape is invalid).  The workspace holds the eviction-state
+ * checkpoints of the scan and, for the backward, per-row and per-block
+ * partial sums; its contents on entry are ignored. */
+size_t tc_forward_workspace_size(const tc_shape_t* shape);
+size_t tc_backward_workspace_size(const tc_shape_t* shape);
+
+/*
+ * tc_forward -- prefill / training forward (Section 3.1 Eq. 1, Section 3.2,
+ * Figure 2; the scan of the abstract).
+ *   q, k, v  [B,H,T,D] dtype, post-RoPE (RoPE, if any, is applied by the
+ *            caller before the keys enter the window, Section 3.1).
+ *   lambda, eta, gate [H] float32: per-head decay, write rate, gate logit.
+ *   y        [B,H,T,D] dtype, out.
+ *   A_final  [B,H,D,D] float32, out, nullable: A after step T-1 (the state a
+ *            decode continuing at position T starts from).
+ *   lse      [B,H,T] float32, out, nullable: natural-log softmax normaliser
+ *            of the scaled window scores (needed by tc_backward).
+ *   ws       device workspace of at least tc_forward_workspace_size bytes.
+ * Outputs must not overlap the inputs or each other.
+ */
+tc_status_t tc_forward(const tc_shape_t* shape, const void* q, const void* k, const void* v,
+                       const float* lambda, const float* eta, const float* gate, void* y,
+                       float* A_final, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tc_decode_step -- one streaming step (Figure 2, steps 1-5) for S streams.
+ *   q, k, v  [S,H,D] dtype: the incoming token of every (stream, head).
+ *   k_ring, v_ring [S,H,W,D] dtype, in/out: token t lives in slot t mod W.
+ *   A        [S,H,D,D] float32, in/out: the eviction memory.
+ *   pos      [S] int64, in/out: index of the incoming token of each stream;
+ *            incremented by one.
+ * With t = pos[s], slot = t mod W, per head: if t >= W the pair in the slot
+ * is evicted and written, A <- lambda*A + eta*k_e v_e^T; the new pair takes
+ * the slot; y = softmax over the min(t+1, W) resident pairs + sigmoid(g)*q A.
+ *   y        [S,H,D] dtype, out.
+ * Rings, A and pos are updated in place, so successive calls need no host
+ * work between them (the sequence can be captured in a HIP graph).
+ */
+tc_status_t tc_decode_step(const tc_decode_shape_t* shape, const void* q, const void* k,
+                           const void* v, void* k_ring, void* v_ring, float* A, int64_t* pos,
+                           const float* lambda, const float* eta, const float* gate, void* y,
+                           void* stream);
+
+/*
+ * tc_backward -- gradients of L = sum_t <dy_t, y_t> through both levels and
+ * the scan (the abstract: decay, write rate and gate are trained end to end).
+ *   q, k, v, y, dy [B,H,T,D] dtype: forward inputs, forward output, upstream
+ *            gradient.
+ *   lse      [B,H,T] float32: from tc_forward.
+ *   dq, dk, dv [B,H,T,D] dtype, out.
+ *   dlambda, deta, dgate [H] float32, out (overwritten): summed over B and T.
+ *   ws       device workspace of at least tc_backward_workspace_size bytes.
+ */
+tc_status_t tc_backward(const tc_shape_t* shape, const void* q, const void* k, const void* v,
+                        const void* y, const void* dy, const float* lse, const float* lambda,
+                        const float* eta, const float* gate, void* dq, void* dk, void* dv,
+                        float* dlambda, float* deta, float* dgate, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Static description of a status code. */
+const char* tc_status_string(tc_status_t status);
+
+/* Library version, e.g. "0.1.0". */
+const char* tc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TC_H_ */

@@ -1,0 +1,115 @@
+"""C-ABI contract on the CPU: the library loads without a GPU, exports every
+symbol include/tc.h declares, and rejects bad arguments on the host before
+any HIP call (so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import eviction_fed_weight_amd as tc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "tc.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tc_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"tc_forward", "tc_decode_step", "tc_backward", "tc_forward_workspace_size",
+            "tc_backward_workspace_size", "tc_status_string", "tc_version"} <= set(names)
+    L = tc.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for s in range(5):
+        assert tc.tc_status_string(s)
+    assert tc.tc_status_string(99) == "unknown status"
+
+
+def fwd(shape, **kw):
+    args = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, lam=FAKE + 0x300000,
+                eta=FAKE + 0x300100, gate=FAKE + 0x300200, y=FAKE + 0x400000, A=None, lse=None,
+                ws=None, wsb=0)
+    args.update(kw)
+    return tc.lib().tc_forward(ctypes.byref(shape), args["q"], args["k"], args["v"], args["lam"],
+                               args["eta"], args["gate"], args["y"], args["A"], args["lse"],
+                               args["ws"], args["wsb"], None)
+
+
+def test_forward_validation():
+    ok = tc.make_shape(1, 1, 64, 64, 8, 8)
+    assert fwd(tc.make_shape(1, 1, 64, 48, 8, 8)) == tc.TC_ERR_UNSUPPORTED
+    assert fwd(tc.make_shape(1, 1, 64, 64, 8, 8, dtype=7)) == tc.TC_ERR_UNSUPPORTED
+    for bad in [tc.make_shape(0, 1, 64, 64, 8, 8), tc.make_shape(1, 1, 0, 64, 8, 8),
+                tc.make_shape(1, 1, 64, 64, 0, 8), tc.make_shape(1, 1, 64, 64, 8, 0),
+                tc.make_shape(1, 0, 64, 64, 8, 8)]:
+        assert fwd(bad) == tc.TC_ERR_INVALID_ARGUMENT
+    assert fwd(ok, q=None) == tc.TC_ERR_INVALID_ARGUMENT
+    assert fwd(ok, y=None) == tc.TC_ERR_INVALID_ARGUMENT
+    assert fwd(ok, gate=None) == tc.TC_ERR_INVALID_ARGUMENT
+    # output aliasing an input
+    assert fwd(ok, y=FAKE) == tc.TC_ERR_INVALID_ARGUMENT
+    assert fwd(ok, lse=FAKE + 0x100010) == tc.TC_ERR_INVALID_ARGUMENT
+    assert tc.lib().tc_forward(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 0,
+                               None) == tc.TC_ERR_INVALID_ARGUMENT
+    # multi-segment shape without a workspace
+    big = tc.make_shape(4, 16, 8192, 128, 512, 64)
+    need = tc.tc_forward_workspace_size(big)
+    assert need > 0
+    G = 1 << 32  # spacing so the fake buffers do not overlap
+    far = dict(q=G, k=2 * G, v=3 * G, lam=4 * G, eta=4 * G + 256, gate=4 * G + 512, y=5 * G)
+    assert fwd(big, **far) == tc.TC_ERR_WORKSPACE
+    assert fwd(big, ws=6 * G, wsb=need - 1, **far) == tc.TC_ERR_WORKSPACE
+    assert fwd(big, ws=5 * G + 4096, wsb=need, **far) == tc.TC_ERR_INVALID_ARGUMENT  # ws overlaps y
+
+
+def test_workspace_sizes():
+    assert tc.tc_forward_workspace_size(tc.make_shape(1, 1, 64, 48, 8, 8)) == 0
+    s2 = tc.make_shape(8, 8, 1024, 64, 256, 64)
+    assert tc.tc_forward_workspace_size(s2) % 256 == 0
+    assert tc.tc_forward_workspace_size(s2) >= 64 * 64 * 4
+
+
+def test_decode_validation():
+    L = tc.lib()
+
+    def call(shape, **kw):
+        p = dict(q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, kr=FAKE + 0x100000, vr=FAKE + 0x200000,
+                 A=FAKE + 0x300000, pos=FAKE + 0x400000, lam=FAKE + 0x500000, eta=FAKE + 0x500100,
+                 gate=FAKE + 0x500200, y=FAKE + 0x600000)
+        p.update(kw)
+        return L.tc_decode_step(ctypes.byref(shape), p["q"], p["k"], p["v"], p["kr"], p["vr"],
+                                p["A"], p["pos"], p["lam"], p["eta"], p["gate"], p["y"], None)
+
+    assert call(tc.DecodeShape(1, 1, 48, 8, 0.0, 1)) == tc.TC_ERR_UNSUPPORTED
+    assert call(tc.DecodeShape(0, 1, 64, 8, 0.0, 1)) == tc.TC_ERR_INVALID_ARGUMENT
+    assert call(tc.DecodeShape(1, 1, 64, 0, 0.0, 1)) == tc.TC_ERR_INVALID_ARGUMENT
+    assert call(tc.DecodeShape(1, 1, 64, 8, 0.0, 1), pos=None) == tc.TC_ERR_INVALID_ARGUMENT
+    assert call(tc.DecodeShape(1, 1, 64, 8, 0.0, 1), y=FAKE) == tc.TC_ERR_INVALID_ARGUMENT
+    assert call(tc.DecodeShape(1, 1, 64, 8, 0.0, 1), A=FAKE + 0x100000 + 64) == tc.TC_ERR_INVALID_ARGUMENT
+
+
+def test_backward_validation():
+    L = tc.lib()
+    s = tc.make_shape(1, 1, 64, 48, 8, 8)
+    args = [FAKE + i * 0x100000 for i in range(15)]
+    assert L.tc_backward(ctypes.byref(s), *args, None, 0, None) == tc.TC_ERR_UNSUPPORTED
+    s = tc.make_shape(1, 1, 64, 64, 8, 8)
+    args2 = list(args)
+    args2[0] = None
+    assert L.tc_backward(ctypes.byref(s), *args2, None, 0, None) == tc.TC_ERR_INVALID_ARGUMENT
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 8, 16)
+    with pytest.raises(ValueError):
+        tc.tc_forward(q, q, q, torch.zeros(1), torch.zeros(1), torch.zeros(1), 4)

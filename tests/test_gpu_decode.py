@@ -1,0 +1,107 @@
+"""GPU parity of tc_decode_step (through the C ABI) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tc_inputs
+from gpu_util import TOL, dev, host, rel, say
+
+pytestmark = pytest.mark.gpu
+
+
+def tc():
+    import eviction_fed_weight_amd as m
+
+    return m
+
+
+@pytest.mark.parametrize("S,H,D,W,steps,dtype", [
+    (3, 2, 16, 5, 13, "f32"),
+    (2, 2, 64, 64, 80, "bf16"),
+    (2, 3, 128, 100, 130, "bf16"),
+    (1, 2, 32, 1, 4, "f32"),
+    (2, 1, 128, 40, 45, "f32"),
+])
+def test_decode_from_empty(S, H, D, W, steps, dtype):
+    """Streaming from an empty ring: warm-up (pos < W), the first evictions,
+    and wrap-around of the ring."""
+    say("decode", S, H, D, W, steps, dtype)
+    rng = np.random.default_rng(S * 100 + D + W)
+    toks = [tc_inputs.bf16_round(rng.standard_normal((steps, S, H, D)).astype(np.float32))
+            if dtype == "bf16" else rng.standard_normal((steps, S, H, D)).astype(np.float32)
+            for _ in range(3)]
+    lam, eta, g = tc_inputs.head_params(rng, rng, rng, H)
+    kr = torch.zeros((S, H, W, D), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+                     device="cuda")
+    vr = torch.zeros_like(kr)
+    A = torch.zeros((S, H, D, D), dtype=torch.float32, device="cuda")
+    pos = torch.zeros(S, dtype=torch.int64, device="cuda")
+    okr = np.zeros((S, H, W, D))
+    ovr = np.zeros((S, H, W, D))
+    oA = np.zeros((S, H, D, D))
+    opos = np.zeros(S, np.int64)
+    L, E, G = dev(lam), dev(eta), dev(g)
+    worst = 0.0
+    for t in range(steps):
+        q, k, v = (dev(x[t], dtype) for x in toks)
+        y = tc().tc_decode_step(q, k, v, kr, vr, A, pos, L, E, G)
+        yo = oracle.decode_step(toks[0][t], toks[1][t], toks[2][t], okr, ovr, oA, opos, lam, eta, g)
+        e = rel(host(y), yo)
+        worst = max(worst, e)
+        assert e <= TOL[dtype], (t, e)
+    torch.cuda.synchronize()
+    say("  worst y", worst, "A", rel(host(A), oA))
+    assert rel(host(A), oA) <= TOL[dtype]
+    assert np.array_equal(host(kr), okr) and np.array_equal(host(vr), ovr)
+    assert np.array_equal(pos.cpu().numpy(), opos)
+
+
+def test_decode_config4_full_launch_sampled_streams():
+    """Full serving shape (64 streams x 32 heads, D=128, W=4096, bf16 ring
+    fully populated, A from 8,192 prior evictions); streams 0 and 41 carry
+    exact seeded data checked against the oracle over 3 steps."""
+    cfg = tc_inputs.CONFIGS[4]
+    S, H, D, W = cfg.S, cfg.H, cfg.D, cfg.W
+    lam, eta, g = tc_inputs.decode_params(4, H)
+    steps = 3
+    say("decode config 4 full launch")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    kr = torch.randn((S, H, W, D), generator=gen, device="cuda").to(torch.bfloat16)
+    vr = torch.randn((S, H, W, D), generator=gen, device="cuda").to(torch.bfloat16)
+    A = torch.randn((S, H, D, D), generator=gen, device="cuda") * 0.1
+    q = torch.randn((steps, S, H, D), generator=gen, device="cuda").to(torch.bfloat16)
+    k = torch.randn((steps, S, H, D), generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn((steps, S, H, D), generator=gen, device="cuda").to(torch.bfloat16)
+    pos = torch.full((S,), cfg.prior + W, dtype=torch.int64, device="cuda")
+    sampled = [0, 41]
+    ref = {}
+    for s in sampled:
+        di = tc_inputs.decode_stream_inputs(4, s, H, D, W, cfg.prior, steps)
+        A0 = oracle.dense.state_after_writes(di["prior_k"], di["prior_v"], lam, eta)
+        A0 = A0.astype(np.float32).astype(np.float64)
+        kr[s] = dev(di["ring_k"], "bf16")
+        vr[s] = dev(di["ring_v"], "bf16")
+        A[s] = dev(A0, "f32")
+        q[:, s] = dev(di["q"], "bf16")
+        k[:, s] = dev(di["k"], "bf16")
+        v[:, s] = dev(di["v"], "bf16")
+        ref[s] = dict(kr=di["ring_k"][None].astype(np.float64).copy(), vr=di["ring_v"][None].astype(np.float64).copy(),
+                      A=A0[None].copy(), pos=np.array([cfg.prior + W], np.int64), q=di["q"], k=di["k"], v=di["v"])
+    L, E, G = dev(lam), dev(eta), dev(g)
+    for t in range(steps):
+        y = tc().tc_decode_step(q[t].contiguous(), k[t].contiguous(), v[t].contiguous(), kr, vr, A, pos, L, E, G)
+        yh = host(y)
+        for s in sampled:
+            r = ref[s]
+            yo = oracle.decode_step(r["q"][t][None], r["k"][t][None], r["v"][t][None], r["kr"], r["vr"], r["A"],
+                                    r["pos"], lam, eta, g)
+            e = rel(yh[s:s + 1], yo)
+            say("  step", t, "stream", s, "y err", e)
+            assert e <= TOL["bf16"]
+    torch.cuda.synchronize()
+    for s in sampled:
+        assert rel(host(A[s:s + 1]), ref[s]["A"]) <= TOL["bf16"]
+        assert np.array_equal(host(kr[s:s + 1]), ref[s]["kr"])
+    assert torch.all(pos == cfg.prior + W + steps)

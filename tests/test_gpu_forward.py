@@ -1,0 +1,152 @@
+"""GPU parity of tc_forward (through the C ABI) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tc_inputs
+from gpu_util import TOL, dev, host, rel, say
+
+pytestmark = pytest.mark.gpu
+
+
+def tc():
+    import eviction_fed_weight_amd as m
+
+    return m
+
+
+def run_and_compare(d, W, C=64, heads=None, check_state=True):
+    """Run the GPU forward on all of d, compare (optionally a subset of heads
+    (b, h) list) against the oracle.  Returns the error dict."""
+    dtype = d["dtype"]
+    q, k, v = (dev(d[x], dtype) for x in ("q", "k", "v"))
+    lam, eta, g = (dev(d[x], "f32") for x in ("lam", "eta", "gate"))
+    y, A, lse = tc().tc_forward(q, k, v, lam, eta, g, W, C)
+    torch.cuda.synchronize()
+    y, A, lse = host(y), host(A), host(lse)
+    if heads is None:
+        yo, Ao, lo = oracle.forward(d["q"], d["k"], d["v"], d["lam"], d["eta"], d["gate"], W)
+        err = dict(y=rel(y, yo), A=rel(A, Ao), lse=rel(lse, lo))
+    else:
+        errs = []
+        for b, h in heads:
+            sl = lambda x: x[b:b + 1, h:h + 1]  # noqa: E731
+            yo, Ao, lo = oracle.forward(sl(d["q"]), sl(d["k"]), sl(d["v"]), d["lam"][h:h + 1],
+                                        d["eta"][h:h + 1], d["gate"][h:h + 1], W)
+            errs.append((rel(sl(y), yo), rel(sl(A), Ao), rel(sl(lse), lo)))
+        e = np.max(np.array(errs), axis=0)
+        err = dict(y=e[0], A=e[1], lse=e[2])
+    if not check_state:
+        err.pop("A")
+    return err
+
+
+SMALL = [
+    # B, H, T, D, W, dtype
+    (1, 1, 64, 16, 8, "f32"),
+    (2, 3, 200, 16, 8, "f32"),
+    (1, 2, 333, 32, 64, "f32"),
+    (2, 2, 300, 64, 100, "f32"),
+    (1, 2, 257, 128, 64, "f32"),
+    (2, 3, 200, 16, 8, "bf16"),
+    (1, 2, 333, 32, 64, "bf16"),
+    (2, 2, 500, 64, 100, "bf16"),
+    (2, 2, 512, 64, 256, "bf16"),
+    (1, 2, 449, 128, 128, "bf16"),
+    (1, 1, 1, 64, 1, "bf16"),
+    (1, 1, 5, 16, 1, "f32"),
+    (1, 2, 100, 64, 1, "bf16"),
+    (1, 2, 130, 64, 200, "bf16"),   # W > T: pure causal softmax, A = 0
+    (1, 1, 64, 64, 64, "bf16"),     # W = T
+    (1, 2, 65, 16, 64, "f32"),      # one eviction
+]
+
+
+@pytest.mark.parametrize("B,H,T,D,W,dtype", SMALL)
+def test_forward_small(B, H, T, D, W, dtype):
+    say("forward", B, H, T, D, W, dtype)
+    d = tc_inputs.prefill_inputs(2, seed=17 + T + D, B=B, H=H, T=T, D=D, W=W, dtype=dtype, plants=False)
+    err = run_and_compare(d, W)
+    say("  errors", err)
+    for key, e in err.items():
+        assert e <= TOL[dtype], (key, e)
+
+
+@pytest.mark.parametrize("lam,eta,gate", [(0.0, 0.5, 0.3), (1.0, 0.25, -0.5), (0.9, 0.0, 0.0),
+                                          (0.95, 0.7, -60.0), (0.5, 2.0, 3.0)])
+def test_forward_parameter_edges(lam, eta, gate):
+    say("forward edges", lam, eta, gate)
+    d = tc_inputs.prefill_inputs(2, seed=5, B=1, H=2, T=300, D=64, W=70, dtype="f32", plants=False)
+    d["lam"][:] = lam
+    d["eta"][:] = eta
+    d["gate"][:] = gate
+    err = run_and_compare(d, 70)
+    say("  errors", err)
+    for key, e in err.items():
+        assert e <= TOL["f32"], (key, e)
+
+
+def test_forward_multi_segment_walk():
+    """Enough blocks that workgroups walk several blocks and segment-start
+    states come from the per-segment pass and the chain."""
+    say("forward multi-segment")
+    d = tc_inputs.prefill_inputs(2, seed=3, B=1, H=2, T=64 * 520 + 17, D=16, W=100, dtype="f32",
+                                 plants=False)
+    err = run_and_compare(d, 100)
+    say("  errors", err)
+    for key, e in err.items():
+        assert e <= TOL["f32"], (key, e)
+
+
+def test_forward_multi_segment_walk_bf16():
+    say("forward multi-segment bf16")
+    d = tc_inputs.prefill_inputs(2, seed=4, B=2, H=4, T=64 * 140, D=64, W=320, dtype="bf16",
+                                 plants=False)
+    err = run_and_compare(d, 320, heads=[(0, 0), (1, 3)])
+    say("  errors", err)
+    for key, e in err.items():
+        assert e <= TOL["bf16"], (key, e)
+
+
+def test_forward_config1_tiny_fp32():
+    d = tc_inputs.prefill_inputs(1)
+    err = run_and_compare(d, 8, C=8)
+    say("config 1", err)
+    for key, e in err.items():
+        assert e <= TOL["f32"], (key, e)
+
+
+def test_forward_config2_full():
+    d = tc_inputs.prefill_inputs(2)
+    err = run_and_compare(d, 256, C=64)
+    say("config 2", err)
+    for key, e in err.items():
+        assert e <= TOL["bf16"], (key, e)
+
+
+def test_forward_config3_sampled_heads():
+    """Full 32,768-token, 12-head launch; the oracle checks two whole heads."""
+    d = tc_inputs.prefill_inputs(3)
+    err = run_and_compare(d, 1024, C=128, heads=[(0, 0), (0, 7)])
+    say("config 3", err)
+    for key, e in err.items():
+        assert e <= TOL["bf16"], (key, e)
+
+
+def test_forward_config5_sampled_heads():
+    d = tc_inputs.prefill_inputs(5, with_dy=False)
+    err = run_and_compare(d, 512, C=64, heads=[(0, 0), (3, 15)])
+    say("config 5 forward", err)
+    for key, e in err.items():
+        assert e <= TOL["bf16"], (key, e)
+
+
+def test_forward_deterministic():
+    d = tc_inputs.prefill_inputs(2, seed=9, B=2, H=4, T=640, D=64, W=192, plants=False)
+    q, k, v = (dev(d[x], "bf16") for x in ("q", "k", "v"))
+    lam, eta, g = (dev(d[x], "f32") for x in ("lam", "eta", "gate"))
+    outs = [tc().tc_forward(q, k, v, lam, eta, g, 192) for _ in range(3)]
+    for o in outs[1:]:
+        for a, b in zip(o, outs[0]):
+            assert torch.equal(a, b)
