@@ -136,6 +136,95 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Column fragment: rows 0..7 of `blk` (row stride ld elements) at column l16,
+// i.e. the 8 contraction values a matrix-core operand needs when the
+// contraction runs down the rows of a row-major LDS tile.  For bf16 this is
+// two gfx950 transpose reads (ds_read_b64_tr_b16): within each group of 16
+// lanes, lane i addresses row i/4, columns 4*(i%4)..+3 of a 4 x 16 block and
+// lane n receives column n of the four rows.
+template <class E>
+struct ColFrag;
+
+template <>
+struct ColFrag<bf16> {
+  static __device__ __forceinline__ bf16x8 read(const bf16* blk, int ld, int l16) {
+    const bf16* p0 = blk + (l16 >> 2) * ld + 4 * (l16 & 3);
+    const bf16* p1 = p0 + 4 * ld;
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p1));
+    bf16x8 r;
+    const bf16* ea = (const bf16*)&a;
+    const bf16* eb = (const bf16*)&b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r[j] = ea[j];
+      r[j + 4] = eb[j];
+    }
+    return r;
+  }
+};
+
+template <>
+struct ColFrag<float> {
+  static __device__ __forceinline__ f32x8 read(const float* blk, int ld, int l16) {
+    f32x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = blk[j * ld + l16];
+    return r;
+  }
+};
+
+// Buffer resource over `bytes` bytes at p: buffer loads at byte offsets
+// outside [0, bytes) return zero, so tile loads need no per-lane branches
+// (rows before the sequence start or past its end read as zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const v4i x = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)byte_off, 0, 0);
+  return uint4{(uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]};
+}
+
+// Unrolled copy of NR rows of a row-major [T][D] matrix: load() issues every
+// global load of the tile at once (through a buffer resource covering the
+// sequence, so out-of-range rows read as zero) so they can be in flight while
+// the previous tile is computed; store() writes the registers to a row-major
+// LDS tile with leading dimension ld.
+template <class E, int D, int NR>
+struct TileRegs {
+  static constexpr int VE = 16 / (int)sizeof(E);
+  static constexpr int VPR = D / VE;
+  static constexpr int NV = NR * VPR;
+  static constexpr int PER = (NV + 255) / 256;
+  uint4 v[PER];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int r0) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int x = (int)threadIdx.x + 256 * p;
+      const int row = x / VPR;
+      const int col = (x - row * VPR) * VE;
+      int off = ((r0 + row) * D + col) * (int)sizeof(E);
+      if (NV % 256 != 0 && x >= NV) off = -16;  // out of range: reads zero
+      v[p] = buf_load16(rs, off);
+    }
+  }
+  __device__ __forceinline__ void store(E* lds, int ld) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int x = (int)threadIdx.x + 256 * p;
+      const int row = x / VPR;
+      const int col = (x - row * VPR) * VE;
+      if (NV % 256 == 0 || x < NV) *(uint4*)(lds + row * ld + col) = v[p];
+    }
+  }
+};
+
 // 16-byte vector of elements.
 template <class E>
 struct Vec16 {

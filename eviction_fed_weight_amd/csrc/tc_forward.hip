@@ -24,21 +24,19 @@
 
 namespace tck {
 
-// LDS plan of the fused forward kernel (bytes).  X (float rows x D) aliases
-// the K/V tiles: it is only live between the band loop and the chunk load.
+// LDS plan of the fused forward kernel (elements / bytes).  K and V tiles
+// are stored row-major; operands that contract down their rows are read with
+// transpose reads (ColFrag).  X (float rows x D) aliases the K/V tiles: it is
+// only live between the band loop and the store of the evicted chunk.
 template <class E, int D>
 struct FwdLds {
   static constexpr int VE = 16 / sizeof(E);
-  static constexpr int LDK = D + VE;   // row-major tiles: K, Q
-  static constexpr int LDT = 64 + VE;  // transposed tiles: V^T, K^T
+  static constexpr int LDK = D + VE;  // row stride of K, V, Q tiles
   static constexpr int LDX = D + 4;
-  static constexpr int KS = 64 * LDK * (int)sizeof(E);
-  static constexpr int VT = D * LDT * (int)sizeof(E);
+  static constexpr int TILE = 64 * LDK * (int)sizeof(E);
   static constexpr int XB = 64 * LDX * 4;
-  static constexpr int U = (KS + VT) > XB ? (KS + VT) : XB;
-  static constexpr int KT = VT;
-  static constexpr int QS = KS;
-  static constexpr int TOTAL = U + KT + QS;
+  static constexpr int U = (2 * TILE) > XB ? (2 * TILE) : XB;
+  static constexpr int TOTAL = U + TILE;  // + Q block
 };
 
 // S[o][at] holds rows a = 16*at + 4*lg + i, column c = 16*(wid + 4*o) + l16.
@@ -49,14 +47,14 @@ struct State {
   f32x4 s[NOWN][NT];
 };
 
-// S <- lambda^len S + sum_{c<len, e0+c>=0} lambda^(len-1-c) K^T[:,c] V[c,:]
-// with K^T and V^T of the chunk in LDS (ld = LDT).
+// S <- lambda^len S + sum_{c<len, e0+c>=0} lambda^(len-1-c) K[c,:]^T V[c,:]
+// with the chunk's K and V row-major in LDS (row stride LDK).
 template <class E, int D>
-__device__ __forceinline__ void state_update(State<E, D>& st, const E* Kt, const E* Vt, const float* pw,
+__device__ __forceinline__ void state_update(State<E, D>& st, const E* Ks, const E* Vs, const float* pw,
                                              int len, int e0, int wid, int l16, int lg) {
   using M = Mfma<E>;
   using frag = typename M::frag;
-  constexpr int NT = D / 16, NOWN = State<E, D>::NOWN, LDT = FwdLds<E, D>::LDT;
+  constexpr int NT = D / 16, NOWN = State<E, D>::NOWN, LDK = FwdLds<E, D>::LDK;
   const float decay = pw[len];
 #pragma unroll
   for (int o = 0; o < NOWN; ++o) {
@@ -69,7 +67,7 @@ __device__ __forceinline__ void state_update(State<E, D>& st, const E* Kt, const
         float wv[8];
         {
           float vv[8];
-          M::to_f32(M::lds8(Vt + (ct * 16 + l16) * LDT + kc * 32 + lg * 8), vv);
+          M::to_f32(ColFrag<E>::read(Vs + (kc * 32 + lg * 8) * LDK + ct * 16, LDK, l16), vv);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int c = kc * 32 + lg * 8 + j;
@@ -81,7 +79,7 @@ __device__ __forceinline__ void state_update(State<E, D>& st, const E* Kt, const
         M::split(wv, bhi, blo);
 #pragma unroll
         for (int at = 0; at < NT; ++at) {
-          const frag a = M::lds8(Kt + (at * 16 + l16) * LDT + kc * 32 + lg * 8);
+          const frag a = ColFrag<E>::read(Ks + (kc * 32 + lg * 8) * LDK + at * 16, LDK, l16);
           st.s[o][at] = M::mma(a, bhi, st.s[o][at]);
           if (M::kSplit) st.s[o][at] = M::mma(a, blo, st.s[o][at]);
         }
@@ -131,41 +129,80 @@ __device__ __forceinline__ void state_store(const State<E, D>& st, float* g, flo
   }
 }
 
+// Fragment made of two runs of four consecutive LDS elements (the second
+// run replaced by zeros when !second).
+template <class E>
+__device__ __forceinline__ typename Mfma<E>::frag lds4x2(const E* p0, const E* p1, bool second);
+template <>
+__device__ __forceinline__ bf16x8 lds4x2<bf16>(const bf16* p0, const bf16* p1, bool second) {
+  const bf16x4 a = *(const bf16x4*)p0;
+  bf16x4 b = *(const bf16x4*)p1;
+  if (!second) b = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+template <>
+__device__ __forceinline__ f32x8 lds4x2<float>(const float* p0, const float* p1, bool second) {
+  const f32x4 a = *(const f32x4*)p0;
+  f32x4 b = *(const f32x4*)p1;
+  if (!second) b = f32x4{0.f, 0.f, 0.f, 0.f};
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Store four consecutive outputs of one row.
+__device__ __forceinline__ void store4(bf16* dst, f32x4 x) {
+  bf16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (bf16)x[i];
+  *(bf16x4*)dst = r;
+}
+__device__ __forceinline__ void store4(float* dst, f32x4 x) { *(f32x4*)dst = x; }
+
 // ---------------------------------------------------------------------------
 // Per-segment local states: L_m = S over the evictions of segment m, from 0.
 // grid = BH * (nseg - 1); writes ws[bh][m + 1].
 template <class E, int D>
-__global__ void __launch_bounds__(256) seg_state_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
   using L = FwdLds<E, D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::VT];
+  __shared__ __attribute__((aligned(16))) char smem[2 * L::TILE];
   __shared__ float pw[72];
-  E* Kt = (E*)smem;
-  E* Vt = (E*)(smem + L::VT);
+  E* Ks = (E*)smem;
+  E* Vs = (E*)(smem + L::TILE);
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int nm = a.nseg - 1;
   const int bh = blockIdx.x / nm, m = blockIdx.x - bh * nm;
   const int h = bh % a.H;
   const size_t base = (size_t)bh * a.T * D;
-  const E* Kg = (const E*)a.k + base;
-  const E* Vg = (const E*)a.v + base;
+  const uint32_t nbytes = (uint32_t)a.T * D * sizeof(E);
+  const auto Kg = make_rsrc((const E*)a.k + base, nbytes);
+  const auto Vg = make_rsrc((const E*)a.v + base, nbytes);
   if (tid <= 64) pw[tid] = powi(a.lam[h], tid);
   State<E, D> st;
   state_zero(st);
-  for (int g = 0; g < a.G; ++g) {
-    const int jj = m * a.G + g;
-    const int e0 = jj * 64 - a.W;
-    if (e0 + 63 < 0) continue;
+  TileRegs<E, D, 64> kl, vl;
+  int g0 = 0;
+  while (g0 < a.G && (m * a.G + g0) * 64 - a.W + 63 < 0) ++g0;
+  if (g0 < a.G) {
+    kl.load(Kg, (m * a.G + g0) * 64 - a.W);
+    vl.load(Vg, (m * a.G + g0) * 64 - a.W);
+  }
+  for (int g = g0; g < a.G; ++g) {
+    const int e0 = (m * a.G + g) * 64 - a.W;
     __syncthreads();
-    stage_rows<E, D, 64, false, true>(Kg, e0, a.T, nullptr, 0, Kt, L::LDT);
-    stage_rows<E, D, 64, false, true>(Vg, e0, a.T, nullptr, 0, Vt, L::LDT);
+    kl.store(Ks, L::LDK);
+    vl.store(Vs, L::LDK);
     __syncthreads();
-    state_update(st, Kt, Vt, pw, 64, e0, wid, l16, lg);
+    if (g + 1 < a.G) {
+      kl.load(Kg, e0 + 64);
+      vl.load(Vg, e0 + 64);
+    }
+    state_update(st, Ks, Vs, pw, 64, e0, wid, l16, lg);
   }
   state_store(st, a.seg_state + ((size_t)bh * a.nseg + m + 1) * D * D, 1.0f, wid, l16, lg);
 }
 
 // Chain over segments, in place: ws[0] = 0, ws[m+1] = lambda^(64G) ws[m] + L_m.
-// grid = (D*D/4 + 255)/256 x BH; each thread owns four consecutive floats.
+// grid = (D*D/4 + 255)/256 x BH; each thread owns four consecutive floats and
+// loads eight segments ahead of the dependent chain.
 template <int D>
 __global__ void __launch_bounds__(256) seg_chain_kernel(FwdArgs a) {
   const int bh = blockIdx.y;
@@ -176,41 +213,48 @@ __global__ void __launch_bounds__(256) seg_chain_kernel(FwdArgs a) {
   const size_t stride = (size_t)D * D / 4;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   p[0] = s;
-  for (int m = 1; m < a.nseg; ++m) {
-    const float4 l = p[m * stride];
-    s.x = decay * s.x + l.x;
-    s.y = decay * s.y + l.y;
-    s.z = decay * s.z + l.z;
-    s.w = decay * s.w + l.w;
-    p[m * stride] = s;
+  for (int m0 = 1; m0 < a.nseg; m0 += 8) {
+    float4 l[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (m0 + u < a.nseg) l[u] = p[(m0 + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (m0 + u < a.nseg) {
+        s.x = decay * s.x + l[u].x;
+        s.y = decay * s.y + l[u].y;
+        s.z = decay * s.z + l[u].z;
+        s.w = decay * s.w + l[u].w;
+        p[(m0 + u) * stride] = s;
+      }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Fused forward: grid = BH * nseg, 256 threads (4 waves x 16 query rows).
 template <class E, int D>
-__global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a) {
   using M = Mfma<E>;
   using frag = typename M::frag;
   using L = FwdLds<E, D>;
   constexpr int NT = D / 16, NKC = (D + 31) / 32, NOWN = State<E, D>::NOWN;
-  constexpr int LDK = L::LDK, LDT = L::LDT, LDX = L::LDX;
+  constexpr int LDK = L::LDK, LDX = L::LDX;
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
   __shared__ float pw[72];
   E* Ks = (E*)smem;
-  E* Vt = (E*)(smem + L::KS);
+  E* Vs = (E*)(smem + L::TILE);
   float* X = (float*)smem;
-  E* Kt = (E*)(smem + L::U);
-  E* Qs = (E*)(smem + L::U + L::KT);
+  E* Qs = (E*)(smem + L::U);
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int bh = blockIdx.x / a.nseg, seg = blockIdx.x - bh * a.nseg;
   const int h = bh % a.H;
   const int T = a.T, W = a.W;
   const size_t base = (size_t)bh * T * D;
-  const E* Qg = (const E*)a.q + base;
-  const E* Kg = (const E*)a.k + base;
-  const E* Vg = (const E*)a.v + base;
+  const uint32_t nbytes = (uint32_t)T * D * sizeof(E);
+  const auto Qg = make_rsrc((const E*)a.q + base, nbytes);
+  const auto Kg = make_rsrc((const E*)a.k + base, nbytes);
+  const auto Vg = make_rsrc((const E*)a.v + base, nbytes);
   E* Yg = (E*)a.y + base;
   const float seta = sigmoidf(a.gate[h]) * a.eta[h];
   const float sl2 = a.scale * kLog2e;
@@ -225,11 +269,20 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
   const int jb = seg * a.G;
   const int je = min(a.nblk, jb + a.G);
   const int r = wid * 16 + l16;  // this lane's row within the block
+  TileRegs<E, D, 64> ql, kl, vl;
+  ql.load(Qg, jb * 64);
+  kl.load(Kg, (max(0, jb * 64 - W + 1) >> 6) * 64);
+  vl.load(Vg, (max(0, jb * 64 - W + 1) >> 6) * 64);
   for (int j = jb; j < je; ++j) {
     const int t0 = j * 64;
     const int trow = t0 + r;
+    const int e0 = t0 - W;
+    const bool has_mem = t0 + 63 >= W;
+    const bool more = j + 1 < je;
+    const int next_k0 = (max(0, t0 + 64 - W + 1) >> 6) * 64;
     __syncthreads();
-    stage_rows<E, D, 64, true, false>(Qg, t0, T, Qs, LDK, nullptr, 0);
+    ql.store(Qs, LDK);
+    ql.load(Qg, t0 + 64);  // next block's queries, in flight during this block
     __syncthreads();
     frag qf[NKC];
 #pragma unroll
@@ -242,14 +295,20 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
     for (int dt = 0; dt < NT; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // ---- L1: band tiles ----
-    const int klo = max(0, t0 - W + 1);
-    const int khi = min(T - 1, t0 + 63);
-    for (int kt = klo >> 6; kt <= (khi >> 6); ++kt) {
+    const int kt_lo = max(0, t0 - W + 1) >> 6;
+    const int kt_hi = min(T - 1, t0 + 63) >> 6;
+    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
       const int k0 = kt * 64;
+      if (kt > kt_lo) __syncthreads();
+      kl.store(Ks, LDK);
+      vl.store(Vs, LDK);
       __syncthreads();
-      stage_rows<E, D, 64, true, false>(Kg, k0, T, Ks, LDK, nullptr, 0);
-      stage_rows<E, D, 64, false, true>(Vg, k0, T, nullptr, 0, Vt, LDT);
-      __syncthreads();
+      {
+        // next tile of this block, else the evicted chunk, else the next block's first tile
+        const int nr = (kt < kt_hi) ? k0 + 64 : (has_mem ? e0 : next_k0);
+        kl.load(Kg, nr);
+        vl.load(Vg, nr);
+      }
       f32x4 Z[4];
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
@@ -262,27 +321,27 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
         }
       }
       const bool full = (k0 + 63 <= t0) && (k0 >= t0 + 64 - W);
-      float sv[16];
-      float mx = kNegInf;
+      float zv[16];
+      float mz = kNegInf;
 #pragma unroll
       for (int n = 0; n < 4; ++n)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = k0 + 32 * (n >> 1) + lg * 8 + (n & 1) * 4 + i;
-          float x = Z[n][i] * sl2;
-          if (!full && !(key <= trow && key > trow - W)) x = kNegInf;
-          sv[(n >> 1) * 8 + (n & 1) * 4 + i] = x;
-          mx = fmaxf(mx, x);
+          float z = Z[n][i];
+          if (!full && !(key <= trow && key > trow - W)) z = kNegInf;
+          zv[(n >> 1) * 8 + (n & 1) * 4 + i] = z;
+          mz = fmaxf(mz, z);
         }
-      mx = max4(mx);
-      const float mnew = fmaxf(mrow, mx);
+      mz = max4(mz);
+      const float mnew = fmaxf(mrow, mz * sl2);
       const float msafe = (mnew == kNegInf) ? 0.0f : mnew;
       const float alpha = exp2f(mrow - msafe);
       float ps = 0.0f;
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        sv[x] = exp2f(sv[x] - msafe);
-        ps += sv[x];
+        zv[x] = exp2f(__builtin_fmaf(zv[x], sl2, -msafe));
+        ps += zv[x];
       }
       ps = sum4(ps);
       lrow = lrow * alpha + ps;
@@ -293,11 +352,11 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
       for (int p = 0; p < 2; ++p) {
         float pv[8];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) pv[jj] = sv[p * 8 + jj];
+        for (int jj = 0; jj < 8; ++jj) pv[jj] = zv[p * 8 + jj];
         const frag pf = M::pack(pv);
 #pragma unroll
         for (int dt = 0; dt < NT; ++dt)
-          O[dt] = M::mma(M::lds8(Vt + (dt * 16 + l16) * LDT + p * 32 + lg * 8), pf, O[dt]);
+          O[dt] = M::mma(ColFrag<E>::read(Vs + (p * 32 + lg * 8) * LDK + dt * 16, LDK, l16), pf, O[dt]);
       }
     }
     {
@@ -308,12 +367,11 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
     }
 
     // ---- L2: read of the eviction state and the evicted chunk ----
-    const int e0 = t0 - W;
     const bool last = (j == a.nblk - 1);
-    if (t0 + 63 >= W) {
+    if (has_mem) {
+      __syncthreads();  // every wave is done with the last band tile
       if (e0 > 0) {
         // (QS)^T for this wave's state columns and all 64 rows -> X[row][c]
-        __syncthreads();
 #pragma unroll
         for (int o = 0; o < NOWN; ++o) {
           const int ct = wid + 4 * o;
@@ -333,14 +391,9 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
               M::split(sv8, shi, slo);
 #pragma unroll
               for (int rg = 0; rg < 4; ++rg) {
-                float qv[8];
                 const E* qrow = Qs + (rg * 16 + l16) * LDK;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  qv[i] = (float)qrow[32 * pp + lg * 4 + i];
-                  qv[4 + i] = (32 * pp + 16 < D) ? (float)qrow[(32 * pp + 16 + lg * 4 + i) % D] : 0.0f;
-                }
-                const frag qb = M::pack(qv);
+                const frag qb = lds4x2<E>(qrow + 32 * pp + lg * 4, qrow + (32 * pp + 16 + lg * 4) % D,
+                                          32 * pp + 16 < D);
                 acc[rg] = M::mma(shi, qb, acc[rg]);
                 if (M::kSplit) acc[rg] = M::mma(slo, qb, acc[rg]);
               }
@@ -357,12 +410,14 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
           const f32x4 xv = *(const f32x4*)(X + r * LDX + dt * 16 + lg * 4);
           O[dt] += f * xv;
         }
+        __syncthreads();
       }
-      // evicted chunk e0 .. e0+63: K (row-major and transposed), V^T
+      // evicted chunk e0 .. e0+63 (prefetched during the last band tile)
+      kl.store(Ks, LDK);
+      vl.store(Vs, LDK);
       __syncthreads();
-      stage_rows<E, D, 64, true, true>(Kg, e0, T, Ks, LDK, Kt, LDT);
-      stage_rows<E, D, 64, false, true>(Vg, e0, T, nullptr, 0, Vt, LDT);
-      __syncthreads();
+      kl.load(Kg, next_k0);
+      vl.load(Vg, next_k0);
       f32x4 Z[4];
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
@@ -386,27 +441,23 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
         const frag pf = M::pack(pv);
 #pragma unroll
         for (int dt = 0; dt < NT; ++dt)
-          O[dt] = M::mma(M::lds8(Vt + (dt * 16 + l16) * LDT + p * 32 + lg * 8), pf, O[dt]);
+          O[dt] = M::mma(ColFrag<E>::read(Vs + (p * 32 + lg * 8) * LDK + dt * 16, LDK, l16), pf, O[dt]);
       }
       // carry the state to the next block (or to step T-1 for A_final)
-      if (j + 1 < je) {
-        state_update(st, Kt, Vt, pw, 64, e0, wid, l16, lg);
+      if (more) {
+        state_update(st, Ks, Vs, pw, 64, e0, wid, l16, lg);
       } else if (last && a.A_final) {
-        state_update(st, Kt, Vt, pw, T - t0, e0, wid, l16, lg);
+        state_update(st, Ks, Vs, pw, T - t0, e0, wid, l16, lg);
       }
     }
     // ---- store y ----
     if (trow < T) {
 #pragma unroll
-      for (int dt = 0; dt < NT; ++dt) {
-        E* dst = Yg + (size_t)trow * D + dt * 16 + lg * 4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = (E)O[dt][i];
-      }
+      for (int dt = 0; dt < NT; ++dt) store4(Yg + (size_t)trow * D + dt * 16 + lg * 4, O[dt]);
     }
     if (last && a.A_final) {
       float* Af = a.A_final + (size_t)bh * D * D;
-      if (t0 + 63 >= W)
+      if (has_mem)
         state_store(st, Af, a.eta[h], wid, l16, lg);
       else
         for (int x = tid; x < D * D; x += 256) Af[x] = 0.0f;
