@@ -157,6 +157,36 @@ def decode_leg(steps, warmup):
                               traffic=None, kernel="decode_kernel + pos_advance_kernel"))
 
 
+def backward_leg(steps, warmup):
+    """Training backward B=4 H=16 D=128 T=8192 W=512: tc_backward per call
+    (the forward that produces y and lse runs once, outside the timing)."""
+    import torch
+
+    import eviction_fed_weight_amd as tc
+    import tc_inputs
+
+    cfg = tc_inputs.CONFIGS[5]
+    d = tc_inputs.prefill_inputs(5)
+    dv = torch.device("cuda")
+    q, k, v, dy = (torch.from_numpy(d[x]).to(dv).to(torch.bfloat16).contiguous() for x in ("q", "k", "v", "dy"))
+    lam, eta, g = (torch.from_numpy(d[x]).to(dv) for x in ("lam", "eta", "gate"))
+    y, _, lse = tc.tc_forward(q, k, v, lam, eta, g, cfg.W, cfg.C)
+    dq, dk, dvv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    shape = tc.make_shape(cfg.B, cfg.H, cfg.T, cfg.D, cfg.W, cfg.C)
+    ws = torch.empty(tc.tc_backward_workspace_size(shape), dtype=torch.uint8, device=dv)
+
+    def call():
+        tc.tc_backward(q, k, v, y, dy, lse, lam, eta, g, cfg.W, cfg.C, dq=dq, dk=dk, dv=dvv, ws=ws)
+
+    ms = time_calls(call, steps, warmup)
+    fl = bwd_flops(cfg.B, cfg.H, cfg.T, cfg.D, cfg.W, cfg.C)
+    tflops = fl / (ms * 1e-3) / 1e12
+    return dict(workload="backward B=%d H=%d D=%d T=%d W=%d C=%d bf16" % (cfg.B, cfg.H, cfg.D, cfg.T, cfg.W, cfg.C),
+                ms_per_call=ms, tokens_per_s=cfg.B * cfg.T / (ms * 1e-3), flops=fl,
+                roofline=dict(bound="mfma", achieved=tflops, peak=PEAK_BF16, unit="TFLOP/s", frac=tflops / PEAK_BF16,
+                              traffic=None, kernel="tc_backward (segment passes + dq + dkdv + reduce)"))
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle (unmodified) on the prefill workload, on the host cores."""
     import numpy as np
@@ -183,7 +213,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--legs", default="prefill,decode,long")
+    ap.add_argument("--legs", default="prefill,decode,long,backward")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -223,6 +253,11 @@ def main():
         lp = prefill_leg(3, max(3, args.steps // 5), 2)
         log("  long", json.dumps(lp))
         out["long_prefill"] = lp
+    if "backward" in legs:
+        log("backward leg ...")
+        bw = backward_leg(max(3, args.steps // 5), 2)
+        log("  backward", json.dumps(bw))
+        out["backward"] = bw
     if not args.no_cpu:
         log("cpu baseline ...")
         out["cpu_baseline"] = cpu_baseline()

@@ -55,7 +55,8 @@ tc_status_t check_shape(const tc_shape_t* s) {
   if (!supported_d(s->D)) return TC_ERR_UNSUPPORTED;
   if (!(s->scale == s->scale)) return TC_ERR_INVALID_ARGUMENT;  // NaN scale
   // index arithmetic is 32-bit inside a (b,h) sequence and 64-bit across
-  if ((long long)s->T * s->D > (1LL << 31) - 1) return TC_ERR_UNSUPPORTED;
+  if ((long long)(s->T + 128) * s->D * (long long)elem_size(s->dtype) > (1LL << 31) - 1)
+    return TC_ERR_UNSUPPORTED;
   if ((long long)s->B * s->H > (1LL << 24)) return TC_ERR_UNSUPPORTED;
   return TC_OK;
 }
@@ -182,9 +183,33 @@ tc_status_t tc_decode_step(const tc_decode_shape_t* s, const void* q, const void
   return e == hipSuccess ? TC_OK : TC_ERR_HIP;
 }
 
+struct BwdPlan {
+  int nblk, G, nseg;
+  size_t off_f, off_t, off_r, off_delta, off_part, total;
+};
+
+BwdPlan bwd_plan_for(const tc_shape_t& s) {
+  BwdPlan p;
+  const long long BH = (long long)s.B * s.H;
+  p.nblk = (s.T + kBlock - 1) / kBlock;
+  long long G = (BH * p.nblk + 511) / 512;
+  if (G < 1) G = 1;
+  if (G > p.nblk) G = p.nblk;
+  p.G = (int)G;
+  p.nseg = (p.nblk + p.G - 1) / p.G;
+  const size_t st = align256((size_t)BH * p.nseg * s.D * s.D * sizeof(float));
+  p.off_f = 0;
+  p.off_t = p.off_f + st;
+  p.off_r = p.off_t + st;
+  p.off_delta = p.off_r + st;
+  p.off_part = p.off_delta + align256((size_t)BH * s.T * sizeof(float));
+  p.total = p.off_part + align256((size_t)BH * p.nseg * 2 * sizeof(float));
+  return p;
+}
+
 size_t tc_backward_workspace_size(const tc_shape_t* s) {
   if (check_shape(s) != TC_OK) return 0;
-  return 0;
+  return bwd_plan_for(*s).total;
 }
 
 tc_status_t tc_backward(const tc_shape_t* s, const void* q, const void* k, const void* v,
@@ -192,15 +217,58 @@ tc_status_t tc_backward(const tc_shape_t* s, const void* q, const void* k, const
                         const float* eta, const float* gate, void* dq, void* dk, void* dv,
                         float* dlambda, float* deta, float* dgate, void* ws, size_t ws_bytes,
                         void* stream) {
-  (void)q; (void)k; (void)v; (void)y; (void)dy; (void)lse; (void)lambda; (void)eta; (void)gate;
-  (void)dq; (void)dk; (void)dv; (void)dlambda; (void)deta; (void)dgate; (void)ws; (void)ws_bytes;
-  (void)stream;
   const tc_status_t st = check_shape(s);
   if (st != TC_OK) return st;
   if (!q || !k || !v || !y || !dy || !lse || !lambda || !eta || !gate || !dq || !dk || !dv ||
       !dlambda || !deta || !dgate)
     return TC_ERR_INVALID_ARGUMENT;
-  return TC_ERR_UNSUPPORTED;
+  const BwdPlan p = bwd_plan_for(*s);
+  if (!ws || ws_bytes < p.total) return TC_ERR_WORKSPACE;
+  const size_t n = (size_t)s->B * s->H * s->T * s->D * elem_size(s->dtype);
+  const size_t nl = (size_t)s->B * s->H * s->T * 4;
+  const size_t nh = (size_t)s->H * 4;
+  const void* ins[9] = {q, k, v, y, dy, lse, lambda, eta, gate};
+  const size_t insz[9] = {n, n, n, n, n, nl, nh, nh, nh};
+  void* outs[7] = {dq, dk, dv, dlambda, deta, dgate, ws};
+  const size_t outsz[7] = {n, n, n, nh, nh, nh, p.total};
+  for (int o = 0; o < 7; ++o) {
+    for (int i = 0; i < 9; ++i)
+      if (overlap(outs[o], outsz[o], ins[i], insz[i])) return TC_ERR_INVALID_ARGUMENT;
+    for (int q2 = o + 1; q2 < 7; ++q2)
+      if (overlap(outs[o], outsz[o], outs[q2], outsz[q2])) return TC_ERR_INVALID_ARGUMENT;
+  }
+  char* w = (char*)ws;
+  tck::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.y = y;
+  a.dy = dy;
+  a.lse = lse;
+  a.lam = lambda;
+  a.eta = eta;
+  a.gate = gate;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dlam = dlambda;
+  a.deta = deta;
+  a.dgate = dgate;
+  a.fstate = (float*)(w + p.off_f);
+  a.tstate = (float*)(w + p.off_t);
+  a.rstate = (float*)(w + p.off_r);
+  a.delta = (float*)(w + p.off_delta);
+  a.part = (float*)(w + p.off_part);
+  a.B = s->B;
+  a.H = s->H;
+  a.T = s->T;
+  a.W = s->W;
+  a.nblk = p.nblk;
+  a.G = p.G;
+  a.nseg = p.nseg;
+  a.scale = scale_of(s->scale, s->D);
+  const hipError_t e = tck::launch_backward(a, s->D, s->dtype == TC_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? TC_OK : TC_ERR_HIP;
 }
 
 }  // extern "C"

@@ -63,7 +63,7 @@ struct BwdArgs {
   float* tstate;   // forward tangent states  [BH][nseg][D*D]  (dS/dlambda)
   float* rstate;   // reverse adjoint states  [BH][nseg][D*D]
   float* delta;    // [BH][T] rowwise <dy, y_local>
-  float* part;     // [BH][nblk][4] per-block partial sums (dlam, eta*deta_free, <dy,m>)
+  float* part;     // [BH][nseg][2] per-workgroup sums of <dy, mt> and <dy, d mt/dlambda>
   int B, H, T, W;
   int nblk, G, nseg;
   float scale;
