@@ -4,7 +4,8 @@
 
 Each HIP source is compiled to an object in parallel, then linked into
 ``eviction_fed_weight_amd/libtc.so``.  All device code is compiled with
-packed float32 instructions disabled.
+packed float32 instructions disabled and with -fno-honor-nans (the kernels
+never see NaN operands; this drops the canonicalising moves around fmaxf).
 """
 from __future__ import annotations
 
@@ -18,10 +19,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtc.so")
-SOURCES = ["tc_api.hip", "tc_forward.hip", "tc_decode.hip", "tc_backward.hip"]
+SOURCES = ["tc_api.hip", "tc_forward.hip", "tc_fwd128.hip", "tc_decode.hip", "tc_backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "-fno-honor-nans",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"),
 ]

@@ -10,7 +10,13 @@
 
 namespace {
 
-constexpr int kBlock = 64;  // query rows per block = tokens per scan chunk
+constexpr int kBlock = 64;  // backward: query rows per block = tokens per scan chunk
+
+// Query rows per block of the forward kernels: 128 (four waves of 32 rows)
+// for bf16 with D <= 64, else 64 (four waves of 16 rows).  The float32 path
+// keeps the 64-row kernel: it runs at two workgroups per compute unit with
+// every accumulator in VGPRs (see the 16x16x4 float32 note in tc_forward.hip).
+int fwd_block(int D, int32_t dtype) { return (D <= 64 && dtype == TC_BF16) ? 128 : 64; }
 
 bool supported_d(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
 
@@ -30,16 +36,33 @@ struct Plan {
   size_t state_bytes;  // one [BH][nseg][D*D] float block
 };
 
-// Blocks per segment: enough segments to give ~1024 workgroups, few enough
-// that the chain over segments stays short.
+// Workgroups of the fused forward kernel resident at once on an MI355X
+// (256 compute units; two per unit for D <= 64, one for D = 128).  Only the
+// speed of the schedule depends on it, never the result.
+long long fwd_slots(int D) { return 256LL * (D >= 128 ? 1 : 2); }
+
+// Blocks per segment.  A workgroup walks G blocks after a start-up of about
+// half a block (state load, first tiles), so the fused kernel takes about
+// ceil(BH * nseg / slots) * (G + 1/2) block-times; the chain over segments
+// adds a little per segment.  Pick the G that minimises the sum.
 Plan plan_for(const tc_shape_t& s) {
   Plan p;
   const long long BH = (long long)s.B * s.H;
-  p.nblk = (s.T + kBlock - 1) / kBlock;
-  long long G = (BH * p.nblk + 1023) / 1024;
-  if (G < 1) G = 1;
-  if (G > p.nblk) G = p.nblk;
-  p.G = (int)G;
+  const long long slots = fwd_slots(s.D);
+  const int bm = fwd_block(s.D, s.dtype);
+  p.nblk = (s.T + bm - 1) / bm;
+  long long best = -1;
+  int bestG = 1;
+  for (int G = 1; G <= p.nblk; ++G) {
+    const long long nseg = (p.nblk + G - 1) / G;
+    if (G > 1 && (p.nblk + G - 2) / (G - 1) == nseg) continue;  // same split as G - 1, more work per segment
+    const long long cost = ((BH * nseg + slots - 1) / slots) * (2 * G + 1) * 100 + nseg;
+    if (best < 0 || cost <= best) {
+      best = cost;
+      bestG = G;
+    }
+  }
+  p.G = bestG;
   p.nseg = (p.nblk + p.G - 1) / p.G;
   p.state_bytes = (size_t)BH * p.nseg * s.D * s.D * sizeof(float);
   return p;
@@ -133,7 +156,9 @@ tc_status_t tc_forward(const tc_shape_t* s, const void* q, const void* k, const 
   a.G = p.G;
   a.nseg = p.nseg;
   a.scale = scale_of(s->scale, s->D);
-  const hipError_t e = tck::launch_forward(a, s->D, s->dtype == TC_BF16, (hipStream_t)stream);
+  const bool is_bf16 = s->dtype == TC_BF16;
+  const hipError_t e = fwd_block(s->D, s->dtype) == 128 ? tck::launch_forward128(a, s->D, is_bf16, (hipStream_t)stream)
+                                              : tck::launch_forward(a, s->D, is_bf16, (hipStream_t)stream);
   return e == hipSuccess ? TC_OK : TC_ERR_HIP;
 }
 

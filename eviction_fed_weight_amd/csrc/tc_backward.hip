@@ -429,6 +429,7 @@ __global__ void __launch_bounds__(256, 1) dq_kernel(BwdArgs a) {
     load_tiles<D, true>(S, a.fstate + ((size_t)bh * a.nseg + seg) * D * D, wid, l16, lg);
     load_tiles<D, true>(B, a.tstate + ((size_t)bh * a.nseg + seg) * D * D, wid, l16, lg);
   }
+  vm_fence_loads();
   const int jb = seg * a.G, je = min(a.nblk, jb + a.G);
   const int r = wid * 16 + l16;
   float md_acc = 0.0f, dl_acc = 0.0f;
@@ -691,6 +692,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
     load_tiles<D, false>(RA, g, wid, l16, lg);
     load_tiles<D, true>(RB, g, wid, l16, lg);
   }
+  vm_fence_loads();
   const int jb = seg * a.G, je = min(a.nblk, jb + a.G);
   const int kidx = wid * 16 + l16;
   TileRegs<E, D, 64> kl, vl, ql, yl;

@@ -130,6 +130,24 @@ __device__ __forceinline__ float sum4(float x) {
   x += __shfl_xor(x, 32);
   return x;
 }
+// Same reductions with the gfx950 lane-swap instructions (VALU only, no LDS
+// round trip).  Every lane of the wavefront must be active.
+__device__ __forceinline__ float xmax4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xsum4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// 2^x with the hardware instruction (results below 2^-126 flush to zero;
+// -inf gives 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
@@ -225,35 +243,10 @@ struct TileRegs {
   }
 };
 
-// 16-byte vector of elements.
-template <class E>
-struct Vec16 {
-  static constexpr int N = 16 / sizeof(E);
-  typedef uint4 raw;
-};
 
-// Copy rows [r0, r0+NR) of a row-major [T][D] matrix into LDS.  Rows outside
-// [0, T) read as zero.  RM: row-major copy (leading dim ldr); TR: transposed
-// copy (element (row, d) at tr[d*ldt + row]).  All 256 threads participate.
-template <class E, int D, int NR, bool RM, bool TR>
-__device__ __forceinline__ void stage_rows(const E* __restrict__ g, int r0, int T, E* rm, int ldr,
-                                           E* tr, int ldt) {
-  constexpr int VE = 16 / sizeof(E);
-  constexpr int VPR = D / VE;  // vectors per row
-  constexpr int NV = NR * VPR;
-  for (int x = threadIdx.x; x < NV; x += 256) {
-    const int row = x / VPR;
-    const int col = (x - row * VPR) * VE;
-    const int gr = r0 + row;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (gr >= 0 && gr < T) val = *(const uint4*)(g + (size_t)gr * D + col);
-    if (RM) *(uint4*)(rm + row * ldr + col) = val;
-    if (TR) {
-      const E* e = (const E*)&val;
-#pragma unroll
-      for (int j = 0; j < VE; ++j) tr[(col + j) * ldt + row] = e[j];
-    }
-  }
-}
+// Compiler-visible s_waitcnt vmcnt(0): marks every earlier vector-memory load
+// complete for the compiler's own wait analysis (used after loads that feed
+// loop-carried registers, so the loop body needs no conservative full waits).
+__device__ __forceinline__ void vm_fence_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace tck

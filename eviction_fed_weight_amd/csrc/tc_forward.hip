@@ -19,7 +19,10 @@
 // A workgroup walks a segment of G consecutive blocks carrying S in float32
 // MFMA accumulators; the segment-start states come from a per-segment pass
 // (seg_state_kernel) and a short chain over segments (seg_chain_kernel).
+#include <type_traits>
+
 #include "tc_device.h"
+#include "tc_fwd_common.h"
 #include "tc_launch.h"
 
 namespace tck {
@@ -39,198 +42,15 @@ struct FwdLds {
   static constexpr int TOTAL = U + TILE;  // + Q block
 };
 
-// S[o][at] holds rows a = 16*at + 4*lg + i, column c = 16*(wid + 4*o) + l16.
-template <class E, int D>
-struct State {
-  static constexpr int NT = D / 16;
-  static constexpr int NOWN = (NT + 3) / 4;
-  f32x4 s[NOWN][NT];
-};
-
-// S <- lambda^len S + sum_{c<len, e0+c>=0} lambda^(len-1-c) K[c,:]^T V[c,:]
-// with the chunk's K and V row-major in LDS (row stride LDK).
-template <class E, int D>
-__device__ __forceinline__ void state_update(State<E, D>& st, const E* Ks, const E* Vs, const float* pw,
-                                             int len, int e0, int wid, int l16, int lg) {
-  using M = Mfma<E>;
-  using frag = typename M::frag;
-  constexpr int NT = D / 16, NOWN = State<E, D>::NOWN, LDK = FwdLds<E, D>::LDK;
-  const float decay = pw[len];
-#pragma unroll
-  for (int o = 0; o < NOWN; ++o) {
-    const int ct = wid + 4 * o;
-    if (ct < NT) {
-#pragma unroll
-      for (int at = 0; at < NT; ++at) st.s[o][at] *= decay;
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        float wv[8];
-        {
-          float vv[8];
-          M::to_f32(ColFrag<E>::read(Vs + (kc * 32 + lg * 8) * LDK + ct * 16, LDK, l16), vv);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int c = kc * 32 + lg * 8 + j;
-            const float w = (c < len && e0 + c >= 0) ? pw[len - 1 - c] : 0.0f;
-            wv[j] = w * vv[j];
-          }
-        }
-        frag bhi, blo;
-        M::split(wv, bhi, blo);
-#pragma unroll
-        for (int at = 0; at < NT; ++at) {
-          const frag a = ColFrag<E>::read(Ks + (kc * 32 + lg * 8) * LDK + at * 16, LDK, l16);
-          st.s[o][at] = M::mma(a, bhi, st.s[o][at]);
-          if (M::kSplit) st.s[o][at] = M::mma(a, blo, st.s[o][at]);
-        }
-      }
-    }
-  }
-}
-
-template <class E, int D>
-__device__ __forceinline__ void state_zero(State<E, D>& st) {
-#pragma unroll
-  for (int o = 0; o < State<E, D>::NOWN; ++o)
-#pragma unroll
-    for (int at = 0; at < D / 16; ++at) st.s[o][at] = f32x4{0.f, 0.f, 0.f, 0.f};
-}
-
-template <class E, int D>
-__device__ __forceinline__ void state_load(State<E, D>& st, const float* g, int wid, int l16, int lg) {
-  constexpr int NT = D / 16;
-#pragma unroll
-  for (int o = 0; o < State<E, D>::NOWN; ++o) {
-    const int ct = wid + 4 * o;
-#pragma unroll
-    for (int at = 0; at < NT; ++at)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = 0.0f;
-        if (ct < NT) x = g[(at * 16 + lg * 4 + i) * D + ct * 16 + l16];
-        st.s[o][at][i] = x;
-      }
-  }
-}
-
-template <class E, int D>
-__device__ __forceinline__ void state_store(const State<E, D>& st, float* g, float mult, int wid, int l16,
-                                            int lg) {
-  constexpr int NT = D / 16;
-#pragma unroll
-  for (int o = 0; o < State<E, D>::NOWN; ++o) {
-    const int ct = wid + 4 * o;
-    if (ct < NT) {
-#pragma unroll
-      for (int at = 0; at < NT; ++at)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) g[(at * 16 + lg * 4 + i) * D + ct * 16 + l16] = mult * st.s[o][at][i];
-    }
-  }
-}
-
-// Fragment made of two runs of four consecutive LDS elements (the second
-// run replaced by zeros when !second).
-template <class E>
-__device__ __forceinline__ typename Mfma<E>::frag lds4x2(const E* p0, const E* p1, bool second);
-template <>
-__device__ __forceinline__ bf16x8 lds4x2<bf16>(const bf16* p0, const bf16* p1, bool second) {
-  const bf16x4 a = *(const bf16x4*)p0;
-  bf16x4 b = *(const bf16x4*)p1;
-  if (!second) b = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
-  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-template <>
-__device__ __forceinline__ f32x8 lds4x2<float>(const float* p0, const float* p1, bool second) {
-  const f32x4 a = *(const f32x4*)p0;
-  f32x4 b = *(const f32x4*)p1;
-  if (!second) b = f32x4{0.f, 0.f, 0.f, 0.f};
-  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// Store four consecutive outputs of one row.
-__device__ __forceinline__ void store4(bf16* dst, f32x4 x) {
-  bf16x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = (bf16)x[i];
-  *(bf16x4*)dst = r;
-}
-__device__ __forceinline__ void store4(float* dst, f32x4 x) { *(f32x4*)dst = x; }
-
 // ---------------------------------------------------------------------------
-// Per-segment local states: L_m = S over the evictions of segment m, from 0.
-// grid = BH * (nseg - 1); writes ws[bh][m + 1].
-template <class E, int D>
-__global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
-  using L = FwdLds<E, D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::TILE];
-  __shared__ float pw[72];
-  E* Ks = (E*)smem;
-  E* Vs = (E*)(smem + L::TILE);
-  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
-  const int nm = a.nseg - 1;
-  const int bh = blockIdx.x / nm, m = blockIdx.x - bh * nm;
-  const int h = bh % a.H;
-  const size_t base = (size_t)bh * a.T * D;
-  const uint32_t nbytes = (uint32_t)a.T * D * sizeof(E);
-  const auto Kg = make_rsrc((const E*)a.k + base, nbytes);
-  const auto Vg = make_rsrc((const E*)a.v + base, nbytes);
-  if (tid <= 64) pw[tid] = powi(a.lam[h], tid);
-  State<E, D> st;
-  state_zero(st);
-  TileRegs<E, D, 64> kl, vl;
-  int g0 = 0;
-  while (g0 < a.G && (m * a.G + g0) * 64 - a.W + 63 < 0) ++g0;
-  if (g0 < a.G) {
-    kl.load(Kg, (m * a.G + g0) * 64 - a.W);
-    vl.load(Vg, (m * a.G + g0) * 64 - a.W);
-  }
-  for (int g = g0; g < a.G; ++g) {
-    const int e0 = (m * a.G + g) * 64 - a.W;
-    __syncthreads();
-    kl.store(Ks, L::LDK);
-    vl.store(Vs, L::LDK);
-    __syncthreads();
-    if (g + 1 < a.G) {
-      kl.load(Kg, e0 + 64);
-      vl.load(Vg, e0 + 64);
-    }
-    state_update(st, Ks, Vs, pw, 64, e0, wid, l16, lg);
-  }
-  state_store(st, a.seg_state + ((size_t)bh * a.nseg + m + 1) * D * D, 1.0f, wid, l16, lg);
-}
-
-// Chain over segments, in place: ws[0] = 0, ws[m+1] = lambda^(64G) ws[m] + L_m.
-// grid = (D*D/4 + 255)/256 x BH; each thread owns four consecutive floats and
-// loads eight segments ahead of the dependent chain.
-template <int D>
-__global__ void __launch_bounds__(256) seg_chain_kernel(FwdArgs a) {
-  const int bh = blockIdx.y;
-  const int x = blockIdx.x * 256 + threadIdx.x;
-  if (x * 4 >= D * D) return;
-  const float decay = powi(a.lam[bh % a.H], 64 * a.G);
-  float4* p = (float4*)(a.seg_state + (size_t)bh * a.nseg * D * D) + x;
-  const size_t stride = (size_t)D * D / 4;
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  p[0] = s;
-  for (int m0 = 1; m0 < a.nseg; m0 += 8) {
-    float4 l[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (m0 + u < a.nseg) l[u] = p[(m0 + u) * stride];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (m0 + u < a.nseg) {
-        s.x = decay * s.x + l[u].x;
-        s.y = decay * s.y + l[u].y;
-        s.z = decay * s.z + l[u].z;
-        s.w = decay * s.w + l[u].w;
-        p[(m0 + u) * stride] = s;
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------
+// Note on float32 inputs.  On gfx950 a VALU read of a float32 16x16x4 MFMA
+// result needs 10 wait states, and a v_accvgpr_mov_b32 copy of it more than
+// 8 (measured).  Where a kernel runs at one workgroup per compute unit the
+// compiler keeps accumulators in AGPRs and, at some control-flow joins, copies
+// them with v_accvgpr_mov_b32 too soon, which reads a stale element.  This
+// kernel at two workgroups per unit (D <= 64) keeps every accumulator in
+// VGPRs, so the library runs float32 inputs of D <= 64 here.
+//
 // Fused forward: grid = BH * nseg, 256 threads (4 waves x 16 query rows).
 template <class E, int D>
 __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a) {
@@ -265,6 +85,7 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
     state_zero(st);
   else
     state_load(st, a.seg_state + ((size_t)bh * a.nseg + seg) * D * D, wid, l16, lg);
+  vm_fence_loads();
 
   const int jb = seg * a.G;
   const int je = min(a.nblk, jb + a.G);
@@ -309,57 +130,67 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
         kl.load(Kg, nr);
         vl.load(Vg, nr);
       }
-      f32x4 Z[4];
+      // scores, online softmax and P V for one 64-key tile; FULL: every key of
+      // the tile is inside every row's window (no mask)
+      auto tile = [&](auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
+        f32x4 Z[4];
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        Z[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int kr = 32 * (n >> 1) + (l16 >> 2) * 8 + (n & 1) * 4 + (l16 & 3);
+        for (int n = 0; n < 4; ++n) {
+          Z[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+          const int kr = 32 * (n >> 1) + (l16 >> 2) * 8 + (n & 1) * 4 + (l16 & 3);
 #pragma unroll
-        for (int dc = 0; dc < NKC; ++dc) {
-          const frag ka = (dc * 32 + lg * 8 < D) ? M::lds8(Ks + kr * LDK + dc * 32 + lg * 8) : M::zero();
-          Z[n] = M::mma(ka, qf[dc], Z[n]);
+          for (int dc = 0; dc < NKC; ++dc) {
+            const frag ka = (dc * 32 + lg * 8 < D) ? M::lds8(Ks + kr * LDK + dc * 32 + lg * 8) : M::zero();
+            Z[n] = M::mma(ka, qf[dc], Z[n]);
+          }
         }
-      }
-      const bool full = (k0 + 63 <= t0) && (k0 >= t0 + 64 - W);
-      float zv[16];
-      float mz = kNegInf;
+        float zv[16];
+        float mz = kNegInf;
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
+        for (int n = 0; n < 4; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k0 + 32 * (n >> 1) + lg * 8 + (n & 1) * 4 + i;
-          float z = Z[n][i];
-          if (!full && !(key <= trow && key > trow - W)) z = kNegInf;
-          zv[(n >> 1) * 8 + (n & 1) * 4 + i] = z;
-          mz = fmaxf(mz, z);
+          for (int i = 0; i < 4; ++i) {
+            float z = Z[n][i];
+            if (!FULL) {
+              const int key = k0 + 32 * (n >> 1) + lg * 8 + (n & 1) * 4 + i;
+              if (!(key <= trow && key > trow - W)) z = kNegInf;
+            }
+            zv[(n >> 1) * 8 + (n & 1) * 4 + i] = z;
+            mz = fmaxf(mz, z);
+          }
+        mz = xmax4(mz);
+        const float mnew = fmaxf(mrow, mz * sl2);
+        const float msafe = (mnew == kNegInf) ? 0.0f : mnew;
+        const float alpha = fast_exp2(mrow - msafe);
+        float ps = 0.0f;
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          zv[x] = fast_exp2(__builtin_fmaf(zv[x], sl2, -msafe));
+          ps += zv[x];
         }
-      mz = max4(mz);
-      const float mnew = fmaxf(mrow, mz * sl2);
-      const float msafe = (mnew == kNegInf) ? 0.0f : mnew;
-      const float alpha = exp2f(mrow - msafe);
-      float ps = 0.0f;
+        lrow = lrow * alpha + ps;  // this lane's share of the row sum
+        mrow = mnew;
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        zv[x] = exp2f(__builtin_fmaf(zv[x], sl2, -msafe));
-        ps += zv[x];
-      }
-      ps = sum4(ps);
-      lrow = lrow * alpha + ps;
-      mrow = mnew;
+        for (int dt = 0; dt < NT; ++dt) O[dt] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < NT; ++dt) O[dt] *= alpha;
+        for (int p = 0; p < 2; ++p) {
+          float pv[8];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        float pv[8];
+          for (int jj = 0; jj < 8; ++jj) pv[jj] = zv[p * 8 + jj];
+          const frag pf = M::pack(pv);
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) pv[jj] = zv[p * 8 + jj];
-        const frag pf = M::pack(pv);
-#pragma unroll
-        for (int dt = 0; dt < NT; ++dt)
-          O[dt] = M::mma(ColFrag<E>::read(Vs + (p * 32 + lg * 8) * LDK + dt * 16, LDK, l16), pf, O[dt]);
-      }
+          for (int dt = 0; dt < NT; ++dt)
+            O[dt] = M::mma(ColFrag<E>::read(Vs + (p * 32 + lg * 8) * LDK + dt * 16, LDK, l16), pf, O[dt]);
+        }
+      };
+      if ((k0 + 63 <= t0) && (k0 >= t0 + 64 - W))
+        tile(std::true_type{});
+      else
+        tile(std::false_type{});
     }
     {
+      lrow = xsum4(lrow);
       const float inv = 1.0f / lrow;
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt) O[dt] *= inv;
@@ -445,9 +276,9 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
       }
       // carry the state to the next block (or to step T-1 for A_final)
       if (more) {
-        state_update(st, Ks, Vs, pw, 64, e0, wid, l16, lg);
+        state_update(st, Ks, L::LDK, Vs, L::LDK, pw, 64, e0, wid, l16, lg);
       } else if (last && a.A_final) {
-        state_update(st, Ks, Vs, pw, T - t0, e0, wid, l16, lg);
+        state_update(st, Ks, LDK, Vs, LDK, pw, T - t0, e0, wid, l16, lg);
       }
     }
     // ---- store y ----
@@ -469,28 +300,20 @@ template <class E, int D>
 static hipError_t launch_fwd_impl(const FwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
   if (a.nseg > 1) {
-    hipLaunchKernelGGL((seg_state_kernel<E, D>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((seg_chain_kernel<D>), dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((seg_state_kernel<E, D, 64>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((seg_chain_kernel<D, 64>), dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, s, a);
   }
   hipLaunchKernelGGL((fwd_kernel<E, D>), dim3(BH * a.nseg), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_forward(const FwdArgs& a, int D, bool is_bf16, hipStream_t s) {
-  if (is_bf16) {
-    switch (D) {
-      case 16: return launch_fwd_impl<bf16, 16>(a, s);
-      case 32: return launch_fwd_impl<bf16, 32>(a, s);
-      case 64: return launch_fwd_impl<bf16, 64>(a, s);
-      case 128: return launch_fwd_impl<bf16, 128>(a, s);
-    }
-  } else {
-    switch (D) {
-      case 16: return launch_fwd_impl<float, 16>(a, s);
-      case 32: return launch_fwd_impl<float, 32>(a, s);
-      case 64: return launch_fwd_impl<float, 64>(a, s);
-      case 128: return launch_fwd_impl<float, 128>(a, s);
-    }
+  if (is_bf16) return D == 128 ? launch_fwd_impl<bf16, 128>(a, s) : hipErrorInvalidValue;
+  switch (D) {
+    case 16: return launch_fwd_impl<float, 16>(a, s);
+    case 32: return launch_fwd_impl<float, 32>(a, s);
+    case 64: return launch_fwd_impl<float, 64>(a, s);
+    case 128: return launch_fwd_impl<float, 128>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -1,0 +1,212 @@
+// Pieces shared by the forward kernels: the eviction state S held in
+// matrix-core accumulators, its decayed rank-64 update, and small LDS and
+// store helpers.
+//
+// Method ("Tensor Cache: Eviction-conditioned Associative Memory for
+// Transformers", Section 3.2): A_t = lambda A_{t-1} + eta k_{t-W} v_{t-W}^T;
+// the kernels carry S = A / eta so eta is applied once at the read.
+#pragma once
+
+#include "tc_device.h"
+#include "tc_launch.h"
+
+namespace tck {
+
+// S[o][at] holds rows a = 16*at + 4*lg + i, column c = 16*(wid + 4*o) + l16.
+template <class E, int D>
+struct State {
+  static constexpr int NT = D / 16;
+  static constexpr int NOWN = (NT + 3) / 4;
+  f32x4 s[NOWN][NT];
+};
+
+// S <- lambda^len S + sum_{c<len, e0+c>=0} lambda^(len-1-c) K[c,:]^T V[c,:]
+// for a 64-row chunk whose K and V are row-major in LDS (row strides ldk,
+// ldv); pw[n] = lambda^n for n <= 64.
+template <class E, int D>
+__device__ __forceinline__ void state_update(State<E, D>& st, const E* Ks, int ldk, const E* Vs, int ldv,
+                                             const float* pw, int len, int e0, int wid, int l16, int lg) {
+  using M = Mfma<E>;
+  using frag = typename M::frag;
+  constexpr int NT = D / 16, NOWN = State<E, D>::NOWN;
+  const float decay = pw[len];
+#pragma unroll
+  for (int o = 0; o < NOWN; ++o) {
+    const int ct = wid + 4 * o;
+    if (ct < NT) {
+#pragma unroll
+      for (int at = 0; at < NT; ++at) st.s[o][at] *= decay;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        float wv[8];
+        {
+          float vv[8];
+          M::to_f32(ColFrag<E>::read(Vs + (kc * 32 + lg * 8) * ldv + ct * 16, ldv, l16), vv);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int c = kc * 32 + lg * 8 + j;
+            const float w = (c < len && e0 + c >= 0) ? pw[len - 1 - c] : 0.0f;
+            wv[j] = w * vv[j];
+          }
+        }
+        frag bhi, blo;
+        M::split(wv, bhi, blo);
+#pragma unroll
+        for (int at = 0; at < NT; ++at) {
+          const frag a = ColFrag<E>::read(Ks + (kc * 32 + lg * 8) * ldk + at * 16, ldk, l16);
+          st.s[o][at] = M::mma(a, bhi, st.s[o][at]);
+          if (M::kSplit) st.s[o][at] = M::mma(a, blo, st.s[o][at]);
+        }
+      }
+    }
+  }
+}
+
+template <class E, int D>
+__device__ __forceinline__ void state_zero(State<E, D>& st) {
+#pragma unroll
+  for (int o = 0; o < State<E, D>::NOWN; ++o)
+#pragma unroll
+    for (int at = 0; at < D / 16; ++at) st.s[o][at] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+template <class E, int D>
+__device__ __forceinline__ void state_load(State<E, D>& st, const float* g, int wid, int l16, int lg) {
+  constexpr int NT = D / 16;
+#pragma unroll
+  for (int o = 0; o < State<E, D>::NOWN; ++o) {
+    const int ct = wid + 4 * o;
+#pragma unroll
+    for (int at = 0; at < NT; ++at)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = 0.0f;
+        if (ct < NT) x = g[(at * 16 + lg * 4 + i) * D + ct * 16 + l16];
+        st.s[o][at][i] = x;
+      }
+  }
+}
+
+template <class E, int D>
+__device__ __forceinline__ void state_store(const State<E, D>& st, float* g, float mult, int wid, int l16,
+                                            int lg) {
+  constexpr int NT = D / 16;
+#pragma unroll
+  for (int o = 0; o < State<E, D>::NOWN; ++o) {
+    const int ct = wid + 4 * o;
+    if (ct < NT) {
+#pragma unroll
+      for (int at = 0; at < NT; ++at)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) g[(at * 16 + lg * 4 + i) * D + ct * 16 + l16] = mult * st.s[o][at][i];
+    }
+  }
+}
+
+// Fragment made of two runs of four consecutive LDS elements (the second
+// run replaced by zeros when !second).
+template <class E>
+__device__ __forceinline__ typename Mfma<E>::frag lds4x2(const E* p0, const E* p1, bool second);
+template <>
+__device__ __forceinline__ bf16x8 lds4x2<bf16>(const bf16* p0, const bf16* p1, bool second) {
+  const bf16x4 a = *(const bf16x4*)p0;
+  bf16x4 b = *(const bf16x4*)p1;
+  if (!second) b = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+template <>
+__device__ __forceinline__ f32x8 lds4x2<float>(const float* p0, const float* p1, bool second) {
+  const f32x4 a = *(const f32x4*)p0;
+  f32x4 b = *(const f32x4*)p1;
+  if (!second) b = f32x4{0.f, 0.f, 0.f, 0.f};
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Store four consecutive outputs of one row.
+__device__ __forceinline__ void store4(bf16* dst, f32x4 x) {
+  bf16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (bf16)x[i];
+  *(bf16x4*)dst = r;
+}
+__device__ __forceinline__ void store4(float* dst, f32x4 x) { *(f32x4*)dst = x; }
+
+// ---------------------------------------------------------------------------
+// Segment states for a forward pass with BM query rows per block and G blocks
+// per segment (segment m holds the evictions e in [m G BM - W, (m+1) G BM - W)).
+
+// Local states L_m = S over the evictions of segment m, from zero.
+// grid = BH * (nseg - 1); writes seg_state[bh][m + 1].
+template <class E, int D, int BM>
+__global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
+  constexpr int LDK = D + 16 / (int)sizeof(E);
+  constexpr int TILE = 64 * LDK * (int)sizeof(E);
+  __shared__ __attribute__((aligned(16))) char smem[2 * TILE];
+  __shared__ float pw[72];
+  E* Ks = (E*)smem;
+  E* Vs = (E*)(smem + TILE);
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  const int nm = a.nseg - 1;
+  const int bh = blockIdx.x / nm, m = blockIdx.x - bh * nm;
+  const int h = bh % a.H;
+  const size_t base = (size_t)bh * a.T * D;
+  const uint32_t nbytes = (uint32_t)a.T * D * sizeof(E);
+  const auto Kg = make_rsrc((const E*)a.k + base, nbytes);
+  const auto Vg = make_rsrc((const E*)a.v + base, nbytes);
+  if (tid <= 64) pw[tid] = powi(a.lam[h], tid);
+  State<E, D> st;
+  state_zero(st);
+  TileRegs<E, D, 64> kl, vl;
+  const int ntile = a.G * (BM / 64);
+  const int ebase = m * a.G * BM - a.W;
+  int t0 = 0;
+  while (t0 < ntile && ebase + 64 * t0 + 63 < 0) ++t0;  // tiles wholly before the first token
+  kl.load(Kg, ebase + 64 * t0);
+  vl.load(Vg, ebase + 64 * t0);
+  for (int t = t0; t < ntile; ++t) {
+    const int e0 = ebase + 64 * t;
+    __syncthreads();
+    kl.store(Ks, LDK);
+    vl.store(Vs, LDK);
+    __syncthreads();
+    if (t + 1 < ntile) {
+      kl.load(Kg, e0 + 64);
+      vl.load(Vg, e0 + 64);
+    }
+    state_update(st, Ks, LDK, Vs, LDK, pw, 64, e0, wid, l16, lg);
+  }
+  state_store(st, a.seg_state + ((size_t)bh * a.nseg + m + 1) * D * D, 1.0f, wid, l16, lg);
+}
+
+// Chain over segments, in place: seg_state[0] = 0 and
+// seg_state[m+1] = lambda^(G BM) seg_state[m] + L_m.
+// grid = (D*D/4 + 255)/256 x BH; each thread owns four consecutive floats and
+// loads eight segments ahead of the dependent chain.
+template <int D, int BM>
+__global__ void __launch_bounds__(256) seg_chain_kernel(FwdArgs a) {
+  const int bh = blockIdx.y;
+  const int x = blockIdx.x * 256 + threadIdx.x;
+  if (x * 4 >= D * D) return;
+  const float decay = powi(a.lam[bh % a.H], BM * a.G);
+  float4* p = (float4*)(a.seg_state + (size_t)bh * a.nseg * D * D) + x;
+  const size_t stride = (size_t)D * D / 4;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  p[0] = s;
+  for (int m0 = 1; m0 < a.nseg; m0 += 8) {
+    float4 l[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (m0 + u < a.nseg) l[u] = p[(m0 + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (m0 + u < a.nseg) {
+        s.x = decay * s.x + l[u].x;
+        s.y = decay * s.y + l[u].y;
+        s.z = decay * s.z + l[u].z;
+        s.w = decay * s.w + l[u].w;
+        p[(m0 + u) * stride] = s;
+      }
+  }
+}
+
+}  // namespace tck

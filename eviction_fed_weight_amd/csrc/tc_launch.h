@@ -19,7 +19,7 @@ struct FwdArgs {
   float* lse;      // nullable
   float* seg_state;  // [B*H][nseg][D*D] segment-start states (eta factored out)
   int B, H, T, W;
-  int nblk;  // ceil(T / 64)
+  int nblk;  // ceil(T / block rows): 128 (bf16, D <= 64) or 64
   int G;     // blocks per segment
   int nseg;  // ceil(nblk / G)
   float scale;
@@ -69,7 +69,8 @@ struct BwdArgs {
   float scale;
 };
 
-hipError_t launch_forward(const FwdArgs& a, int D, bool is_bf16, hipStream_t s);
+hipError_t launch_forward(const FwdArgs& a, int D, bool is_bf16, hipStream_t s);     // 64-row blocks: float32, and bf16 with D = 128
+hipError_t launch_forward128(const FwdArgs& a, int D, bool is_bf16, hipStream_t s);  // 128-row blocks: bf16 with D <= 64
 hipError_t launch_decode(const DecArgs& a, int D, bool is_bf16, hipStream_t s);
 hipError_t launch_backward(const BwdArgs& a, int D, bool is_bf16, hipStream_t s);
 
