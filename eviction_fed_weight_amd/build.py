@@ -19,7 +19,17 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtc.so")
-SOURCES = ["tc_api.hip", "tc_forward.hip", "tc_fwd128.hip", "tc_decode.hip", "tc_backward.hip"]
+# (source, object name, extra flags)
+UNITS = [
+    ("tc_api.hip", "tc_api", []),
+    ("tc_forward.hip", "tc_forward", []),
+    ("tc_fwd128.hip", "tc_fwd128", []),
+    ("tc_decode.hip", "tc_decode", []),
+    # bf16 backward: matrix-core results kept in VGPRs (fewer scratch spills)
+    ("tc_backward.hip", "tc_backward_bf16", ["-DTC_BWD_BF16=1", "-mllvm", "-amdgpu-mfma-vgpr-form"]),
+    ("tc_backward.hip", "tc_backward_f32", ["-DTC_BWD_BF16=0"]),
+]
+SOURCES = sorted({u[0] for u in UNITS})
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -29,9 +39,10 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(unit) -> str:
+    src, name, extra = unit
+    obj = os.path.join(BUILD, name + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr[-6000:]))
@@ -40,9 +51,8 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(UNITS))) as ex:
+        objs = list(ex.map(_compile, UNITS))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -170,6 +170,8 @@ tc_status_t tc_decode_step(const tc_decode_shape_t* s, const void* q, const void
   if (!valid_dtype(s->dtype) || !supported_d(s->D)) return TC_ERR_UNSUPPORTED;
   if (!(s->scale == s->scale)) return TC_ERR_INVALID_ARGUMENT;
   if ((long long)s->S * s->H > (1LL << 30)) return TC_ERR_UNSUPPORTED;
+  // byte offsets inside one (stream, head) ring are 32-bit
+  if ((long long)(s->W + 512) * s->D * (long long)elem_size(s->dtype) > (1LL << 31) - 1) return TC_ERR_UNSUPPORTED;
   if (!q || !k || !v || !k_ring || !v_ring || !A || !pos || !lambda || !eta || !gate || !y)
     return TC_ERR_INVALID_ARGUMENT;
   const size_t es = elem_size(s->dtype);

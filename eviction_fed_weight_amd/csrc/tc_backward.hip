@@ -28,6 +28,9 @@
 //   dkdv_kernel : reverse walk over key blocks (R carried in registers in
 //                 both operand layouts): memory-path dk, dv, then band dk, dv
 //   reduce_kernel : deterministic sums for dlambda, deta, dgate.
+#ifndef TC_BWD_BF16
+#error "compile with -DTC_BWD_BF16=1 (bf16 kernels) or -DTC_BWD_BF16=0 (float32 kernels)"
+#endif
 #include "tc_device.h"
 #include "tc_launch.h"
 
@@ -871,7 +874,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
 
 // dlambda[h] = sigma eta sum dl, deta[h] = sigma sum md,
 // dgate[h] = sigma (1-sigma) eta sum md; sums over b then segments in order.
-__global__ void reduce_kernel(BwdArgs a) {
+static __global__ void reduce_kernel(BwdArgs a) {
   const int h = blockIdx.x * blockDim.x + threadIdx.x;
   if (h >= a.H) return;
   double smd = 0.0, sdl = 0.0;
@@ -903,23 +906,31 @@ static hipError_t launch_bwd_impl(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_backward(const BwdArgs& a, int D, bool is_bf16, hipStream_t s) {
-  if (is_bf16) {
-    switch (D) {
-      case 16: return launch_bwd_impl<bf16, 16>(a, s);
-      case 32: return launch_bwd_impl<bf16, 32>(a, s);
-      case 64: return launch_bwd_impl<bf16, 64>(a, s);
-      case 128: return launch_bwd_impl<bf16, 128>(a, s);
-    }
-  } else {
-    switch (D) {
-      case 16: return launch_bwd_impl<float, 16>(a, s);
-      case 32: return launch_bwd_impl<float, 32>(a, s);
-      case 64: return launch_bwd_impl<float, 64>(a, s);
-      case 128: return launch_bwd_impl<float, 128>(a, s);
-    }
+// This file is compiled twice: TC_BWD_BF16=1 builds the bf16 kernels (with
+// matrix-core results kept in VGPRs, which removes most scratch spills of
+// the D = 128 walks), TC_BWD_BF16=0 the float32 kernels (default register
+// form: a float32 16x16x4 MFMA result copied between VGPR forms too early
+// reads stale elements on gfx950).
+#if TC_BWD_BF16
+hipError_t launch_backward_bf16(const BwdArgs& a, int D, hipStream_t s) {
+  switch (D) {
+    case 16: return launch_bwd_impl<bf16, 16>(a, s);
+    case 32: return launch_bwd_impl<bf16, 32>(a, s);
+    case 64: return launch_bwd_impl<bf16, 64>(a, s);
+    case 128: return launch_bwd_impl<bf16, 128>(a, s);
   }
   return hipErrorInvalidValue;
 }
+#else
+hipError_t launch_backward_f32(const BwdArgs& a, int D, hipStream_t s) {
+  switch (D) {
+    case 16: return launch_bwd_impl<float, 16>(a, s);
+    case 32: return launch_bwd_impl<float, 32>(a, s);
+    case 64: return launch_bwd_impl<float, 64>(a, s);
+    case 128: return launch_bwd_impl<float, 128>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+#endif
 
 }  // namespace tck

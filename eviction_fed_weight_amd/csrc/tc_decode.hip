@@ -10,22 +10,44 @@
 // ring once (2 W D element loads) and reads+writes the D x D float32 state.
 // One workgroup of four waves per (stream, head); no matrix cores.
 //   * A: float4-coalesced read-modify-write fused with the partial q A.
-//   * L1: each wave walks ring rows with D/VE lanes per row, 16-byte loads,
-//     several rows in flight per lane, an online softmax per lane group, and
-//     a log-sum-exp merge across lanes and waves at the end.
-//   * The slot being overwritten is never read back from HBM during the
-//     attention pass: its new pair is taken from LDS.
+//   * L1: each wave walks ring rows with D/VE lanes per row, 16-byte buffer
+//     loads (no per-row branches), the next stage in flight while the
+//     current one is reduced (DPP butterflies inside each lane group), an
+//     online softmax per lane group, and a log-sum-exp merge across lanes
+//     and waves at the end.
+//   * The slot being overwritten is masked out of the streamed rows: its new
+//     pair, known from the inputs, seeds the softmax state of one lane group.
 #include "tc_device.h"
 #include "tc_launch.h"
 
 namespace tck {
+
+// Sum over each aligned group of N lanes (N = 1 .. 32), result in every lane
+// of the group: DPP butterflies inside rows of 16 lanes (xor 1, xor 2, then
+// the half-row and row mirrors), a lane swap across row pairs for N = 32.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror
+  if constexpr (N >= 16) x += dpp_mov<0x140>(x); // row_mirror
+  if constexpr (N >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return x;
+}
 
 template <class E, int D>
 __global__ void __launch_bounds__(256) decode_kernel(DecArgs a) {
   constexpr int VE = 16 / (int)sizeof(E);
   constexpr int LPR = D / VE;     // lanes per ring row
   constexpr int RPW = 64 / LPR;   // ring rows per wave per load
-  constexpr int UN = (D >= 64) ? 4 : 2;  // rows in flight per lane
+  constexpr int UN = 2;           // ring rows per lane per stage (two stages in flight)
   constexpr int CG = D / 4;       // float4 column groups of A
   constexpr int RG = 256 / CG;    // row groups of A
   __shared__ float qs[D], kn[D], vn[D], ke[D], ve[D];
@@ -94,6 +116,11 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs a) {
   }
 
   // ---- step 5 (L1): softmax over the resident pairs ----
+  // Rows j < nvalid of the ring, except the overwritten slot, are streamed
+  // with branch-free buffer loads (rows past the resource read as zero and
+  // are masked); the new pair in the slot seeds the softmax state of lane
+  // group 0 of wave 0.  The next stage's rows are loaded while the current
+  // stage is reduced.
   const float sl2 = a.scale * kLog2e;
   const int lr = lane / LPR, lc = lane - (lane / LPR) * LPR;
   float qv[VE];
@@ -103,64 +130,76 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs a) {
   float acc[VE];
 #pragma unroll
   for (int j = 0; j < VE; ++j) acc[j] = 0.0f;
-
-  for (int j0 = wid * RPW; j0 < nvalid; j0 += 4 * RPW * UN) {
-    float kk[UN][VE], vv[UN][VE];
-    bool ok[UN];
+  {
+    float d = 0.0f;
 #pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      const int j = j0 + u * 4 * RPW + lr;
-      ok[u] = j < nvalid;
-      if (ok[u] && j != slot) {
-        const uint4 kraw = *(const uint4*)(kr + (size_t)j * D + lc * VE);
-        const uint4 vraw = *(const uint4*)(vr + (size_t)j * D + lc * VE);
-        const E* ke8 = (const E*)&kraw;
-        const E* ve8 = (const E*)&vraw;
+    for (int x = 0; x < VE; ++x) d += qv[x] * kn[lc * VE + x];
+    d = group_sum<LPR>(d);  // every lane (the lane exchange needs them all)
+    if (wid == 0 && lr == 0) {
+      mloc = d * sl2;
+      lloc = 1.0f;
 #pragma unroll
-        for (int x = 0; x < VE; ++x) {
-          kk[u][x] = (float)ke8[x];
-          vv[u][x] = (float)ve8[x];
-        }
-      } else {
-#pragma unroll
-        for (int x = 0; x < VE; ++x) {
-          kk[u][x] = kn[lc * VE + x];
-          vv[u][x] = vn[lc * VE + x];
-        }
-      }
+      for (int x = 0; x < VE; ++x) acc[x] = vn[lc * VE + x];
     }
-    float sc[UN];
-    float mb = mloc;
-#pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      float d = 0.0f;
-#pragma unroll
-      for (int x = 0; x < VE; ++x) d += qv[x] * kk[u][x];
-#pragma unroll
-      for (int o = 1; o < LPR; o <<= 1) d += __shfl_xor(d, o);
-      sc[u] = ok[u] ? d * sl2 : kNegInf;
-      mb = fmaxf(mb, sc[u]);
-    }
-    if (mb != kNegInf) {
-      const float c = exp2f(mloc - mb);
-      lloc *= c;
-#pragma unroll
-      for (int x = 0; x < VE; ++x) acc[x] *= c;
+  }
+  {
+    const uint32_t rbytes = (uint32_t)((size_t)W * D * sizeof(E));
+    const auto Kr = make_rsrc(kr, rbytes);
+    const auto Vr = make_rsrc(vr, rbytes);
+    constexpr int STEP = 4 * RPW * UN;  // rows per stage per workgroup
+    uint4 kc[UN], vc[UN], kx[UN], vx[UN];
+    auto row_of = [&](int j0, int u) { return j0 + u * 4 * RPW + wid * RPW + lr; };
+    auto load = [&](int j0, uint4 (&kd)[UN], uint4 (&vd)[UN]) {
 #pragma unroll
       for (int u = 0; u < UN; ++u) {
-        const float p = exp2f(sc[u] - mb);
-        lloc += p;
-#pragma unroll
-        for (int x = 0; x < VE; ++x) acc[x] += p * vv[u][x];
+        const int off = (row_of(j0, u) * D + lc * VE) * (int)sizeof(E);
+        kd[u] = buf_load16(Kr, off);
+        vd[u] = buf_load16(Vr, off);
       }
-      mloc = mb;
+    };
+    load(0, kc, vc);
+    for (int j0 = 0; j0 < nvalid; j0 += STEP) {
+      load(j0 + STEP, kx, vx);  // past nvalid: masked (past W: zeros)
+      float sc[UN];
+      float mb = mloc;
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        const E* k8 = (const E*)&kc[u];
+        float d = 0.0f;
+#pragma unroll
+        for (int x = 0; x < VE; ++x) d += qv[x] * (float)k8[x];
+        d = group_sum<LPR>(d);
+        const int j = row_of(j0, u);
+        sc[u] = (j < nvalid && j != slot) ? d * sl2 : kNegInf;
+        mb = fmaxf(mb, sc[u]);
+      }
+      if (mb != kNegInf) {
+        const float c = fast_exp2(mloc - mb);
+        lloc *= c;
+#pragma unroll
+        for (int x = 0; x < VE; ++x) acc[x] *= c;
+#pragma unroll
+        for (int u = 0; u < UN; ++u) {
+          const float p = fast_exp2(sc[u] - mb);
+          const E* v8 = (const E*)&vc[u];
+          lloc += p;
+#pragma unroll
+          for (int x = 0; x < VE; ++x) acc[x] += p * (float)v8[x];
+        }
+        mloc = mb;
+      }
+#pragma unroll
+      for (int u = 0; u < UN; ++u) {
+        kc[u] = kx[u];
+        vc[u] = vx[u];
+      }
     }
   }
   // merge lanes of the wave: common max, then sum over lanes with equal lc
   float M = mloc;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-  const float f = (mloc == kNegInf) ? 0.0f : exp2f(mloc - M);
+  const float f = (mloc == kNegInf) ? 0.0f : fast_exp2(mloc - M);
   lloc *= f;
 #pragma unroll
   for (int x = 0; x < VE; ++x) acc[x] *= f;
@@ -186,7 +225,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecArgs a) {
     float num = 0.0f, den = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float fw = (wml[w][0] == kNegInf) ? 0.0f : exp2f(wml[w][0] - Mb);
+      const float fw = (wml[w][0] == kNegInf) ? 0.0f : fast_exp2(wml[w][0] - Mb);
       num += fw * wacc[w][tid];
       den += fw * wml[w][1];
     }
