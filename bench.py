@@ -7,7 +7,7 @@ serving workload (64 streams x 32 heads, D=128, W=4096: tc_decode_step calls
 per second), the long-context prefill and the backward, each with its
 roofline, plus the CPU oracle timed on the host.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--legs prefill,decode,long,backward]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--legs prefill,decode,long,backward[,calib]]
 """
 from __future__ import annotations
 
@@ -187,6 +187,23 @@ def backward_leg(steps, warmup):
                               traffic=None, kernel="tc_backward (segment passes + dq + dkdv + reduce)"))
 
 
+def calib_leg(steps, warmup, mib=256):
+    """A plain device copy of known size (read mib MiB, write mib MiB), for
+    scaling the HBM byte counters of a profiler run to bytes."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def call():
+        dst.copy_(src)
+
+    ms = time_calls(call, steps, warmup)
+    return dict(workload="device copy %d MiB -> %d MiB" % (mib, mib), bytes_read=n * 4, bytes_written=n * 4,
+                ms_per_call=ms, gbs=2 * n * 4 / (ms * 1e-3) / 1e9)
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle (unmodified) on the prefill workload, on the host cores."""
     import numpy as np
@@ -258,6 +275,11 @@ def main():
         bw = backward_leg(max(3, args.steps // 5), 2)
         log("  backward", json.dumps(bw))
         out["backward"] = bw
+    if "calib" in legs:
+        log("copy calibration leg ...")
+        cb = calib_leg(args.steps, args.warmup)
+        log("  calib", json.dumps(cb))
+        out["calib_copy"] = cb
     if not args.no_cpu:
         log("cpu baseline ...")
         out["cpu_baseline"] = cpu_baseline()

@@ -137,7 +137,7 @@ tc_status_t tc_forward(const tc_shape_t* s, const void* q, const void* k, const 
     for (int i = 0; i < 6; ++i)
       if (overlap(ws, need, ins[i], insz[i])) return TC_ERR_INVALID_ARGUMENT;
   }
-  tck::FwdArgs a;
+  tck::FwdArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;

@@ -244,6 +244,15 @@ struct TileRegs {
 };
 
 
+// Workgroup b of a grid of n runs on XCD b % 8 (the eight chiplets take
+// workgroups in turn, each with its own L2).  Renumber so that each XCD gets
+// one contiguous range of logical indices: neighbouring work (segments of one
+// head, which share key/value rows) then shares an L2.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int x = b & 7, q = n >> 3, r = n & 7;
+  return x * q + (x < r ? x : r) + (b >> 3);
+}
+
 // Compiler-visible s_waitcnt vmcnt(0): marks every earlier vector-memory load
 // complete for the compiler's own wait analysis (used after loads that feed
 // loop-carried registers, so the loop body needs no conservative full waits).

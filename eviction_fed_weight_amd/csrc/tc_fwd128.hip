@@ -125,7 +125,8 @@ __global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(F
   constexpr int LDS = L::LDS;
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
-  const int bh = blockIdx.x / a.nseg, seg = blockIdx.x - bh * a.nseg;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / a.nseg, seg = wg - bh * a.nseg;
   const int h = bh % a.H;
   const int T = a.T, W = a.W;
   const size_t base = (size_t)bh * T * D;
@@ -141,6 +142,25 @@ __global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(F
   // S(e0) of the segment's first block -> LDS (transposed)
   if (seg == 0) {
     for (int x = tid; x < D * D; x += 256) Sl[(x % D) * LDS + x / D] = 0.0f;
+  } else if (a.prefix_direct) {
+    // S at the segment start from the local states L_m (stored at index m+1):
+    // S = sum_{m < seg} lambda^((seg-1-m) 128 G) L_m, in chain order
+    constexpr int PER = D * D / 256;
+    const float dec = powi(a.lam[h], 128 * a.G);
+    const float* g = a.seg_state + (size_t)bh * a.nseg * D * D;
+    float acc[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
+#pragma unroll 4
+    for (int m = 1; m <= seg; ++m) {
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc[k] = dec * acc[k] + g[(size_t)m * D * D + tid + 256 * k];
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int x = tid + 256 * k;
+      Sl[(x % D) * LDS + x / D] = acc[k];
+    }
   } else {
     const float* g = a.seg_state + ((size_t)bh * a.nseg + seg) * D * D;
     for (int x = tid; x < D * D; x += 256) Sl[(x % D) * LDS + x / D] = g[x];
@@ -430,12 +450,20 @@ __global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(F
   }
 }
 
+// Segments up to which the fused kernel sums the local states itself (each
+// workgroup reads at most this many D x D states, L2-resident) instead of a
+// separate chain kernel.
+constexpr int kDirectPrefixMaxSeg = 16;
+
 template <class E, int D>
-static hipError_t launch_fwd128_impl(const FwdArgs& a, hipStream_t s) {
+static hipError_t launch_fwd128_impl(const FwdArgs& a0, hipStream_t s) {
+  FwdArgs a = a0;
   const int BH = a.B * a.H;
+  a.prefix_direct = a.nseg <= kDirectPrefixMaxSeg ? 1 : 0;
   if (a.nseg > 1) {
     hipLaunchKernelGGL((seg_state_kernel<E, D, 128>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((seg_chain_kernel<D, 128>), dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, s, a);
+    if (!a.prefix_direct)
+      hipLaunchKernelGGL((seg_chain_kernel<D, 128>), dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, s, a);
   }
   hipLaunchKernelGGL((fwd128_kernel<E, D>), dim3(BH * a.nseg), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -22,6 +22,7 @@ struct FwdArgs {
   int nblk;  // ceil(T / block rows): 128 (bf16, D <= 64) or 64
   int G;     // blocks per segment
   int nseg;  // ceil(nblk / G)
+  int prefix_direct;  // fused kernel combines the local segment states itself (no chain kernel)
   float scale;
 };
 
