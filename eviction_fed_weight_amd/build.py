@@ -23,7 +23,7 @@ LIB = os.path.join(HERE, "libtc.so")
 UNITS = [
     ("tc_api.hip", "tc_api", []),
     ("tc_forward.hip", "tc_forward", []),
-    ("tc_fwd128.hip", "tc_fwd128", []),
+    ("tc_fwd_rows.hip", "tc_fwd_rows", []),
     ("tc_decode.hip", "tc_decode", []),
     # bf16 backward: matrix-core results kept in VGPRs (fewer scratch spills)
     ("tc_backward.hip", "tc_backward_bf16", ["-DTC_BWD_BF16=1", "-mllvm", "-amdgpu-mfma-vgpr-form"]),

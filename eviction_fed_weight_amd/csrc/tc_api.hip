@@ -13,9 +13,9 @@ namespace {
 constexpr int kBlock = 64;  // backward: query rows per block = tokens per scan chunk
 
 // Query rows per block of the forward kernels: 128 (four waves of 32 rows)
-// for bf16 with D <= 64, else 64 (four waves of 16 rows).  The float32 path
-// keeps the 64-row kernel: it runs at two workgroups per compute unit with
-// every accumulator in VGPRs (see the 16x16x4 float32 note in tc_forward.hip).
+// for bf16 with D <= 64, else 64 (four waves of 16 rows).  The float32 path keeps the 64-row kernel: it runs at two
+// workgroups per compute unit with every accumulator in VGPRs (see the
+// 16x16x4 float32 note in tc_forward.hip).
 int fwd_block(int D, int32_t dtype) { return (D <= 64 && dtype == TC_BF16) ? 128 : 64; }
 
 bool supported_d(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
@@ -37,9 +37,12 @@ struct Plan {
 };
 
 // Workgroups of the fused forward kernel resident at once on an MI355X
-// (256 compute units; two per unit for D <= 64, one for D = 128).  Only the
+// (256 compute units): two per unit for D <= 64, one for D = 128.  Only the
 // speed of the schedule depends on it, never the result.
-long long fwd_slots(int D) { return 256LL * (D >= 128 ? 1 : 2); }
+long long fwd_slots(int D, int32_t dtype) {
+  (void)dtype;
+  return D >= 128 ? 256 : 512;
+}
 
 // Blocks per segment.  A workgroup walks G blocks after a start-up of about
 // half a block (state load, first tiles), so the fused kernel takes about
@@ -48,7 +51,7 @@ long long fwd_slots(int D) { return 256LL * (D >= 128 ? 1 : 2); }
 Plan plan_for(const tc_shape_t& s) {
   Plan p;
   const long long BH = (long long)s.B * s.H;
-  const long long slots = fwd_slots(s.D);
+  const long long slots = fwd_slots(s.D, s.dtype);
   const int bm = fwd_block(s.D, s.dtype);
   p.nblk = (s.T + bm - 1) / bm;
   long long best = -1;
@@ -157,7 +160,7 @@ tc_status_t tc_forward(const tc_shape_t* s, const void* q, const void* k, const 
   a.nseg = p.nseg;
   a.scale = scale_of(s->scale, s->D);
   const bool is_bf16 = s->dtype == TC_BF16;
-  const hipError_t e = fwd_block(s->D, s->dtype) == 128 ? tck::launch_forward128(a, s->D, is_bf16, (hipStream_t)stream)
+  const hipError_t e = fwd_block(s->D, s->dtype) == 128 ? tck::launch_forward_rows(a, s->D, is_bf16, (hipStream_t)stream)
                                               : tck::launch_forward(a, s->D, is_bf16, (hipStream_t)stream);
   return e == hipSuccess ? TC_OK : TC_ERR_HIP;
 }

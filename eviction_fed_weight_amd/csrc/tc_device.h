@@ -209,36 +209,36 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t rs, int byte_
   return uint4{(uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]};
 }
 
-// Unrolled copy of NR rows of a row-major [T][D] matrix: load() issues every
+// Unrolled copy of NR rows of a row-major [T][D] matrix by NTH threads: load() issues every
 // global load of the tile at once (through a buffer resource covering the
 // sequence, so out-of-range rows read as zero) so they can be in flight while
 // the previous tile is computed; store() writes the registers to a row-major
 // LDS tile with leading dimension ld.
-template <class E, int D, int NR>
+template <class E, int D, int NR, int NTH = 256>
 struct TileRegs {
   static constexpr int VE = 16 / (int)sizeof(E);
   static constexpr int VPR = D / VE;
   static constexpr int NV = NR * VPR;
-  static constexpr int PER = (NV + 255) / 256;
+  static constexpr int PER = (NV + NTH - 1) / NTH;
   uint4 v[PER];
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int r0) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int x = (int)threadIdx.x + 256 * p;
+      const int x = (int)threadIdx.x + NTH * p;
       const int row = x / VPR;
       const int col = (x - row * VPR) * VE;
       int off = ((r0 + row) * D + col) * (int)sizeof(E);
-      if (NV % 256 != 0 && x >= NV) off = -16;  // out of range: reads zero
+      if (NV % NTH != 0 && x >= NV) off = -16;  // out of range: reads zero
       v[p] = buf_load16(rs, off);
     }
   }
   __device__ __forceinline__ void store(E* lds, int ld) const {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int x = (int)threadIdx.x + 256 * p;
+      const int x = (int)threadIdx.x + NTH * p;
       const int row = x / VPR;
       const int col = (x - row * VPR) * VE;
-      if (NV % 256 == 0 || x < NV) *(uint4*)(lds + row * ld + col) = v[p];
+      if (NV % NTH == 0 || x < NV) *(uint4*)(lds + row * ld + col) = v[p];
     }
   }
 };

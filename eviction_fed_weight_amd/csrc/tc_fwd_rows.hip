@@ -1,5 +1,6 @@
-// TC forward for head dimensions up to 64 on gfx950: 128 query rows per
-// block, four waves of 32 rows each.
+// TC forward for head dimensions up to 64 on gfx950: blocks of BM = 32 NW
+// query rows, NW waves of 32 rows each (NW = 4: 128-row blocks, two
+// workgroups per compute unit).
 //
 // Method ("Tensor Cache: Eviction-conditioned Associative Memory for
 // Transformers"): Section 3.1 Eq. (1) window softmax over the last W keys;
@@ -8,26 +9,29 @@
 // weighted-sum scan of the evicted pairs.
 //
 // Scan.  S(e) = sum_{i<e} lambda^(e-1-i) k_i v_i^T and A_t = eta S(t-W+1).
-// Block j holds rows t0 = 128 j .. t0+127 and evicts e0 = t0 - W .. e0+127;
+// Block j holds rows t0 = BM j .. t0+BM-1 and evicts e0 = t0 - W .. e0+BM-1;
 // for row t = t0 + r
 //   A_t = eta [ lambda^(r+1) S(e0) + sum_{c<=r} lambda^(r-c) k_{e0+c} v_{e0+c}^T ]
-// so the read is q S(e0) plus a lower-triangular decay-weighted 128 x 128
+// so the read is q S(e0) plus a lower-triangular decay-weighted BM x BM
 // product with the evicted chunk (q (k outer v) = <q,k> v), and the state
-// advances by two decayed rank-64 updates.
+// advances by BM/64 decayed rank-64 updates.
 //
-// Work of a workgroup: the blocks of one segment, each as a stream of 64-key
-// items -- the window's key tiles, then the two tiles of the evicted chunk --
-// through a two-buffer LDS pipeline with one barrier per item.  While an
-// item is computed from one buffer, the next item (already in registers) is
-// written to the other and the item after it is being loaded from HBM.
+// Work of a workgroup: the blocks of one segment, each as a stream of 64-row
+// items -- its Q block, the window's key tiles, then the tiles of the evicted
+// chunk -- through a two-buffer LDS pipeline with one barrier per item.
+// While an item is computed from one buffer, the next item (already in
+// registers) is written to the other and the item after it is being loaded.
+// Every key/value tile fetched serves all BM rows of the block, so the
+// window's overlap between neighbouring blocks is re-read (W + BM) / BM
+// times per row instead of (W + 64) / 64.
 //
 // Per wave and item: scores for 32 rows x 64 keys (16 MFMAs; every K
 // fragment read from LDS feeds both 16-row groups), softmax on the
 // transposed score layout (a lane holds one query row, so row statistics need
 // only a four-lane exchange), and P V (16 MFMAs, V fragments shared by both
-// groups).  The running max is only moved when a row's maximum grows by more
-// than 2^8 (probabilities stay below 256), which leaves most tiles without
-// the rescale of the accumulators.
+// groups; 4 more give the row sums of P).  The running max is only moved
+// when a row's maximum grows by more than 2^8 (probabilities stay below 256),
+// which leaves most tiles without the rescale of the accumulators.
 #include <type_traits>
 
 #include "tc_device.h"
@@ -36,8 +40,11 @@
 
 namespace tck {
 
-template <class E, int D>
-struct F128 {
+template <class E, int D, int NW>
+struct FRows {
+  static constexpr int NTH = 64 * NW;   // threads
+  static constexpr int BM = 32 * NW;    // query rows per block (32 per wave)
+  static constexpr int NQ = BM / 128;   // Q items per block (128 rows each)
   static constexpr int VE = 16 / (int)sizeof(E);
   // Row strides (elements).  K, Q and S^T are read 16 rows x 16 bytes at a
   // time (odd number of 16-byte chunks per row: no bank conflicts); V is read
@@ -47,7 +54,7 @@ struct F128 {
   static constexpr int KT = 64 * LDK * (int)sizeof(E);
   static constexpr int VT = 64 * LDV * (int)sizeof(E);
   static constexpr int BUF = KT + VT;
-  static constexpr int QB = 128 * LDK * (int)sizeof(E);
+  static constexpr int QB = BM * LDK * (int)sizeof(E);
   // The state lives in LDS as float S^T (S[a][c] at c * LDS + a; 17 chunks
   // per row for D = 64), so it costs no registers between its uses.
   static constexpr int LDS = D + 4;
@@ -94,32 +101,61 @@ struct VFrag<float> {
   }
 };
 
-// S <- lambda^len S + (decayed rank-64 update) on the LDS copy of S: each of
-// the first D/16 waves updates its 16 columns in registers.
-template <class E, int D>
-__device__ __forceinline__ void lds_state_update(float* Sl, const E* Kb, int ldk, const E* Vb, int ldv,
+// S <- lambda^len S + sum_{c<len, e0+c>=0} lambda^(len-1-c) K[c,:]^T V[c,:]
+// on the LDS copy of S (float S^T), for a 64-row chunk whose K and V are
+// row-major in LDS.  The D/16 x D/16 accumulator tiles are split over the
+// waves: wave w takes column tile w % NT and a contiguous range of row tiles.
+template <class E, int D, int NW>
+__device__ __forceinline__ void lds_state_update(float* Sl, const E* Ks, int ldk, const E* Vs, int ldv,
                                                  const float* pw, int len, int e0, int wid, int l16, int lg) {
-  constexpr int NT = D / 16, LDS = F128<E, D>::LDS;
-  if (wid < NT) {
-    State<E, D> st;
-    float* col = Sl + (16 * wid + l16) * LDS + 4 * lg;
-#pragma unroll
-    for (int at = 0; at < NT; ++at) st.s[0][at] = *(const f32x4*)(col + 16 * at);
-    state_update(st, Kb, ldk, Vb, ldv, pw, len, e0, wid, l16, lg);
-#pragma unroll
-    for (int at = 0; at < NT; ++at) *(f32x4*)(col + 16 * at) = st.s[0][at];
-  }
-}
-
-template <class E, int D>
-__global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(FwdArgs a) {
   using M = Mfma<E>;
   using frag = typename M::frag;
-  using L = F128<E, D>;
+  constexpr int NT = D / 16, LDS = FRows<E, D, NW>::LDS;
+  constexpr int RG = (NW / NT < NT) ? NW / NT : NT;  // row-tile groups per column tile
+  constexpr int AT = NT / RG;                        // row tiles per wave
+  const int ct = wid % NT, ar = wid / NT;
+  if (ar >= RG) return;
+  f32x4 st[AT];
+  float* col = Sl + (16 * ct + l16) * LDS + 4 * lg;
+  const float decay = pw[len];
+#pragma unroll
+  for (int k = 0; k < AT; ++k) st[k] = decay * *(const f32x4*)(col + 16 * (ar * AT + k));
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+    float wv[8];
+    {
+      float vv[8];
+      M::to_f32(ColFrag<E>::read(Vs + (kc * 32 + lg * 8) * ldv + ct * 16, ldv, l16), vv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = kc * 32 + lg * 8 + j;
+        const float w = (c < len && e0 + c >= 0) ? pw[len - 1 - c] : 0.0f;
+        wv[j] = w * vv[j];
+      }
+    }
+    frag bhi, blo;
+    M::split(wv, bhi, blo);
+#pragma unroll
+    for (int k = 0; k < AT; ++k) {
+      const frag af = ColFrag<E>::read(Ks + (kc * 32 + lg * 8) * ldk + (ar * AT + k) * 16, ldk, l16);
+      st[k] = M::mma(af, bhi, st[k]);
+      if (M::kSplit) st[k] = M::mma(af, blo, st[k]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < AT; ++k) *(f32x4*)(col + 16 * (ar * AT + k)) = st[k];
+}
+
+template <class E, int D, int NW>
+__global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdArgs a) {
+  using M = Mfma<E>;
+  using frag = typename M::frag;
+  using L = FRows<E, D, NW>;
   constexpr int NT = L::NT, NKC = L::NKC, LDK = L::LDK, LDV = L::LDV;
-  static_assert(D <= 64, "one state column tile per wave");
+  constexpr int NTH = L::NTH, BM = L::BM, NQ = L::NQ;
+  static_assert(D <= 64 && NW >= 4 && NW % 4 == 0, "shape");
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
-  __shared__ float pw[132];
+  __shared__ float pw[BM + 4];
   E* Qs = (E*)(smem + 2 * L::BUF);
   float* Sl = (float*)(smem + 2 * L::BUF + L::QB);
   constexpr int LDS = L::LDS;
@@ -137,16 +173,16 @@ __global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(F
   E* Yg = (E*)a.y + base;
   const float seta = sigmoidf(a.gate[h]) * a.eta[h];
   const float sl2 = a.scale * kLog2e;
-  if (tid <= 128) pw[tid] = powi(a.lam[h], tid);
+  if (tid <= BM) pw[tid] = powi(a.lam[h], tid);
 
   // S(e0) of the segment's first block -> LDS (transposed)
   if (seg == 0) {
-    for (int x = tid; x < D * D; x += 256) Sl[(x % D) * LDS + x / D] = 0.0f;
+    for (int x = tid; x < D * D; x += NTH) Sl[(x % D) * LDS + x / D] = 0.0f;
   } else if (a.prefix_direct) {
     // S at the segment start from the local states L_m (stored at index m+1):
-    // S = sum_{m < seg} lambda^((seg-1-m) 128 G) L_m, in chain order
-    constexpr int PER = D * D / 256;
-    const float dec = powi(a.lam[h], 128 * a.G);
+    // S = sum_{m < seg} lambda^((seg-1-m) BM G) L_m, in chain order
+    constexpr int PER = (D * D + NTH - 1) / NTH;
+    const float dec = powi(a.lam[h], BM * a.G);
     const float* g = a.seg_state + (size_t)bh * a.nseg * D * D;
     float acc[PER];
 #pragma unroll
@@ -154,52 +190,54 @@ __global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(F
 #pragma unroll 4
     for (int m = 1; m <= seg; ++m) {
 #pragma unroll
-      for (int k = 0; k < PER; ++k) acc[k] = dec * acc[k] + g[(size_t)m * D * D + tid + 256 * k];
+      for (int k = 0; k < PER; ++k)
+        if ((D * D) % NTH == 0 || tid + NTH * k < D * D) acc[k] = dec * acc[k] + g[(size_t)m * D * D + tid + NTH * k];
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int x = tid + 256 * k;
-      Sl[(x % D) * LDS + x / D] = acc[k];
+      const int x = tid + NTH * k;
+      if ((D * D) % NTH == 0 || x < D * D) Sl[(x % D) * LDS + x / D] = acc[k];
     }
   } else {
     const float* g = a.seg_state + ((size_t)bh * a.nseg + seg) * D * D;
-    for (int x = tid; x < D * D; x += 256) Sl[(x % D) * LDS + x / D] = g[x];
+    for (int x = tid; x < D * D; x += NTH) Sl[(x % D) * LDS + x / D] = g[x];
   }
 
   const int jb = seg * a.G;
   const int je = min(a.nblk, jb + a.G);
 
-  // Item stream.  Block j contributes, in order: its Q block (item 0, two
-  // 64-row halves written to the Q area), its window's key tiles (items
-  // 1..nb) and, when it evicts, the two tiles of its evicted chunk.
+  // Item stream.  Block j contributes, in order: its Q block (NQ items of
+  // 128 rows, each two 64-row halves written to the Q area), its window's key
+  // tiles (nb items) and, when it evicts, the BM/64 tiles of its evicted chunk.
   struct Blk {
     int t0, lo, nb, nit;
   };
   auto blk = [&](int j) {
     Blk b;
-    b.t0 = j * 128;
+    b.t0 = j * BM;
     b.lo = max(0, b.t0 - W + 1) >> 6;
-    const int hi = min(T - 1, b.t0 + 127) >> 6;
+    const int hi = min(T - 1, b.t0 + BM - 1) >> 6;
     b.nb = hi - b.lo + 1;
-    b.nit = 1 + b.nb + ((b.t0 + 127 >= W) ? 2 : 0);
+    b.nit = NQ + b.nb + ((b.t0 + BM - 1 >= W) ? BM / 64 : 0);
     return b;
   };
   // cursor of the item held in the staging registers
   int pj = jb, pidx = 0;
   Blk pb = blk(jb);
   int kv_stored = 0;  // key/value items written to LDS so far (buffer parity)
-  TileRegs<E, D, 64> kr, vr;
+  TileRegs<E, D, 64, NTH> kr, vr;
   auto load_next = [&]() {
-    const bool q = pidx == 0;
-    int r0 = q ? pb.t0 : (pidx <= pb.nb ? (pb.lo + pidx - 1) * 64 : pb.t0 - W + 64 * (pidx - 1 - pb.nb));
+    const bool q = pidx < NQ;
+    const int ki = pidx - NQ;
+    int r0 = q ? pb.t0 + 128 * pidx : (ki < pb.nb ? (pb.lo + ki) * 64 : pb.t0 - W + 64 * (ki - pb.nb));
     if (pj >= je) r0 = T + 64;  // past the end: reads zeros
     kr.load(q ? Qg : Kg, r0);
     vr.load(q ? Qg : Vg, q ? r0 + 64 : r0);
   };
   auto store_next = [&]() {
-    if (pidx == 0) {
-      kr.store(Qs, LDK);
-      vr.store(Qs + 64 * LDK, LDK);
+    if (pidx < NQ) {
+      kr.store(Qs + 128 * pidx * LDK, LDK);
+      vr.store(Qs + (128 * pidx + 64) * LDK, LDK);
     } else {
       E* bp = (E*)(smem + (kv_stored & 1) * L::BUF);
       kr.store(bp, LDK);
@@ -230,14 +268,22 @@ __global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(F
   for (int j = jb; j < je; ++j) {
     const Blk cb = blk(j);
     const int t0 = cb.t0, e0 = t0 - W;
-    const int nb = cb.nb, nkv = cb.nit - 1;
+    const int nb = cb.nb, nkv = cb.nit - NQ;
     const bool has_mem = nkv > nb;
     const bool last = (j == a.nblk - 1);
     const bool more = j + 1 < je;
     const int R0 = t0 + rw;  // first query row of this wave
 
-    // item 0: the Q block
+    // items 0 .. NQ-1: the Q block
+    for (int qi = 1; qi < NQ; ++qi) step();
     frag qf[2][NKC];
+    frag ones;
+    {
+      float o8[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) o8[x] = 1.0f;
+      ones = M::pack(o8);
+    }
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -246,11 +292,12 @@ __global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(F
     step();
 
     f32x4 O[2][NT];
-    float mrow[2], lrow[2];
+    float mrow[2];
+    f32x4 Lsum[2];  // row sums of P via the matrix core (element 0 is used)
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       mrow[g] = kNegInf;
-      lrow[g] = 0.0f;
+      Lsum[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt) O[g][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -275,8 +322,10 @@ __global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(F
           }
         }
       };
-      // O[g] += P[g] V with P[g][8 p + 4 (n & 1) + i] the weight of key 16 n + 4 lg + i
-      auto accum_pv = [&](const float (&P)[2][16]) {
+      // O[g] += P[g] V with P[g][8 p + 4 (n & 1) + i] the weight of key 16 n + 4 lg + i;
+      // with SUM also Lsum[g] += (row sums of P), from the same packed P
+      auto accum_pv = [&](const float (&P)[2][16], auto sum_c) {
+        constexpr bool SUM = decltype(sum_c)::value;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           float x0[8], x1[8];
@@ -286,6 +335,10 @@ __global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(F
             x1[jj] = P[1][8 * p + jj];
           }
           const frag p0 = M::pack(x0), p1 = M::pack(x1);
+          if (SUM) {
+            Lsum[0] = M::mma(ones, p0, Lsum[0]);
+            Lsum[1] = M::mma(ones, p1, Lsum[1]);
+          }
 #pragma unroll
           for (int dt = 0; dt < NT; ++dt) {
             const frag vf = VFrag<E>::read(Vb, LDV, 32 * p + 4 * lg, dt * 16, l16);
@@ -316,8 +369,8 @@ __global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(F
               for (int i = 0; i < 4; ++i) {
                 float z = Z[g][n][i];
                 if (!FULL) {
-                  const int key = k0 + 16 * n + 4 * lg + i;
-                  if (!(key <= trow && key > trow - W)) z = kNegInf;
+                    // key k0 + 16 n + 4 lg + i is in the window iff 0 <= trow - key < W
+                  if ((unsigned)(trow - k0 - 4 * lg - (16 * n + i)) >= (unsigned)W) z = kNegInf;
                 }
                 P[g][8 * (n >> 1) + 4 * (n & 1) + i] = z;
                 m = fmaxf(m, z);
@@ -331,7 +384,7 @@ __global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(F
             for (int g = 0; g < 2; ++g) {
               const float mnew = fmaxf(mrow[g], mz[g]);
               const float alpha = fast_exp2(mrow[g] - (mnew == kNegInf ? 0.0f : mnew));
-              lrow[g] *= alpha;
+              Lsum[g][0] *= alpha;
 #pragma unroll
               for (int dt = 0; dt < NT; ++dt) O[g][dt] *= alpha;
               mrow[g] = mnew;
@@ -340,15 +393,10 @@ __global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(F
 #pragma unroll
           for (int g = 0; g < 2; ++g) {
             const float ms = (mrow[g] == kNegInf) ? 0.0f : mrow[g];
-            float ps = 0.0f;
 #pragma unroll
-            for (int x = 0; x < 16; ++x) {
-              P[g][x] = fast_exp2(__builtin_fmaf(P[g][x], sl2, -ms));
-              ps += P[g][x];
-            }
-            lrow[g] += ps;
+            for (int x = 0; x < 16; ++x) P[g][x] = fast_exp2(__builtin_fmaf(P[g][x], sl2, -ms));
           }
-          accum_pv(P);
+          accum_pv(P, std::true_type{});
         };
         if (!skip) {
           if (full)
@@ -360,7 +408,7 @@ __global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(F
           // softmax done: normalise, then add the read of S(e0)
 #pragma unroll
           for (int g = 0; g < 2; ++g) {
-            const float l = xsum4(lrow[g]);
+            const float l = Lsum[g][0];
             const float inv = 1.0f / l;
 #pragma unroll
             for (int dt = 0; dt < NT; ++dt) O[g][dt] *= inv;
@@ -420,11 +468,11 @@ __global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(F
                 P[g][8 * (n >> 1) + 4 * (n & 1) + i] = w * Z[g][n][i];
               }
           }
-          accum_pv(P);
+          accum_pv(P, std::false_type{});
         }
         if (more || (last && a.A_final)) {
           const int len = more ? 64 : min(64, T - t0 - 64 * c);
-          if (len > 0) lds_state_update<E, D>(Sl, Kb, LDK, Vb, LDV, pw, len, ck0, wid, l16, lg);
+          if (len > 0) lds_state_update<E, D, NW>(Sl, Kb, LDK, Vb, LDV, pw, len, ck0, wid, l16, lg);
         }
       }
 
@@ -445,7 +493,7 @@ __global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(F
       float* Af = a.A_final + (size_t)bh * D * D;
       // the last item's barrier has published the final state
       const float eta = a.eta[h];
-      for (int x = tid; x < D * D; x += 256) Af[x] = has_mem ? eta * Sl[(x % D) * LDS + x / D] : 0.0f;
+      for (int x = tid; x < D * D; x += NTH) Af[x] = has_mem ? eta * Sl[(x % D) * LDS + x / D] : 0.0f;
     }
   }
 }
@@ -454,27 +502,33 @@ __global__ void __launch_bounds__(256, (sizeof(E) == 2 ? 2 : 1)) fwd128_kernel(F
 // workgroup reads at most this many D x D states, L2-resident) instead of a
 // separate chain kernel.
 constexpr int kDirectPrefixMaxSeg = 16;
+// Waves per workgroup of the bf16 kernel: 4 waves x 32 rows = 128-row blocks,
+// two workgroups per compute unit.  (Eight waves and 256-row blocks halve the
+// key/value tile traffic but run all eight waves in barrier lockstep at one
+// workgroup per unit, which measured slower.)
+constexpr int kRowWaves = 4;
 
 template <class E, int D>
-static hipError_t launch_fwd128_impl(const FwdArgs& a0, hipStream_t s) {
+static hipError_t launch_rows_impl(const FwdArgs& a0, hipStream_t s) {
+  constexpr int NW = kRowWaves, BM = 32 * NW;
   FwdArgs a = a0;
   const int BH = a.B * a.H;
   a.prefix_direct = a.nseg <= kDirectPrefixMaxSeg ? 1 : 0;
   if (a.nseg > 1) {
-    hipLaunchKernelGGL((seg_state_kernel<E, D, 128>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((seg_state_kernel<E, D, BM>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
     if (!a.prefix_direct)
-      hipLaunchKernelGGL((seg_chain_kernel<D, 128>), dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((seg_chain_kernel<D, BM>), dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, s, a);
   }
-  hipLaunchKernelGGL((fwd128_kernel<E, D>), dim3(BH * a.nseg), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW>), dim3(BH * a.nseg), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_forward128(const FwdArgs& a, int D, bool is_bf16, hipStream_t s) {
+hipError_t launch_forward_rows(const FwdArgs& a, int D, bool is_bf16, hipStream_t s) {
   if (!is_bf16) return hipErrorInvalidValue;
   switch (D) {
-    case 16: return launch_fwd128_impl<bf16, 16>(a, s);
-    case 32: return launch_fwd128_impl<bf16, 32>(a, s);
-    case 64: return launch_fwd128_impl<bf16, 64>(a, s);
+    case 16: return launch_rows_impl<bf16, 16>(a, s);
+    case 32: return launch_rows_impl<bf16, 32>(a, s);
+    case 64: return launch_rows_impl<bf16, 64>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -71,7 +71,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_forward(const FwdArgs& a, int D, bool is_bf16, hipStream_t s);     // 64-row blocks: float32, and bf16 with D = 128
-hipError_t launch_forward128(const FwdArgs& a, int D, bool is_bf16, hipStream_t s);  // 128-row blocks: bf16 with D <= 64
+hipError_t launch_forward_rows(const FwdArgs& a, int D, bool is_bf16, hipStream_t s);  // 128-row blocks: bf16 with D <= 64
 hipError_t launch_decode(const DecArgs& a, int D, bool is_bf16, hipStream_t s);
 hipError_t launch_backward_bf16(const BwdArgs& a, int D, hipStream_t s);
 hipError_t launch_backward_f32(const BwdArgs& a, int D, hipStream_t s);
