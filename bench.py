@@ -28,6 +28,45 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+CSRC = os.path.join(ROOT, "eviction_fed_weight_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_pmc.txt")
+
+
+def csrc_digest():
+    """sha256 over the library's HIP sources (names and bytes, sorted)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per call of each leg from the committed profiler summary
+    (FETCH_SIZE and WRITE_SIZE runs, scaled by a copy of known size), or {}
+    when the kernels changed after the counters were taken."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return {}
+    kv = {}
+    for ln in lines:
+        if ":" in ln and not ln.startswith("#"):
+            k, v = ln.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("csrc_sha256") != csrc_digest():
+        return {}
+    out = {}
+    for leg in ("prefill", "long", "decode", "backward"):
+        key = "%s_bytes_per_call" % leg
+        if key in kv:
+            out[leg] = float(kv[key])
+    return out
+
+
 def fwd_flops(B, H, T, D, W, C):
     """Algorithmic forward FLOPs: band QK^T+PV (4D per pair) plus the memory
     write (2D^2), read (2D^2) and intra-chunk triangle (2D(C+1)) per evicted
@@ -96,7 +135,8 @@ def prefill_leg(cfg_id, steps, warmup):
         workload="prefill B=%d H=%d D=%d T=%d W=%d C=%d bf16" % (cfg.B, cfg.H, cfg.D, cfg.T, cfg.W, cfg.C),
         ms_per_call=ms, tokens_per_s=cfg.B * cfg.T / (ms * 1e-3), flops=fl, bytes=by,
         roofline=dict(bound="mfma", achieved=tflops, peak=PEAK_BF16, unit="TFLOP/s", frac=tflops / PEAK_BF16,
-                      traffic=None, kernel="tc_forward (seg_state + seg_chain + fwd kernels)"),
+                      traffic=measured_traffic().get("prefill" if cfg_id == 2 else "long"),
+                      kernel="one tc_forward call (seg_state_kernel [+ seg_chain_kernel] + fwd_kernel_rows)"),
         hbm_gbs=by / (ms * 1e-3) / 1e9,
     )
 
@@ -154,7 +194,8 @@ def decode_leg(steps, warmup):
     return dict(workload="decode S=%d H=%d D=%d W=%d bf16, %d consecutive steps" % (S, H, D, W, n),
                 ms_per_step=ms, steps_per_s=1e3 / ms, tokens_per_s=S * 1e3 / ms, bytes=by,
                 roofline=dict(bound="hbm", achieved=gbs, peak=PEAK_HBM, unit="GB/s", frac=gbs / PEAK_HBM,
-                              traffic=None, kernel="decode_kernel + pos_advance_kernel"))
+                              traffic=measured_traffic().get("decode"),
+                              kernel="one tc_decode_step call (decode_kernel + pos_advance_kernel)"))
 
 
 def backward_leg(steps, warmup):
@@ -184,7 +225,8 @@ def backward_leg(steps, warmup):
     return dict(workload="backward B=%d H=%d D=%d T=%d W=%d C=%d bf16" % (cfg.B, cfg.H, cfg.D, cfg.T, cfg.W, cfg.C),
                 ms_per_call=ms, tokens_per_s=cfg.B * cfg.T / (ms * 1e-3), flops=fl,
                 roofline=dict(bound="mfma", achieved=tflops, peak=PEAK_BF16, unit="TFLOP/s", frac=tflops / PEAK_BF16,
-                              traffic=None, kernel="tc_backward (segment passes + dq + dkdv + reduce)"))
+                              traffic=measured_traffic().get("backward"),
+                              kernel="one tc_backward call (segment passes + dq_kernel + dkdv_kernel + reduce)"))
 
 
 def calib_leg(steps, warmup, mib=256):
@@ -275,6 +317,7 @@ def main():
         bw = backward_leg(max(3, args.steps // 5), 2)
         log("  backward", json.dumps(bw))
         out["backward"] = bw
+    out["csrc_sha256"] = csrc_digest()
     if "calib" in legs:
         log("copy calibration leg ...")
         cb = calib_leg(args.steps, args.warmup)

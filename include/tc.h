@@ -114,6 +114,8 @@ tc_status_t tc_forward(const tc_shape_t* shape, const void* q, const void* k, co
  *   y        [S,H,D] dtype, out.
  * Rings, A and pos are updated in place, so successive calls need no host
  * work between them (the sequence can be captured in a HIP graph).
+ * One (stream, head) ring must stay below 2 GiB ((W + 512) * D * element
+ * size < 2^31), else TC_ERR_UNSUPPORTED.
  */
 tc_status_t tc_decode_step(const tc_decode_shape_t* shape, const void* q, const void* k,
                            const void* v, void* k_ring, void* v_ring, float* A, int64_t* pos,
