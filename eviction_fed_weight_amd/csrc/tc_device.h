@@ -253,6 +253,18 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return x * q + (x < r ? x : r) + (b >> 3);
 }
 
+// xcd_remap with the second half of each XCD's range in reverse order.  An
+// XCD fills each compute unit's first slot before its second, so the two
+// workgroups that share a unit get indices u and nx - 1 - u of the range: with
+// one head's segments (light ones first) contiguous, a heavy segment then
+// shares its unit with a light one.
+__device__ __forceinline__ int xcd_remap_paired(int b, int n) {
+  const int x = b & 7, q = n >> 3, r = n & 7;
+  const int nx = q + (x < r ? 1 : 0), bx = x * q + (x < r ? x : r);
+  const int u = b >> 3, hh = nx >> 1;
+  return bx + (u < hh ? u : hh + (nx - 1 - u));
+}
+
 // Compiler-visible s_waitcnt vmcnt(0): marks every earlier vector-memory load
 // complete for the compiler's own wait analysis (used after loads that feed
 // loop-carried registers, so the loop body needs no conservative full waits).

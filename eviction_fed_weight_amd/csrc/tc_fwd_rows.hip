@@ -21,9 +21,11 @@
 // chunk -- through a two-buffer LDS pipeline with one barrier per item.
 // While an item is computed from one buffer, the next item (already in
 // registers) is written to the other and the item after it is being loaded.
-// Every key/value tile fetched serves all BM rows of the block, so the
-// window's overlap between neighbouring blocks is re-read (W + BM) / BM
-// times per row instead of (W + 64) / 64.
+// Workgroups are renumbered so one head's segments run on one XCD (shared L2
+// for the overlapping window rows) and a heavy segment shares its compute
+// unit with a light one.  Every key/value tile fetched serves all BM rows of
+// the block, so the window's overlap between neighbouring blocks is re-read
+// (W + BM) / BM times per row instead of (W + 64) / 64.
 //
 // Per wave and item: scores for 32 rows x 64 keys (16 MFMAs; every K
 // fragment read from LDS feeds both 16-row groups), softmax on the
@@ -161,7 +163,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   constexpr int LDS = L::LDS;
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int wg = xcd_remap_paired(blockIdx.x, gridDim.x);
   const int bh = wg / a.nseg, seg = wg - bh * a.nseg;
   const int h = bh % a.H;
   const int T = a.T, W = a.W;
@@ -173,36 +175,6 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   E* Yg = (E*)a.y + base;
   const float seta = sigmoidf(a.gate[h]) * a.eta[h];
   const float sl2 = a.scale * kLog2e;
-  if (tid <= BM) pw[tid] = powi(a.lam[h], tid);
-
-  // S(e0) of the segment's first block -> LDS (transposed)
-  if (seg == 0) {
-    for (int x = tid; x < D * D; x += NTH) Sl[(x % D) * LDS + x / D] = 0.0f;
-  } else if (a.prefix_direct) {
-    // S at the segment start from the local states L_m (stored at index m+1):
-    // S = sum_{m < seg} lambda^((seg-1-m) BM G) L_m, in chain order
-    constexpr int PER = (D * D + NTH - 1) / NTH;
-    const float dec = powi(a.lam[h], BM * a.G);
-    const float* g = a.seg_state + (size_t)bh * a.nseg * D * D;
-    float acc[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
-#pragma unroll 4
-    for (int m = 1; m <= seg; ++m) {
-#pragma unroll
-      for (int k = 0; k < PER; ++k)
-        if ((D * D) % NTH == 0 || tid + NTH * k < D * D) acc[k] = dec * acc[k] + g[(size_t)m * D * D + tid + NTH * k];
-    }
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int x = tid + NTH * k;
-      if ((D * D) % NTH == 0 || x < D * D) Sl[(x % D) * LDS + x / D] = acc[k];
-    }
-  } else {
-    const float* g = a.seg_state + ((size_t)bh * a.nseg + seg) * D * D;
-    for (int x = tid; x < D * D; x += NTH) Sl[(x % D) * LDS + x / D] = g[x];
-  }
-
   const int jb = seg * a.G;
   const int je = min(a.nblk, jb + a.G);
 
@@ -260,7 +232,38 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
     __syncthreads();
   };
 
-  load_next();
+  load_next();  // the first item's loads overlap the state set-up below
+
+  if (tid <= BM) pw[tid] = powi(a.lam[h], tid);
+
+  // S(e0) of the segment's first block -> LDS (transposed)
+  if (seg == 0) {
+    for (int x = tid; x < D * D; x += NTH) Sl[(x % D) * LDS + x / D] = 0.0f;
+  } else if (a.prefix_direct) {
+    // S at the segment start from the local states L_m (stored at index m+1):
+    // S = sum_{m < seg} lambda^((seg-1-m) BM G) L_m, in chain order
+    constexpr int PER = (D * D + NTH - 1) / NTH;
+    const float dec = powi(a.lam[h], BM * a.G);
+    const float* g = a.seg_state + (size_t)bh * a.nseg * D * D;
+    float acc[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
+#pragma unroll 4
+    for (int m = 1; m <= seg; ++m) {
+#pragma unroll
+      for (int k = 0; k < PER; ++k)
+        if ((D * D) % NTH == 0 || tid + NTH * k < D * D) acc[k] = dec * acc[k] + g[(size_t)m * D * D + tid + NTH * k];
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int x = tid + NTH * k;
+      if ((D * D) % NTH == 0 || x < D * D) Sl[(x % D) * LDS + x / D] = acc[k];
+    }
+  } else {
+    const float* g = a.seg_state + ((size_t)bh * a.nseg + seg) * D * D;
+    for (int x = tid; x < D * D; x += NTH) Sl[(x % D) * LDS + x / D] = g[x];
+  }
+
   step();
 
   int kv_used = 0;  // key/value items consumed (buffer parity)
