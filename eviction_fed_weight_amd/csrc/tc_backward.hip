@@ -407,7 +407,8 @@ __global__ void __launch_bounds__(256, 1) dq_kernel(BwdArgs a) {
   E* Ys = (E*)(smem + C::U + C::TILE);
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
-  const int bh = blockIdx.x / a.nseg, seg = blockIdx.x - bh * a.nseg;
+  const int wgi = xcd_remap(blockIdx.x, gridDim.x);  // one head's segments on one XCD
+  const int bh = wgi / a.nseg, seg = wgi - bh * a.nseg;
   const int h = bh % a.H;
   const int T = a.T, W = a.W;
   const size_t base = (size_t)bh * T * D;
@@ -482,7 +483,7 @@ __global__ void __launch_bounds__(256, 1) dq_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float v = sum4(yp[g]);
+          const float v = xsum4(yp[g]);
           if (lg == 0) ypart[wid][g * 16 + l16] = v;
         }
         __syncthreads();
@@ -496,7 +497,7 @@ __global__ void __launch_bounds__(256, 1) dq_kernel(BwdArgs a) {
           for (int i = 0; i < 4; ++i) qx += (float)qrow[i] * xv[i];
           dQ[dt] += (seta * f) * xv;
         }
-        qx = sum4(qx);
+        qx = xsum4(qx);
         const float qy = ypart[0][r] + ypart[1][r] + ypart[2][r] + ypart[3][r];
         md += f * qx;
         dlr += df * qx + f * qy;
@@ -542,8 +543,8 @@ __global__ void __launch_bounds__(256, 1) dq_kernel(BwdArgs a) {
         for (int dt = 0; dt < NT; ++dt)
           dQ[dt] = M::mma(ColFrag<E>::read(Ks + (p * 32 + lg * 8) * LDK + dt * 16, LDK, l16), gf, dQ[dt]);
       }
-      md += sum4(mp);
-      dlr += sum4(dp);
+      md += xsum4(mp);
+      dlr += xsum4(dp);
       // carry S and B to the next block of this segment
       if (j + 1 < je) {
         __shared__ float w1[64], w2[64];
@@ -570,7 +571,7 @@ __global__ void __launch_bounds__(256, 1) dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int x = 0; x < VE; ++x) yd += (float)ye[x] * (float)dy[x];
     }
-    yd = sum4(yd);
+    yd = xsum4(yd);
     const float delta = yd - seta * md;
     if (lg == 0 && trow < T) a.delta[(size_t)bh * T + trow] = delta;
     const float lse2 = (trow < T) ? a.lse[(size_t)bh * T + trow] * kLog2e : __builtin_huge_valf();
@@ -613,7 +614,7 @@ __global__ void __launch_bounds__(256, 1) dq_kernel(BwdArgs a) {
           const bool band = full || (key <= trow && key > trow - W);
           const float z = Z[2 * p + (jj >> 2)][jj & 3];
           const float dpv = P[2 * p + (jj >> 2)][jj & 3];
-          const float pr = band ? exp2f(__builtin_fmaf(z, sl2, -lse2)) : 0.0f;
+          const float pr = band ? fast_exp2(__builtin_fmaf(z, sl2, -lse2)) : 0.0f;
           gv[jj] = tau * pr * (dpv - delta);
         }
         const frag gf = M::pack(gv);
@@ -669,7 +670,8 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
   float* X = (float*)(smem + 2 * C::TILE);
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
-  const int bh = blockIdx.x / a.nseg, seg = blockIdx.x - bh * a.nseg;
+  const int wgi = xcd_remap(blockIdx.x, gridDim.x);  // one head's segments on one XCD
+  const int bh = wgi / a.nseg, seg = wgi - bh * a.nseg;
   const int h = bh % a.H;
   const int T = a.T, W = a.W;
   const size_t base = (size_t)bh * T * D;
@@ -846,7 +848,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
           const int rr = g * 16 + lg * 4 + (jj & 3);
           const int t = q0 + rr;
           const bool band = full || (key <= t && key > t - W && t < T);
-          const float pr = band ? exp2f(__builtin_fmaf(Z[g][jj & 3], sl2, -lse_s[rr])) : 0.0f;
+          const float pr = band ? fast_exp2(__builtin_fmaf(Z[g][jj & 3], sl2, -lse_s[rr])) : 0.0f;
           pv[jj] = pr;
           gv[jj] = tau * pr * (P[g][jj & 3] - del_s[rr]);
         }
