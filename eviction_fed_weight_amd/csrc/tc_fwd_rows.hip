@@ -155,7 +155,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   using L = FRows<E, D, NW>;
   constexpr int NT = L::NT, NKC = L::NKC, LDK = L::LDK, LDV = L::LDV;
   constexpr int NTH = L::NTH, BM = L::BM, NQ = L::NQ;
-  static_assert(D <= 64 && NW >= 4 && NW % 4 == 0, "shape");
+  static_assert(D <= 64 && NW == 4, "128-row blocks: the two chunk tiles fit the two buffers");
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
   __shared__ float pw[BM + 4];
   E* Qs = (E*)(smem + 2 * L::BUF);
@@ -181,18 +181,36 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   // Item stream.  Block j contributes, in order: its Q block (NQ items of
   // 128 rows, each two 64-row halves written to the Q area), its window's key
   // tiles (nb items) and, when it evicts, the BM/64 tiles of its evicted chunk.
+  // Key tiles of block j start at kb = t0 - W (not at multiples of 64): tile i
+  // holds keys kb + 64 i .. kb + 64 i + 63, so tiles 0 and 1 are exactly the
+  // block's evicted chunk.  A block that evicts visits its window tiles
+  // 2 .. ihi first and tiles 0 and 1 last; after the last one (softmax done)
+  // both chunk tiles are still in the two LDS buffers for the memory read and
+  // the state update, so the chunk costs no items of its own.
   struct Blk {
-    int t0, lo, nb, nit;
+    int t0, kb, ilo, nfront, nlate, nb, nit;
+    bool mem;
   };
   auto blk = [&](int j) {
     Blk b;
     b.t0 = j * BM;
-    b.lo = max(0, b.t0 - W + 1) >> 6;
-    const int hi = min(T - 1, b.t0 + BM - 1) >> 6;
-    b.nb = hi - b.lo + 1;
-    b.nit = NQ + b.nb + ((b.t0 + BM - 1 >= W) ? BM / 64 : 0);
+    b.kb = b.t0 - W;
+    const int ihi = (min(T - 1, b.t0 + BM - 1) - b.kb) >> 6;  // last tile with a key in range
+    b.mem = b.t0 + BM - 1 >= W;
+    if (b.mem) {
+      b.nlate = min(2, ihi + 1);
+      b.ilo = 2;
+      b.nfront = ihi + 1 - b.nlate;
+    } else {
+      b.nlate = 0;
+      b.ilo = (-b.kb - 63 > 0) ? ((-b.kb) >> 6) : 0;  // first tile with a key >= 0
+      b.nfront = ihi - b.ilo + 1;
+    }
+    b.nb = b.nfront + b.nlate;
+    b.nit = NQ + b.nb;
     return b;
   };
+  auto tile_of = [&](const Blk& b, int idx) { return idx < b.nfront ? b.ilo + idx : idx - b.nfront; };
   // cursor of the item held in the staging registers
   int pj = jb, pidx = 0;
   Blk pb = blk(jb);
@@ -201,7 +219,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   auto load_next = [&]() {
     const bool q = pidx < NQ;
     const int ki = pidx - NQ;
-    int r0 = q ? pb.t0 + 128 * pidx : (ki < pb.nb ? (pb.lo + ki) * 64 : pb.t0 - W + 64 * (ki - pb.nb));
+    int r0 = q ? pb.t0 + 128 * pidx : pb.kb + 64 * tile_of(pb, ki);
     if (pj >= je) r0 = T + 64;  // past the end: reads zeros
     kr.load(q ? Qg : Kg, r0);
     vr.load(q ? Qg : Vg, q ? r0 + 64 : r0);
@@ -271,8 +289,8 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   for (int j = jb; j < je; ++j) {
     const Blk cb = blk(j);
     const int t0 = cb.t0, e0 = t0 - W;
-    const int nb = cb.nb, nkv = cb.nit - NQ;
-    const bool has_mem = nkv > nb;
+    const int nb = cb.nb;
+    const bool has_mem = cb.mem;
     const bool last = (j == a.nblk - 1);
     const bool more = j + 1 < je;
     const int R0 = t0 + rw;  // first query row of this wave
@@ -305,66 +323,68 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
       for (int dt = 0; dt < NT; ++dt) O[g][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    for (int it = 0; it < nkv; ++it) {
+    // scores Z[g][n][i] = <q_row, k_key>, row = R0 + 16 g + l16,
+    // key = tile row 16 n + 4 lg + i of the K tile at Kt
+    auto scores = [&](f32x4 (&Z)[2][4], const E* Kt) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        Z[0][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Z[1][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < NKC; ++dc) {
+          const frag ka =
+              (dc * 32 + lg * 8 < D) ? M::lds8(Kt + (16 * n + l16) * LDK + dc * 32 + lg * 8) : M::zero();
+          Z[0][n] = M::mma(ka, qf[0][dc], Z[0][n]);
+          Z[1][n] = M::mma(ka, qf[1][dc], Z[1][n]);
+        }
+      }
+    };
+    // O[g] += P[g] V with P[g][8 p + 4 (n & 1) + i] the weight of key 16 n + 4 lg + i;
+    // with SUM also Lsum[g] += (row sums of P), from the same packed P; V tile at Vt
+    auto accum_pv = [&](const float (&P)[2][16], auto sum_c, const E* Vt) {
+      constexpr bool SUM = decltype(sum_c)::value;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        float x0[8], x1[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          x0[jj] = P[0][8 * p + jj];
+          x1[jj] = P[1][8 * p + jj];
+        }
+        const frag p0 = M::pack(x0), p1 = M::pack(x1);
+        if (SUM) {
+          Lsum[0] = M::mma(ones, p0, Lsum[0]);
+          Lsum[1] = M::mma(ones, p1, Lsum[1]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) {
+          const frag vf = VFrag<E>::read(Vt, LDV, 32 * p + 4 * lg, dt * 16, l16);
+          O[0][dt] = M::mma(vf, p0, O[0][dt]);
+          O[1][dt] = M::mma(vf, p1, O[1][dt]);
+        }
+      }
+    };
+
+    for (int it = 0; it < nb; ++it) {
       const E* Kb = (const E*)(smem + (kv_used & 1) * L::BUF);
       const E* Vb = (const E*)(smem + (kv_used & 1) * L::BUF + L::KT);
 
-      // scores Z[g][n][i] = <q_row, k_key>, row = R0 + 16 g + l16,
-      // key = tile row 16 n + 4 lg + i
-      auto scores = [&](f32x4 (&Z)[2][4]) {
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          Z[0][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-          Z[1][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int dc = 0; dc < NKC; ++dc) {
-            const frag ka =
-                (dc * 32 + lg * 8 < D) ? M::lds8(Kb + (16 * n + l16) * LDK + dc * 32 + lg * 8) : M::zero();
-            Z[0][n] = M::mma(ka, qf[0][dc], Z[0][n]);
-            Z[1][n] = M::mma(ka, qf[1][dc], Z[1][n]);
-          }
-        }
-      };
-      // O[g] += P[g] V with P[g][8 p + 4 (n & 1) + i] the weight of key 16 n + 4 lg + i;
-      // with SUM also Lsum[g] += (row sums of P), from the same packed P
-      auto accum_pv = [&](const float (&P)[2][16], auto sum_c) {
-        constexpr bool SUM = decltype(sum_c)::value;
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          float x0[8], x1[8];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            x0[jj] = P[0][8 * p + jj];
-            x1[jj] = P[1][8 * p + jj];
-          }
-          const frag p0 = M::pack(x0), p1 = M::pack(x1);
-          if (SUM) {
-            Lsum[0] = M::mma(ones, p0, Lsum[0]);
-            Lsum[1] = M::mma(ones, p1, Lsum[1]);
-          }
-#pragma unroll
-          for (int dt = 0; dt < NT; ++dt) {
-            const frag vf = VFrag<E>::read(Vb, LDV, 32 * p + 4 * lg, dt * 16, l16);
-            O[0][dt] = M::mma(vf, p0, O[0][dt]);
-            O[1][dt] = M::mma(vf, p1, O[1][dt]);
-          }
-        }
-      };
-
-      if (it < nb) {
+      {
         // ---- window tile: keys k0 .. k0+63 ----
-        const int k0 = (cb.lo + it) * 64;
-        const bool skip = (k0 > R0 + 31) || (k0 + 63 <= R0 - W);
-        const bool full = (k0 + 63 <= R0) && (k0 >= R0 + 32 - W);
+        const int k0 = cb.kb + 64 * tile_of(cb, it);
+        // (tiles of early blocks may start before token 0: those keys are masked)
+        const bool skip = (k0 > R0 + 31) || (k0 + 63 <= R0 - W) || (k0 + 63 < 0);
+        const bool full = (k0 + 63 <= R0) && (k0 >= R0 + 32 - W) && (k0 >= 0);
         auto tile = [&](auto full_c) {
           constexpr bool FULL = decltype(full_c)::value;
           f32x4 Z[2][4];
-          scores(Z);
+          scores(Z, Kb);
           float P[2][16];
           float mz[2];
 #pragma unroll
           for (int g = 0; g < 2; ++g) {
             const int trow = R0 + 16 * g + l16;
+            const unsigned wr = (unsigned)min(W, trow + 1);  // window of trow: keys trow - wr + 1 .. trow, all >= 0
             float m = kNegInf;
 #pragma unroll
             for (int n = 0; n < 4; ++n)
@@ -372,8 +392,8 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
               for (int i = 0; i < 4; ++i) {
                 float z = Z[g][n][i];
                 if (!FULL) {
-                    // key k0 + 16 n + 4 lg + i is in the window iff 0 <= trow - key < W
-                  if ((unsigned)(trow - k0 - 4 * lg - (16 * n + i)) >= (unsigned)W) z = kNegInf;
+                  // key k0 + 16 n + 4 lg + i is in the window iff 0 <= trow - key < min(W, trow + 1)
+                  if ((unsigned)(trow - k0 - 4 * lg - (16 * n + i)) >= wr) z = kNegInf;
                 }
                 P[g][8 * (n >> 1) + 4 * (n & 1) + i] = z;
                 m = fmaxf(m, z);
@@ -399,7 +419,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
 #pragma unroll
             for (int x = 0; x < 16; ++x) P[g][x] = fast_exp2(__builtin_fmaf(P[g][x], sl2, -ms));
           }
-          accum_pv(P, std::true_type{});
+          accum_pv(P, std::true_type{}, Vb);
         };
         if (!skip) {
           if (full)
@@ -407,81 +427,95 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
           else
             tile(std::false_type{});
         }
-        if (it == nb - 1) {
-          // softmax done: normalise, then add the read of S(e0)
-#pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            const float l = Lsum[g][0];
-            const float inv = 1.0f / l;
-#pragma unroll
-            for (int dt = 0; dt < NT; ++dt) O[g][dt] *= inv;
-            const int trow = R0 + 16 * g + l16;
-            if (a.lse && lg == 0 && trow < T) a.lse[(size_t)bh * T + trow] = (mrow[g] + __log2f(l)) * kLn2;
-          }
-          if (has_mem && e0 > 0) {
-            // O += sigma(g) eta lambda^(r+1) q S(e0), S^T read from LDS as hi/lo bf16
-#pragma unroll
-            for (int dt = 0; dt < NT; ++dt) {
-              f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-              for (int dc = 0; dc < NKC; ++dc) {
-                const bool in = dc * 32 + lg * 8 < D;  // D = 16: upper half of the contraction is empty
-                float sv[8];
-                {
-                  const float* p = Sl + (dt * 16 + l16) * LDS + dc * 32 + lg * 8;
-                  const f32x4 x0 = in ? *(const f32x4*)p : f32x4{0.f, 0.f, 0.f, 0.f};
-                  const f32x4 x1 = in ? *(const f32x4*)(p + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                  for (int i = 0; i < 4; ++i) {
-                    sv[i] = x0[i];
-                    sv[4 + i] = x1[i];
-                  }
-                }
-                frag shi, slo;
-                M::split(sv, shi, slo);
-                acc[0] = M::mma(shi, qf[0][dc], acc[0]);
-                acc[1] = M::mma(shi, qf[1][dc], acc[1]);
-                if (M::kSplit) {
-                  acc[0] = M::mma(slo, qf[0][dc], acc[0]);
-                  acc[1] = M::mma(slo, qf[1][dc], acc[1]);
-                }
-              }
-#pragma unroll
-              for (int g = 0; g < 2; ++g) O[g][dt] += (seta * pw[rw + 16 * g + l16 + 1]) * acc[g];
-            }
-          }
-        }
-      } else {
-        // ---- tile c of the evicted chunk: keys e0 + 64 c .. +63 ----
-        const int c = it - nb;
-        const int ck0 = e0 + 64 * c;
-        if (64 * c <= rw + 31) {
-          f32x4 Z[2][4];
-          scores(Z);
-          float P[2][16];
-#pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            const int r = rw + 16 * g + l16;  // row within the block
-#pragma unroll
-            for (int n = 0; n < 4; ++n)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int ci = 64 * c + 16 * n + 4 * lg + i;  // index within the chunk
-                const float w = (ci <= r && e0 + ci >= 0) ? seta * pw[r - ci] : 0.0f;
-                P[g][8 * (n >> 1) + 4 * (n & 1) + i] = w * Z[g][n][i];
-              }
-          }
-          accum_pv(P, std::false_type{});
-        }
-        if (more || (last && a.A_final)) {
-          const int len = more ? 64 : min(64, T - t0 - 64 * c);
-          if (len > 0) lds_state_update<E, D, NW>(Sl, Kb, LDK, Vb, LDV, pw, len, ck0, wid, l16, lg);
-        }
       }
-
       ++kv_used;
       step();
     }
+
+    // ---- after the window: normalise, read S(e0), the evicted chunk, the state ----
+    // (the last step wrote only the Q area: both chunk tiles are still in the buffers)
+      // softmax done: normalise, then add the read of S(e0)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const float l = Lsum[g][0];
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) O[g][dt] *= inv;
+        const int trow = R0 + 16 * g + l16;
+        if (a.lse && lg == 0 && trow < T) a.lse[(size_t)bh * T + trow] = (mrow[g] + __log2f(l)) * kLn2;
+      }
+      if (has_mem && e0 > 0) {
+        // O += sigma(g) eta lambda^(r+1) q S(e0), S^T read from LDS as hi/lo bf16
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) {
+          f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+          for (int dc = 0; dc < NKC; ++dc) {
+            const bool in = dc * 32 + lg * 8 < D;  // D = 16: upper half of the contraction is empty
+            float sv[8];
+            {
+              const float* p = Sl + (dt * 16 + l16) * LDS + dc * 32 + lg * 8;
+              const f32x4 x0 = in ? *(const f32x4*)p : f32x4{0.f, 0.f, 0.f, 0.f};
+              const f32x4 x1 = in ? *(const f32x4*)(p + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                sv[i] = x0[i];
+                sv[4 + i] = x1[i];
+              }
+            }
+            frag shi, slo;
+            M::split(sv, shi, slo);
+            acc[0] = M::mma(shi, qf[0][dc], acc[0]);
+            acc[1] = M::mma(shi, qf[1][dc], acc[1]);
+            if (M::kSplit) {
+              acc[0] = M::mma(slo, qf[0][dc], acc[0]);
+              acc[1] = M::mma(slo, qf[1][dc], acc[1]);
+            }
+          }
+#pragma unroll
+          for (int g = 0; g < 2; ++g) O[g][dt] += (seta * pw[rw + 16 * g + l16 + 1]) * acc[g];
+        }
+      }
+      if (has_mem) {
+        // the evicted chunk: tiles 0 and 1 were the last nlate items, still in the two buffers
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          if (c < cb.nlate && 64 * c <= rw + 31) {
+            const int ub = kv_used - cb.nlate + c;  // kv index of chunk tile c
+            const E* Kc = (const E*)(smem + (ub & 1) * L::BUF);
+            const E* Vc = (const E*)(smem + (ub & 1) * L::BUF + L::KT);
+            f32x4 Z[2][4];
+            scores(Z, Kc);
+            float P[2][16];
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+              const int r = rw + 16 * g + l16;  // row within the block
+#pragma unroll
+              for (int n = 0; n < 4; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int ci = 64 * c + 16 * n + 4 * lg + i;  // index within the chunk
+                  const float w = (ci <= r && e0 + ci >= 0) ? seta * pw[r - ci] : 0.0f;
+                  P[g][8 * (n >> 1) + 4 * (n & 1) + i] = w * Z[g][n][i];
+                }
+            }
+            accum_pv(P, std::false_type{}, Vc);
+          }
+        }
+        if (more || (last && a.A_final)) {
+          __syncthreads();  // every wave has read S(e0)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int len = more ? 64 : min(64, T - t0 - 64 * c);
+            if (c < cb.nlate && len > 0) {
+              const int ub = kv_used - cb.nlate + c;  // kv index of chunk tile c
+              const E* Kc = (const E*)(smem + (ub & 1) * L::BUF);
+              const E* Vc = (const E*)(smem + (ub & 1) * L::BUF + L::KT);
+              lds_state_update<E, D, NW>(Sl, Kc, LDK, Vc, LDV, pw, len, e0 + 64 * c, wid, l16, lg);
+            }
+          }
+        }
+      }
 
     // ---- store y ----
 #pragma unroll
@@ -494,7 +528,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
     }
     if (last && a.A_final) {
       float* Af = a.A_final + (size_t)bh * D * D;
-      // the last item's barrier has published the final state
+      __syncthreads();  // the state updates above are done
       const float eta = a.eta[h];
       for (int x = tid; x < D * D; x += NTH) Af[x] = has_mem ? eta * Sl[(x % D) * LDS + x / D] : 0.0f;
     }

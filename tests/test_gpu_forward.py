@@ -109,6 +109,30 @@ def test_forward_multi_segment_walk_bf16():
         assert e <= TOL["bf16"], (key, e)
 
 
+@pytest.mark.parametrize("T", [2048, 2048 + 50])
+def test_forward_segment_prefix_paths(T):
+    """bf16 D=64 with one block per segment: 16 segments (the fused kernel
+    combines the local segment states itself) and 17 with a ragged last block
+    (the chain kernel combines them)."""
+    say("forward segment prefix", T)
+    d = tc_inputs.prefill_inputs(2, seed=21, B=1, H=2, T=T, D=64, W=300, dtype="bf16", plants=False)
+    err = run_and_compare(d, 300)
+    say("  errors", err)
+    for key, e in err.items():
+        assert e <= TOL["bf16"], (key, e)
+
+
+def test_forward_blocks_per_segment_bf16():
+    """Many heads, short sequences: each workgroup walks several 128-row
+    blocks, carrying the state through its chunk updates."""
+    say("forward several blocks per segment")
+    d = tc_inputs.prefill_inputs(2, seed=22, B=4, H=64, T=1024, D=64, W=200, dtype="bf16", plants=False)
+    err = run_and_compare(d, 200, heads=[(0, 0), (1, 33), (3, 63)])
+    say("  errors", err)
+    for key, e in err.items():
+        assert e <= TOL["bf16"], (key, e)
+
+
 def test_forward_config1_tiny_fp32():
     d = tc_inputs.prefill_inputs(1)
     err = run_and_compare(d, 8, C=8)
