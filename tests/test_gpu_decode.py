@@ -105,3 +105,47 @@ def test_decode_config4_full_launch_sampled_streams():
         assert rel(host(A[s:s + 1]), ref[s]["A"]) <= TOL["bf16"]
         assert np.array_equal(host(kr[s:s + 1]), ref[s]["kr"])
     assert torch.all(pos == cfg.prior + W + steps)
+
+
+def test_decode_mixed_stream_positions():
+    """Streams at different positions in one call: one warming up (pos < W),
+    one about to fill its ring, one several wraps in (evicting every step)."""
+    S, H, D, W, dtype = 3, 2, 64, 48, "bf16"
+    prefix = [0, W - 1, 3 * W + 5]
+    steps = 60
+    say("decode mixed positions", prefix)
+    rng = np.random.default_rng(77)
+    n = max(prefix) + steps
+    toks = [tc_inputs.bf16_round(rng.standard_normal((n, S, H, D)).astype(np.float32)) for _ in range(3)]
+    lam, eta, g = tc_inputs.head_params(rng, rng, rng, H)
+    okr = np.zeros((S, H, W, D))
+    ovr = np.zeros((S, H, W, D))
+    oA = np.zeros((S, H, D, D))
+    opos = np.zeros(S, np.int64)
+    # bring each stream to its start position with the oracle alone
+    for s in range(S):
+        for t in range(prefix[s]):
+            oracle.decode_step(toks[0][t, s:s + 1], toks[1][t, s:s + 1], toks[2][t, s:s + 1], okr[s:s + 1],
+                               ovr[s:s + 1], oA[s:s + 1], opos[s:s + 1], lam, eta, g)
+    assert list(opos) == prefix
+    kr = dev(okr, dtype)
+    vr = dev(ovr, dtype)
+    A = dev(oA.astype(np.float32), "f32")
+    oA = oA.astype(np.float32).astype(np.float64)  # the GPU starts from the float32-rounded state
+    pos = torch.tensor(prefix, dtype=torch.int64, device="cuda")
+    L, E, G = dev(lam), dev(eta), dev(g)
+    worst = 0.0
+    for i in range(steps):
+        q = np.stack([toks[0][prefix[s] + i, s] for s in range(S)])
+        k = np.stack([toks[1][prefix[s] + i, s] for s in range(S)])
+        v = np.stack([toks[2][prefix[s] + i, s] for s in range(S)])
+        y = tc().tc_decode_step(dev(q, dtype), dev(k, dtype), dev(v, dtype), kr, vr, A, pos, L, E, G)
+        yo = oracle.decode_step(q, k, v, okr, ovr, oA, opos, lam, eta, g)
+        e = rel(host(y), yo)
+        worst = max(worst, e)
+        assert e <= TOL[dtype], (i, e)
+    torch.cuda.synchronize()
+    say("  worst y", worst, "A", rel(host(A), oA))
+    assert rel(host(A), oA) <= TOL[dtype]
+    assert np.array_equal(host(kr), okr) and np.array_equal(host(vr), ovr)
+    assert np.array_equal(pos.cpu().numpy(), opos)
