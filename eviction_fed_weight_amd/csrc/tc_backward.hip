@@ -809,21 +809,36 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
       __syncthreads();
     }
     // ---- L1 band: query tiles covering rows key .. key + W - 1 ----
+    // (each tile's Q, dY, lse and Delta rows are loaded one tile ahead)
     const int qt_lo = i0 >> 6;
     const int qt_hi = min(T - 1, i0 + 62 + W) >> 6;
-    for (int qt = qt_lo; qt <= qt_hi; ++qt) {
-      const int q0 = qt * 64;
-      __syncthreads();
+    float lse_r = 0.0f, del_r = 0.0f;
+    auto load_qtile = [&](int q0) {
       ql.load(Qg, q0);
       yl.load(dYg, q0);
       if (tid < 64) {
         const bool ok = q0 + tid < T;
-        lse_s[tid] = ok ? a.lse[(size_t)bh * T + q0 + tid] * kLog2e : __builtin_huge_valf();
-        del_s[tid] = ok ? a.delta[(size_t)bh * T + q0 + tid] : 0.0f;
+        const size_t ix = (size_t)bh * T + (ok ? q0 + tid : 0);
+        lse_r = a.lse[ix];
+        del_r = a.delta[ix];
+        if (!ok) {
+          lse_r = __builtin_huge_valf();
+          del_r = 0.0f;
+        }
+      }
+    };
+    load_qtile(qt_lo * 64);
+    for (int qt = qt_lo; qt <= qt_hi; ++qt) {
+      const int q0 = qt * 64;
+      __syncthreads();
+      if (tid < 64) {
+        lse_s[tid] = lse_r * kLog2e;
+        del_s[tid] = del_r;
       }
       ql.store(Qs, LDK);
       yl.store(Ys, LDK);
       __syncthreads();
+      if (qt < qt_hi) load_qtile(q0 + 64);
       f32x4 Z[4], P[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
