@@ -23,10 +23,13 @@
 // Kernels (64-row blocks, G blocks per workgroup segment):
 //   bseg_fwd_kernel / bchain_fwd_kernel : segment-start S and B
 //   bseg_rev_kernel / bchain_rev_kernel : segment-end R
-//   dq_kernel   : forward walk over query blocks (S, B carried in registers):
-//                 memory-path dq and scalars, Delta, then the band dq loop
+//   dq_kernel   : forward walk over query blocks (S, B carried in registers,
+//                 eight waves): memory-path dq and scalars, then the band key
+//                 tiles from the evicted chunk on (Delta fixed in the first)
 //   dkdv_kernel : reverse walk over key blocks (R carried in registers in
-//                 both operand layouts): memory-path dk, dv, then band dk, dv
+//                 both operand layouts, eight waves): memory path of the later
+//                 queries, then the band query tiles ending with the queries
+//                 that evict the block
 //   reduce_kernel : deterministic sums for dlambda, deta, dgate.
 #ifndef TC_BWD_BF16
 #error "compile with -DTC_BWD_BF16=1 (bf16 kernels) or -DTC_BWD_BF16=0 (float32 kernels)"
@@ -40,13 +43,17 @@ template <class E, int D>
 struct BwdCfg {
   static constexpr int NT = D / 16;
   static constexpr int NKC = (D + 31) / 32;
-  static constexpr int NOWN = (NT + 3) / 4;
   static constexpr int VE = 16 / (int)sizeof(E);
   static constexpr int LDK = D + VE;
   static constexpr int LDX = D + 4;
   static constexpr int TILE = 64 * LDK * (int)sizeof(E);
   static constexpr int XB = 64 * LDX * 4;
-  static constexpr int U = (2 * TILE) > XB ? (2 * TILE) : XB;
+};
+
+// Compile-time variant tag for the per-tile element math.
+template <int V>
+struct Mode {
+  static constexpr int value = V;
 };
 
 // Fragment of two runs of four rows (rows r0..r0+3 at p0, r0'..r0'+3 at p1)
@@ -119,17 +126,21 @@ __device__ __forceinline__ void fill_pow_tables(float lam, float* pw, float* dpw
   }
 }
 
+// A D x D float state split over NW waves: wave wid owns the 16-column tiles
+// n = wid + NW*o of all 16-row tiles m.
+template <int D, int NW>
+using StateTiles = f32x4[(D / 16 + NW - 1) / NW][D / 16];
+
 // Load a D x D float state (row a, column c at g[a*D + c]) into tiles
 // t[o][m] where the lane holds element [row = 16*m + 4lg + i][col = 16*n + l16]
-// with n = wid + 4o (ROWS_BY_LG) -- the layout of an MFMA output out[m][n] --
-// or its transpose (element [row = 16*n + l16][col = 16*m + 4lg + i]).
-template <int D, bool TRANS>
-__device__ __forceinline__ void load_tiles(f32x4 (&t)[(D / 16 + 3) / 4][D / 16], const float* g, int wid,
-                                           int l16, int lg) {
-  constexpr int NT = D / 16, NOWN = (NT + 3) / 4;
+// with n = wid + NW*o -- the layout of an MFMA output out[m][n] -- or its
+// transpose (element [row = 16*n + l16][col = 16*m + 4lg + i]).
+template <int D, int NW, bool TRANS>
+__device__ __forceinline__ void load_tiles(StateTiles<D, NW>& t, const float* g, int wid, int l16, int lg) {
+  constexpr int NT = D / 16, NOWN = (NT + NW - 1) / NW;
 #pragma unroll
   for (int o = 0; o < NOWN; ++o) {
-    const int n = wid + 4 * o;
+    const int n = wid + NW * o;
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
       f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -146,13 +157,12 @@ __device__ __forceinline__ void load_tiles(f32x4 (&t)[(D / 16 + 3) / 4][D / 16],
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_tiles(const f32x4 (&t)[(D / 16 + 3) / 4][D / 16], float* g, int wid,
-                                            int l16, int lg) {
-  constexpr int NT = D / 16, NOWN = (NT + 3) / 4;
+template <int D, int NW>
+__device__ __forceinline__ void store_tiles(const StateTiles<D, NW>& t, float* g, int wid, int l16, int lg) {
+  constexpr int NT = D / 16, NOWN = (NT + NW - 1) / NW;
 #pragma unroll
   for (int o = 0; o < NOWN; ++o) {
-    const int n = wid + 4 * o;
+    const int n = wid + NW * o;
     if (n < NT) {
 #pragma unroll
       for (int m = 0; m < NT; ++m)
@@ -162,29 +172,28 @@ __device__ __forceinline__ void store_tiles(const f32x4 (&t)[(D / 16 + 3) / 4][D
   }
 }
 
-template <int D>
-__device__ __forceinline__ void zero_tiles(f32x4 (&t)[(D / 16 + 3) / 4][D / 16]) {
+template <int D, int NW>
+__device__ __forceinline__ void zero_tiles(StateTiles<D, NW>& t) {
 #pragma unroll
-  for (int o = 0; o < (D / 16 + 3) / 4; ++o)
+  for (int o = 0; o < (D / 16 + NW - 1) / NW; ++o)
 #pragma unroll
     for (int m = 0; m < D / 16; ++m) t[o][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // acc(o, m) <- scale*acc + sum_{c<64} A[c][16m + ..]^T (w_c B[c][16n + ..]),
 // i.e. out[m-row][n-col] += sum_c A[c][row] w_c B[c][col], where A, B are 64-row
-// row-major LDS tiles, all m tiles, owned n = wid + 4o.  Optionally a second
+// row-major LDS tiles, all m tiles, owned n = wid + NW*o.  Optionally a second
 // accumulator gets the same product with weights w2 (no extra scale).
-template <class E, int D, bool TWO>
-__device__ __forceinline__ void rank64_update(f32x4 (&acc)[(D / 16 + 3) / 4][D / 16], float scale,
-                                              f32x4 (&acc2)[(D / 16 + 3) / 4][D / 16], const E* A,
-                                              const E* B, const float* w, const float* w2, int wid, int l16,
-                                              int lg) {
+template <class E, int D, int NW, bool TWO>
+__device__ __forceinline__ void rank64_update(StateTiles<D, NW>& acc, float scale, StateTiles<D, NW>& acc2,
+                                              const E* A, const E* B, const float* w, const float* w2, int wid,
+                                              int l16, int lg) {
   using M = Mfma<E>;
   using frag = typename M::frag;
-  constexpr int NT = D / 16, NOWN = (NT + 3) / 4, LDK = BwdCfg<E, D>::LDK;
+  constexpr int NT = D / 16, NOWN = (NT + NW - 1) / NW, LDK = BwdCfg<E, D>::LDK;
 #pragma unroll
   for (int o = 0; o < NOWN; ++o) {
-    const int n = wid + 4 * o;
+    const int n = wid + NW * o;
     if (n < NT) {
 #pragma unroll
       for (int m = 0; m < NT; ++m) acc[o][m] *= scale;
@@ -219,9 +228,9 @@ __device__ __forceinline__ void rank64_update(f32x4 (&acc)[(D / 16 + 3) / 4][D /
 // state tile column: acc[g] += sum_k St[k][x] * R[16g + l16][k], where the
 // state tiles t[o][*] hold [k = 16*kt + 4lg + i][x = 16*n + l16] and R is a
 // row-major LDS tile (4-element runs).  Used for q S, S dy, R v, R^T k.
-template <class E, int D>
-__device__ __forceinline__ void state_times_rows(const f32x4 (&t)[(D / 16 + 3) / 4][D / 16], int o,
-                                                 const E* R, f32x4 (&acc)[4], int l16, int lg) {
+template <class E, int D, int NW>
+__device__ __forceinline__ void state_times_rows(const StateTiles<D, NW>& t, int o, const E* R, f32x4 (&acc)[4],
+                                                 int l16, int lg) {
   using M = Mfma<E>;
   using frag = typename M::frag;
   constexpr int NT = D / 16, LDK = BwdCfg<E, D>::LDK;
@@ -267,9 +276,9 @@ __global__ void __launch_bounds__(256, 2) bseg_fwd_kernel(BwdArgs a) {
   const auto Kg = make_rsrc((const E*)a.k + base, nbytes);
   const auto Vg = make_rsrc((const E*)a.v + base, nbytes);
   fill_pow_tables(a.lam[h], pw, dpw);
-  f32x4 S[C::NOWN][C::NT], B[C::NOWN][C::NT];
-  zero_tiles<D>(S);
-  zero_tiles<D>(B);
+  StateTiles<D, 4> S, B;
+  zero_tiles<D, 4>(S);
+  zero_tiles<D, 4>(B);
   TileRegs<E, D, 64> kl, vl;
   for (int g = 0; g < a.G; ++g) {
     const int e0 = (m * a.G + g) * 64 - a.W;
@@ -287,13 +296,13 @@ __global__ void __launch_bounds__(256, 2) bseg_fwd_kernel(BwdArgs a) {
     __syncthreads();
     // B <- lam^64 B + 64 lam^63 S + sum w2 k v^T ; S <- lam^64 S + sum w1 k v^T
 #pragma unroll
-    for (int o = 0; o < C::NOWN; ++o)
+    for (int o = 0; o < (C::NT + 3) / 4; ++o)
 #pragma unroll
       for (int mm = 0; mm < C::NT; ++mm) B[o][mm] = pw[64] * B[o][mm] + dpw[64] * S[o][mm];
-    rank64_update<E, D, true>(S, pw[64], B, Ks, Vs, w1, w2, wid, l16, lg);
+    rank64_update<E, D, 4, true>(S, pw[64], B, Ks, Vs, w1, w2, wid, l16, lg);
   }
-  store_tiles<D>(S, a.fstate + ((size_t)bh * a.nseg + m + 1) * D * D, wid, l16, lg);
-  store_tiles<D>(B, a.tstate + ((size_t)bh * a.nseg + m + 1) * D * D, wid, l16, lg);
+  store_tiles<D, 4>(S, a.fstate + ((size_t)bh * a.nseg + m + 1) * D * D, wid, l16, lg);
+  store_tiles<D, 4>(B, a.tstate + ((size_t)bh * a.nseg + m + 1) * D * D, wid, l16, lg);
 }
 
 // S[0] = B[0] = 0; S[m+1] = L S[m] + Ls_m; B[m+1] = L' S[m] + L B[m] + Lb_m
@@ -347,8 +356,8 @@ __global__ void __launch_bounds__(256, 2) bseg_rev_kernel(BwdArgs a) {
   const auto Qg = make_rsrc((const E*)a.q + base, nbytes);
   const auto Yg = make_rsrc((const E*)a.dy + base, nbytes);
   fill_pow_tables(a.lam[h], pw, dpw);
-  f32x4 R[C::NOWN][C::NT];
-  zero_tiles<D>(R);
+  StateTiles<D, 4> R;
+  zero_tiles<D, 4>(R);
   const int jb = m * a.G, je = min(a.nblk, jb + a.G);
   TileRegs<E, D, 64> ql, yl;
   for (int jk = je - 1; jk >= jb; --jk) {
@@ -362,11 +371,11 @@ __global__ void __launch_bounds__(256, 2) bseg_rev_kernel(BwdArgs a) {
     __syncthreads();
     // R[a][c] <- lam^64 R + sum_c' Q[c'][a] lam^c' dY[c'][c]  (skipped blocks
     // contribute zero and need no decay: R is zero until the first block)
-    rank64_update<E, D, false>(R, pw[64], R, Qs, Ys, pw, pw, wid, l16, lg);
+    rank64_update<E, D, 4, false>(R, pw[64], R, Qs, Ys, pw, pw, wid, l16, lg);
   }
   // blocks skipped at the top (q0 >= T) would only scale a zero state;
   // blocks present below them were decayed correctly relative to jb.
-  store_tiles<D>(R, a.rstate + ((size_t)bh * a.nseg + m - 1) * D * D, wid, l16, lg);
+  store_tiles<D, 4>(R, a.rstate + ((size_t)bh * a.nseg + m - 1) * D * D, wid, l16, lg);
 }
 
 // R_end[nseg-1] = 0; R_end[m] = lambda^(64G) R_end[m+1] + Lr_{m+1} (in place).
@@ -391,26 +400,59 @@ __global__ void __launch_bounds__(256) bchain_rev_kernel(BwdArgs a) {
 }
 
 // ===========================================================================
-// dq kernel: grid = BH * nseg, 4 waves x 16 query rows per 64-row block.
+// Band tiles of a 64-row block start at its evicted chunk.  For query block
+// t0 the key tiles start at e0 + 64 m (e0 = t0 - W, m = 0 .. ceil(W/64)):
+// tile 0 is the chunk that the block's rows evict, the last one holds the
+// diagonal.  For key block i0 the query tiles start at i0 + W - 64 m: tile 0,
+// taken last, holds the queries that evict the block.  The intra-chunk part
+// of the memory path then reuses the scores of one band tile, and the band
+// needs no tile of its own for it.  Streamed tiles go through two LDS buffers
+// (one barrier per tile) when six 64-row tiles fit, else through one.
 template <class E, int D>
-__global__ void __launch_bounds__(256, 1) dq_kernel(BwdArgs a) {
+struct BandBufs {
+  static constexpr int N = 6 * BwdCfg<E, D>::TILE <= 150 * 1024 ? 2 : 1;
+};
+
+// The dq and dk/dv kernels run eight waves: waves w and w ^ 4 share one
+// 16-row group (w & 3) and take one half (w >> 2) of each 64-row band tile
+// each; the D x D states are split over all eight.  The pair's partial sums
+// meet in LDS at the end of each block.
+constexpr int kBwdWaves = 8;
+
+// dq kernel: grid = BH * nseg, one 64-row query block at a time.  Per block:
+// the state part of the memory path (S(e0) dy, B(e0) dy), then the key tiles
+// from the evicted chunk on (tile 0 adds the intra-chunk memory terms and
+// fixes Delta before its band terms), then S and B carried past the chunk.
+template <class E, int D>
+__global__ void __launch_bounds__(64 * kBwdWaves, 1) dq_kernel(BwdArgs a) {
   using M = Mfma<E>;
   using frag = typename M::frag;
   using C = BwdCfg<E, D>;
-  constexpr int NT = C::NT, NKC = C::NKC, NOWN = C::NOWN, LDK = C::LDK, LDX = C::LDX, VE = C::VE;
-  __shared__ __attribute__((aligned(16))) char smem[C::U + 2 * C::TILE];
-  __shared__ float pw[72], dpw[72], ypart[4][64], red[4][2];
-  E* Ks = (E*)smem;
-  E* Vs = (E*)(smem + C::TILE);
-  float* X = (float*)smem;
-  E* Qs = (E*)(smem + C::U);
-  E* Ys = (E*)(smem + C::U + C::TILE);
+  constexpr int NW = kBwdWaves, NTH = 64 * NW;
+  constexpr int NT = C::NT, NKC = C::NKC, NOWN = (NT + NW - 1) / NW, LDK = C::LDK, LDX = C::LDX, VE = C::VE;
+  constexpr int NB = BandBufs<E, D>::N;
+  constexpr int NVR = D / VE / 2;  // 16-byte vectors in half a row
+  constexpr int NYV = (NVR + 3) / 4;
+  static_assert(2 * C::TILE >= C::XB, "the exchange area must fit in one key buffer");
+  static_assert(2 * NB * C::TILE >= ((NT + 1) / 2) * NW * 64 * 16, "the dq exchange must fit in the key buffers");
+  __shared__ __attribute__((aligned(16))) char smem[(2 + 2 * NB) * C::TILE];
+  __shared__ float pw[72], dpw[72], ypart[NW][64], red[NW][2], w1[64], w2[64], dex[2][64];
+  E* Qs = (E*)smem;
+  E* Ys = (E*)(smem + C::TILE);
+  // key buffer b: K at (2 + 2b) tiles, V after it.  X (the state-product
+  // exchange) aliases the last key buffer, which holds no tile while in use;
+  // XQ (the pair's dq exchange) all key buffers once the band is done.
+  auto Kb = [&](int b) { return (E*)(smem + (2 + 2 * b) * C::TILE); };
+  auto Vb = [&](int b) { return (E*)(smem + (3 + 2 * b) * C::TILE); };
+  float* X = (float*)(smem + 2 * NB * C::TILE);
+  f32x4* XQ = (f32x4*)(smem + 2 * C::TILE);
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  const int half = wid >> 2;
   const int wgi = xcd_remap(blockIdx.x, gridDim.x);  // one head's segments on one XCD
   const int bh = wgi / a.nseg, seg = wgi - bh * a.nseg;
   const int h = bh % a.H;
-  const int T = a.T, W = a.W;
+  const int T = a.T, W = min(a.W, a.T);  // a window of T or more evicts nothing
   const size_t base = (size_t)bh * T * D;
   const uint32_t nbytes = (uint32_t)T * D * sizeof(E);
   const auto Qg = make_rsrc((const E*)a.q + base, nbytes);
@@ -424,208 +466,254 @@ __global__ void __launch_bounds__(256, 1) dq_kernel(BwdArgs a) {
   const float tau = a.scale, sl2 = a.scale * kLog2e;
   fill_pow_tables(a.lam[h], pw, dpw);
 
-  // S^T and B^T: tiles [o][ct] hold element [c = 16 ct + 4lg + i][a = 16 (wid+4o) + l16]
-  f32x4 S[NOWN][NT], B[NOWN][NT];
+  // S^T and B^T: tiles [o][ct] hold element [c = 16 ct + 4lg + i][a = 16 (wid+NW*o) + l16]
+  StateTiles<D, NW> S, B;
   if (seg == 0) {
-    zero_tiles<D>(S);
-    zero_tiles<D>(B);
+    zero_tiles<D, NW>(S);
+    zero_tiles<D, NW>(B);
   } else {
-    load_tiles<D, true>(S, a.fstate + ((size_t)bh * a.nseg + seg) * D * D, wid, l16, lg);
-    load_tiles<D, true>(B, a.tstate + ((size_t)bh * a.nseg + seg) * D * D, wid, l16, lg);
+    load_tiles<D, NW, true>(S, a.fstate + ((size_t)bh * a.nseg + seg) * D * D, wid, l16, lg);
+    load_tiles<D, NW, true>(B, a.tstate + ((size_t)bh * a.nseg + seg) * D * D, wid, l16, lg);
   }
   vm_fence_loads();
   const int jb = seg * a.G, je = min(a.nblk, jb + a.G);
-  const int r = wid * 16 + l16;
+  const int r = (wid & 3) * 16 + l16;  // this lane's query row in the block
+  const int mt = (W + 63) >> 6;        // key tiles e0 + 64 m, m = mlo .. mt
+  // first tile with a key >= 0
+  auto mlo_of = [](int e0) { return e0 + 63 >= 0 ? 0 : (-e0) >> 6; };
   float md_acc = 0.0f, dl_acc = 0.0f;
-  TileRegs<E, D, 64> ql, yl, kl, vl;
+  TileRegs<E, D, 64, NTH> ql, yl, kl, vl;
+  uint4 yv[NYV];  // this lane's part of this wave's half of row t0 + r of y
+  float lse_r = 0.0f;
+  auto load_rows = [&](int j) {  // Q, dY, y rows and lse of query block j
+    const int t = j * 64 + r;
+    ql.load(Qg, j * 64);
+    yl.load(dYg, j * 64);
+#pragma unroll
+    for (int i = 0; i < NYV; ++i) {
+      const int vv = lg + 4 * i;
+      yv[i] = buf_load16(Yg, vv < NVR ? (t * D + (half * NVR + vv) * VE) * (int)sizeof(E) : -16);
+    }
+    lse_r = a.lse[(size_t)bh * T + min(t, T - 1)];
+  };
+  auto load_keys = [&](int k0) {
+    kl.load(Kg, k0);
+    vl.load(Vg, k0);
+  };
+  auto put_keys = [&](int b) {
+    kl.store(Kb(b), LDK);
+    vl.store(Vb(b), LDK);
+  };
+  load_rows(jb);
+  load_keys(jb * 64 - W + 64 * mlo_of(jb * 64 - W));
   for (int j = jb; j < je; ++j) {
     const int t0 = j * 64, trow = t0 + r, e0 = t0 - W;
-    const bool has_mem = t0 + 63 >= W;
+    const int mlo = mlo_of(e0);
     __syncthreads();
-    ql.load(Qg, t0);
-    yl.load(dYg, t0);
-    kl.load(Kg, e0);
-    vl.load(Vg, e0);
     ql.store(Qs, LDK);
     yl.store(Ys, LDK);
-    __syncthreads();
-    frag qf[NKC], yf[NKC];
-#pragma unroll
-    for (int dc = 0; dc < NKC; ++dc) {
-      const bool in = dc * 32 + lg * 8 < D;
-      qf[dc] = in ? M::lds8(Qs + r * LDK + dc * 32 + lg * 8) : M::zero();
-      yf[dc] = in ? M::lds8(Ys + r * LDK + dc * 32 + lg * 8) : M::zero();
+    if (tid < 64) {
+      const bool ok = e0 + tid >= 0;
+      w1[tid] = ok ? pw[63 - tid] : 0.0f;
+      w2[tid] = ok ? dpw[63 - tid] : 0.0f;
     }
+    __syncthreads();
+    // <dy, y> of row trow over this wave's half of the columns
+    float yd = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NYV; ++i) {
+      const int vv = lg + 4 * i;
+      if (vv < NVR) {
+        const E* ye = (const E*)&yv[i];
+        const E* dy = Ys + r * LDK + (half * NVR + vv) * VE;
+#pragma unroll
+        for (int x = 0; x < VE; ++x) yd += (float)ye[x] * (float)dy[x];
+      }
+    }
+    yd = xsum4(yd);
+    const float lse2 = (trow < T) ? lse_r * kLog2e : __builtin_huge_valf();
+
     f32x4 dQ[NT];
 #pragma unroll
     for (int dt = 0; dt < NT; ++dt) dQ[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float md = 0.0f, dlr = 0.0f;  // <dy, mt> and <dy, d mt/dlam> of row r (all 4 lanes)
+    // this wave's shares of <dy, mt> and <dy, d mt/dlam> for row r (all 4 lanes)
+    float md = 0.0f, dlr = 0.0f;
 
-    if (has_mem) {
-      if (e0 > 0) {
-        // X = S dY (all rows, owned a-tiles) and partial <q, B dY>
-        float yp[4] = {0.f, 0.f, 0.f, 0.f};
+    if (mlo == 0 && e0 > 0) {
+      // X = S dY (all rows, owned a-tiles) and partial <q, B dY>
+      float yp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int o = 0; o < NOWN; ++o) {
-          const int at = wid + 4 * o;
-          if (at < NT) {
-            f32x4 xa[4], ya[4];
-            state_times_rows<E, D>(S, o, Ys, xa, l16, lg);
-            state_times_rows<E, D>(B, o, Ys, ya, l16, lg);
+      for (int o = 0; o < NOWN; ++o) {
+        const int at = wid + NW * o;
+        if (at < NT) {
+          f32x4 xa[4], ya[4];
+          state_times_rows<E, D, NW>(S, o, Ys, xa, l16, lg);
+          state_times_rows<E, D, NW>(B, o, Ys, ya, l16, lg);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              *(f32x4*)(X + (g * 16 + l16) * LDX + at * 16 + lg * 4) = xa[g];
-              const E* qrow = Qs + (g * 16 + l16) * LDK + at * 16 + lg * 4;
+          for (int g = 0; g < 4; ++g) {
+            *(f32x4*)(X + (g * 16 + l16) * LDX + at * 16 + lg * 4) = xa[g];
+            const E* qrow = Qs + (g * 16 + l16) * LDK + at * 16 + lg * 4;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) yp[g] += (float)qrow[i] * ya[g][i];
-            }
+            for (int i = 0; i < 4; ++i) yp[g] += (float)qrow[i] * ya[g][i];
           }
         }
+      }
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float v = xsum4(yp[g]);
-          if (lg == 0) ypart[wid][g * 16 + l16] = v;
-        }
-        __syncthreads();
-        const float f = pw[r + 1], df = dpw[r + 1];
-        float qx = 0.0f;
+      for (int g = 0; g < 4; ++g) {
+        const float v = xsum4(yp[g]);
+        if (lg == 0) ypart[wid][g * 16 + l16] = v;
+      }
+      __syncthreads();
+      // this wave takes the column tiles dt with dt % 2 == half of row r
+      const float f = pw[r + 1], df = dpw[r + 1];
+      float qx = 0.0f;
 #pragma unroll
-        for (int dt = 0; dt < NT; ++dt) {
+      for (int dt = 0; dt < NT; ++dt) {
+        if ((dt & 1) == half) {
           const f32x4 xv = *(const f32x4*)(X + r * LDX + dt * 16 + lg * 4);
           const E* qrow = Qs + r * LDK + dt * 16 + lg * 4;
 #pragma unroll
           for (int i = 0; i < 4; ++i) qx += (float)qrow[i] * xv[i];
           dQ[dt] += (seta * f) * xv;
         }
-        qx = xsum4(qx);
-        const float qy = ypart[0][r] + ypart[1][r] + ypart[2][r] + ypart[3][r];
-        md += f * qx;
-        dlr += df * qx + f * qy;
-        __syncthreads();
       }
-      kl.store(Ks, LDK);
-      vl.store(Vs, LDK);
+      qx = xsum4(qx);
+      float qy = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) qy += ypart[w][r];
+      md += f * qx;
+      dlr += df * qx + (half == 0 ? f * qy : 0.0f);
       __syncthreads();
-      // intra-chunk decayed tile: Z = K q, P = V dy
-      f32x4 Z[4], P[4];
+    }
+    put_keys(0);
+    __syncthreads();
+    // the next key tile, or after the last one the next query block's rows and first key tile
+    auto next_loads = [&](int mn) {
+      if (mn <= mt) {
+        load_keys(e0 + 64 * mn);
+      } else if (j + 1 < je) {
+        load_rows(j + 1);
+        load_keys(e0 + 64 + 64 * mlo_of(e0 + 64));
+      }
+    };
+    next_loads(mlo + 1);
+    float delta = 0.0f;
+    int buf = 0;
+    for (int m = mlo; m <= mt; ++m) {
+      const int k0 = e0 + 64 * m;
+      const E* Ks = Kb(buf);
+      const E* Vs = Vb(buf);
+      // Z = K q, P = V dy for this wave's 32 keys (rows) and this lane's query (column)
+      // (the query row's fragments are re-read from LDS each tile: fewer live registers)
+      f32x4 Z[2], P[2];
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        Z[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-        P[n] = Z[n];
-        const int kr = 32 * (n >> 1) + (l16 >> 2) * 8 + (n & 1) * 4 + (l16 & 3);
+      for (int n2 = 0; n2 < 2; ++n2) {
+        Z[n2] = f32x4{0.f, 0.f, 0.f, 0.f};
+        P[n2] = Z[n2];
+      }
 #pragma unroll
-        for (int dc = 0; dc < NKC; ++dc) {
-          const bool in = dc * 32 + lg * 8 < D;
+      for (int dc = 0; dc < NKC; ++dc) {
+        const bool in = dc * 32 + lg * 8 < D;
+        const frag qf = in ? M::lds8(Qs + r * LDK + dc * 32 + lg * 8) : M::zero();
+        const frag yf = in ? M::lds8(Ys + r * LDK + dc * 32 + lg * 8) : M::zero();
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2) {
+          const int n = 2 * half + n2;
+          const int kr = 32 * (n >> 1) + (l16 >> 2) * 8 + (n & 1) * 4 + (l16 & 3);
           const frag ka = in ? M::lds8(Ks + kr * LDK + dc * 32 + lg * 8) : M::zero();
           const frag va = in ? M::lds8(Vs + kr * LDK + dc * 32 + lg * 8) : M::zero();
-          Z[n] = M::mma(ka, qf[dc], Z[n]);
-          P[n] = M::mma(va, yf[dc], P[n]);
+          Z[n2] = M::mma(ka, qf, Z[n2]);
+          P[n2] = M::mma(va, yf, P[n2]);
         }
       }
-      float mp = 0.0f, dp = 0.0f;
+      if (m == 0) {
+        // the evicted chunk: intra-chunk memory terms of <dy, mt> and its lambda derivative
+        float mp = 0.0f, dp = 0.0f;
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
+        for (int jj = 0; jj < 8; ++jj) {
+          const int c = 32 * half + lg * 8 + jj;
+          const float zp = Z[jj >> 2][jj & 3] * P[jj >> 2][jj & 3];
+          const float mem = ((c <= r) & (e0 + c >= 0)) ? zp : 0.0f;
+          const int di = max(r - c, 0);
+          mp = __builtin_fmaf(pw[di], mem, mp);
+          dp = __builtin_fmaf(dpw[di], mem, dp);
+        }
+        md += xsum4(mp);
+        dlr += xsum4(dp);
+      }
+      if (m == mlo) {
+        // Delta = <dy, y> - sigma eta <dy, mt>, the two halves' shares summed
+        if (lg == 0) dex[half][r] = yd - seta * md;
+        __syncthreads();
+        delta = dex[0][r] + dex[1][r];
+        if (half == 0 && lg == 0 && trow < T) a.delta[(size_t)bh * T + trow] = delta;
+      }
+      // dS for this lane's query and the wave's 32 keys, then dQ += dS K.
+      // Variants: 0 = tile inside the band, 1 = band edge, 2 = band edge plus
+      // the intra-chunk memory weights (the evicted chunk).  Masks enter as an
+      // added -inf or a 0/1 factor, so that no operand load sits under a branch.
+      auto tile_update = [&](auto mode_c) {
+        constexpr int mode = decltype(mode_c)::value;
         float gv[8];
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-          const int c = 32 * p + lg * 8 + jj;
-          const float z = Z[2 * p + (jj >> 2)][jj & 3];
-          const float pv = P[2 * p + (jj >> 2)][jj & 3];
-          const bool mem = c <= r && e0 + c >= 0;
-          const float w = mem ? pw[r - c] : 0.0f;
-          const float dw = mem ? dpw[r - c] : 0.0f;
-          mp += w * z * pv;
-          dp += dw * z * pv;
-          gv[jj] = seta * w * pv;
+          const int c = 32 * half + lg * 8 + jj;
+          const int key = k0 + c;
+          const float z = Z[jj >> 2][jj & 3];
+          const float dpv = P[jj >> 2][jj & 3];
+          float x = __builtin_fmaf(z, sl2, -lse2);
+          if (mode != 0) {
+            const bool in = ((unsigned)(trow - key) < (unsigned)W) & (key >= 0);
+            x += in ? 0.0f : -__builtin_huge_valf();
+          }
+          float g = tau * fast_exp2(x) * (dpv - delta);
+          if (mode == 2) {
+            const float w = seta * pw[max(r - c, 0)] * (((c <= r) & (key >= 0)) ? 1.0f : 0.0f);
+            g = __builtin_fmaf(w, dpv, g);
+          }
+          gv[jj] = g;
         }
         const frag gf = M::pack(gv);
 #pragma unroll
         for (int dt = 0; dt < NT; ++dt)
-          dQ[dt] = M::mma(ColFrag<E>::read(Ks + (p * 32 + lg * 8) * LDK + dt * 16, LDK, l16), gf, dQ[dt]);
-      }
-      md += xsum4(mp);
-      dlr += xsum4(dp);
-      // carry S and B to the next block of this segment
-      if (j + 1 < je) {
-        __shared__ float w1[64], w2[64];
-        if (tid < 64) {
-          const bool ok = e0 + tid >= 0;
-          w1[tid] = ok ? pw[63 - tid] : 0.0f;
-          w2[tid] = ok ? dpw[63 - tid] : 0.0f;
-        }
-        __syncthreads();
+          dQ[dt] = M::mma(ColFrag<E>::read(Ks + (half * 32 + lg * 8) * LDK + dt * 16, LDK, l16), gf, dQ[dt]);
+      };
+      if (m == 0)
+        tile_update(Mode<2>{});
+      else if ((k0 >= 0) && (k0 + 63 <= t0) && (k0 >= t0 + 64 - W))
+        tile_update(Mode<0>{});
+      else
+        tile_update(Mode<1>{});
+      if (m == 0 && j + 1 < je) {
+        // carry S and B past the evicted chunk
 #pragma unroll
         for (int o = 0; o < NOWN; ++o)
 #pragma unroll
-          for (int m = 0; m < NT; ++m) B[o][m] = pw[64] * B[o][m] + dpw[64] * S[o][m];
+          for (int mm = 0; mm < NT; ++mm) B[o][mm] = pw[64] * B[o][mm] + dpw[64] * S[o][mm];
         // S^T[c][a] += sum_c' V[c'][c] w K[c'][a]
-        rank64_update<E, D, true>(S, pw[64], B, Vs, Ks, w1, w2, wid, l16, lg);
+        rank64_update<E, D, NW, true>(S, pw[64], B, Vs, Ks, w1, w2, wid, l16, lg);
+      }
+      if (m < mt) {
+        const int nb = NB == 2 ? buf ^ 1 : 0;
+        if (NB == 1) __syncthreads();
+        put_keys(nb);
+        __syncthreads();
+        buf = nb;
+        next_loads(m + 2);
       }
     }
-    // Delta = <dy, y> - sigma eta <dy, mt>
-    float yd = 0.0f;
-    for (int vv = lg; vv < D / VE; vv += 4) {
-      const uint4 yr = buf_load16(Yg, (trow * D + vv * VE) * (int)sizeof(E));
-      const E* ye = (const E*)&yr;
-      const E* dy = Ys + r * LDK + vv * VE;
+    // the pair's dq shares: half h keeps the tiles dt with dt % 2 == h
+    __syncthreads();
 #pragma unroll
-      for (int x = 0; x < VE; ++x) yd += (float)ye[x] * (float)dy[x];
-    }
-    yd = xsum4(yd);
-    const float delta = yd - seta * md;
-    if (lg == 0 && trow < T) a.delta[(size_t)bh * T + trow] = delta;
-    const float lse2 = (trow < T) ? a.lse[(size_t)bh * T + trow] * kLog2e : __builtin_huge_valf();
-
-    // ---- L1 band: dq += tau sum dS k ----
-    const int kt_lo = max(0, t0 - W + 1) >> 6;
-    const int kt_hi = min(T - 1, t0 + 63) >> 6;
-    kl.load(Kg, kt_lo * 64);
-    vl.load(Vg, kt_lo * 64);
-    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-      const int k0 = kt * 64;
-      __syncthreads();
-      kl.store(Ks, LDK);
-      vl.store(Vs, LDK);
-      __syncthreads();
-      kl.load(Kg, k0 + 64);
-      vl.load(Vg, k0 + 64);
-      f32x4 Z[4], P[4];
+    for (int dt = 0; dt < NT; ++dt)
+      if ((dt & 1) != half) XQ[((dt >> 1) * NW + wid) * 64 + lane] = dQ[dt];
+    __syncthreads();
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        Z[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-        P[n] = Z[n];
-        const int kr = 32 * (n >> 1) + (l16 >> 2) * 8 + (n & 1) * 4 + (l16 & 3);
-#pragma unroll
-        for (int dc = 0; dc < NKC; ++dc) {
-          const bool in = dc * 32 + lg * 8 < D;
-          const frag ka = in ? M::lds8(Ks + kr * LDK + dc * 32 + lg * 8) : M::zero();
-          const frag va = in ? M::lds8(Vs + kr * LDK + dc * 32 + lg * 8) : M::zero();
-          Z[n] = M::mma(ka, qf[dc], Z[n]);
-          P[n] = M::mma(va, yf[dc], P[n]);
-        }
+    for (int dt = 0; dt < NT; ++dt) {
+      if ((dt & 1) == half) {
+        const f32x4 o = dQ[dt] + XQ[((dt >> 1) * NW + (wid ^ 4)) * 64 + lane];
+        if (trow < T) st4(dQg + (size_t)trow * D + dt * 16 + lg * 4, o);
       }
-      const bool full = (k0 + 63 <= t0) && (k0 >= t0 + 64 - W);
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        float gv[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int key = k0 + 32 * p + lg * 8 + jj;
-          const bool band = full || (key <= trow && key > trow - W);
-          const float z = Z[2 * p + (jj >> 2)][jj & 3];
-          const float dpv = P[2 * p + (jj >> 2)][jj & 3];
-          const float pr = band ? fast_exp2(__builtin_fmaf(z, sl2, -lse2)) : 0.0f;
-          gv[jj] = tau * pr * (dpv - delta);
-        }
-        const frag gf = M::pack(gv);
-#pragma unroll
-        for (int dt = 0; dt < NT; ++dt)
-          dQ[dt] = M::mma(ColFrag<E>::read(Ks + (p * 32 + lg * 8) * LDK + dt * 16, LDK, l16), gf, dQ[dt]);
-      }
-    }
-    if (trow < T) {
-#pragma unroll
-      for (int dt = 0; dt < NT; ++dt) st4(dQg + (size_t)trow * D + dt * 16 + lg * 4, dQ[dt]);
     }
     if (lg == 0 && trow < T) {
       md_acc += md;
@@ -642,7 +730,7 @@ __global__ void __launch_bounds__(256, 1) dq_kernel(BwdArgs a) {
   __syncthreads();
   if (tid == 0) {
     float s0 = 0.0f, s1 = 0.0f;
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       s0 += red[w][0];
       s1 += red[w][1];
     }
@@ -652,28 +740,39 @@ __global__ void __launch_bounds__(256, 1) dq_kernel(BwdArgs a) {
 }
 
 // ===========================================================================
-// dk/dv kernel: grid = BH * nseg, reverse walk over key blocks; wave w owns
-// keys 16w .. 16w+15 of the 64-key block.
+// dk/dv kernel: grid = BH * nseg, reverse walk over 64-row key blocks.  Per
+// key block: the memory path of the later queries (R(i0+64) v, R(i0+64)^T k),
+// the query tiles of the band (the last one, the queries that evict the
+// block, also carries the intra-chunk memory weights), then R(i0) from that
+// last tile.
 template <class E, int D>
-__global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(64 * kBwdWaves, 1) dkdv_kernel(BwdArgs a) {
   using M = Mfma<E>;
   using frag = typename M::frag;
   using C = BwdCfg<E, D>;
-  constexpr int NT = C::NT, NKC = C::NKC, NOWN = C::NOWN, LDK = C::LDK, LDX = C::LDX;
-  constexpr int QY = (2 * C::TILE) > C::XB ? (2 * C::TILE) : C::XB;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::TILE + QY];
-  __shared__ float pw[72], dpw[72], lse_s[64], del_s[64];
+  constexpr int NW = kBwdWaves, NTH = 64 * NW;
+  constexpr int NT = C::NT, NKC = C::NKC, NOWN = (NT + NW - 1) / NW, LDK = C::LDK, LDX = C::LDX;
+  constexpr int NB = BandBufs<E, D>::N;
+  static_assert(2 * C::TILE >= C::XB, "the exchange area must fit in one query buffer");
+  static_assert(2 * NB * C::TILE >= NT * NW * 64 * 16, "the dk/dv exchange must fit in the query buffers");
+  __shared__ __attribute__((aligned(16))) char smem[(2 + 2 * NB) * C::TILE];
+  __shared__ float pw[72], dpw[72], lse_s[NB][64], del_s[NB][64];
   E* Ks = (E*)smem;
   E* Vs = (E*)(smem + C::TILE);
-  E* Qs = (E*)(smem + 2 * C::TILE);
-  E* Ys = (E*)(smem + 3 * C::TILE);
-  float* X = (float*)(smem + 2 * C::TILE);
+  // query buffer b: Q at (2 + 2b) tiles, dY after it.  X (the state-product
+  // exchange) aliases the last query buffer, which holds no tile while in
+  // use; XK (the pair's dk/dv exchange) all query buffers after the band.
+  auto Qb = [&](int b) { return (E*)(smem + (2 + 2 * b) * C::TILE); };
+  auto Yb = [&](int b) { return (E*)(smem + (3 + 2 * b) * C::TILE); };
+  float* X = (float*)(smem + 2 * NB * C::TILE);
+  f32x4* XK = (f32x4*)(smem + 2 * C::TILE);
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  const int half = wid >> 2;
   const int wgi = xcd_remap(blockIdx.x, gridDim.x);  // one head's segments on one XCD
   const int bh = wgi / a.nseg, seg = wgi - bh * a.nseg;
   const int h = bh % a.H;
-  const int T = a.T, W = a.W;
+  const int T = a.T, W = min(a.W, a.T);  // a window of T or more evicts nothing
   const size_t base = (size_t)bh * T * D;
   const uint32_t nbytes = (uint32_t)T * D * sizeof(E);
   const auto Qg = make_rsrc((const E*)a.q + base, nbytes);
@@ -686,204 +785,223 @@ __global__ void __launch_bounds__(256, 1) dkdv_kernel(BwdArgs a) {
   const float tau = a.scale, sl2 = a.scale * kLog2e;
   fill_pow_tables(a.lam[h], pw, dpw);
 
-  // RA tiles [o][at]: element R[a = 16 at + 4lg + i][c = 16 (wid+4o) + l16]
-  // RB tiles [o][ct]: element R[a = 16 (wid+4o) + l16][c = 16 ct + 4lg + i]
-  f32x4 RA[NOWN][NT], RB[NOWN][NT];
+  // RA tiles [o][at]: element R[a = 16 at + 4lg + i][c = 16 (wid+NW*o) + l16]
+  // RB tiles [o][ct]: element R[a = 16 (wid+NW*o) + l16][c = 16 ct + 4lg + i]
+  StateTiles<D, NW> RA, RB;
   if (seg == a.nseg - 1) {
-    zero_tiles<D>(RA);
-    zero_tiles<D>(RB);
+    zero_tiles<D, NW>(RA);
+    zero_tiles<D, NW>(RB);
   } else {
     const float* g = a.rstate + ((size_t)bh * a.nseg + seg) * D * D;
-    load_tiles<D, false>(RA, g, wid, l16, lg);
-    load_tiles<D, true>(RB, g, wid, l16, lg);
+    load_tiles<D, NW, false>(RA, g, wid, l16, lg);
+    load_tiles<D, NW, true>(RB, g, wid, l16, lg);
   }
   vm_fence_loads();
   const int jb = seg * a.G, je = min(a.nblk, jb + a.G);
-  const int kidx = wid * 16 + l16;
-  TileRegs<E, D, 64> kl, vl, ql, yl;
+  const int kidx = (wid & 3) * 16 + l16;  // this lane's key in the block
+  const int mt = (W + 63) >> 6;           // query tiles i0 + W - 64 m, m = mt .. mlo
+  // last tile index that starts before T
+  auto mlo_of = [&](int i0) { return i0 + W < T ? 0 : ((i0 + W - T) >> 6) + 1; };
+  TileRegs<E, D, 64, NTH> kl, vl, ql, yl;
+  float lse_r = 0.0f, del_r = 0.0f;
+  auto load_qtile = [&](int q0) {
+    ql.load(Qg, q0);
+    yl.load(dYg, q0);
+    if (tid < 64) {
+      const int t = q0 + tid;
+      const bool ok = t >= 0 && t < T;
+      const size_t ix = (size_t)bh * T + (ok ? t : 0);
+      lse_r = a.lse[ix];
+      del_r = a.delta[ix];
+      if (!ok) {
+        lse_r = __builtin_huge_valf();
+        del_r = 0.0f;
+      }
+    }
+  };
+  auto put_qtile = [&](int b) {
+    ql.store(Qb(b), LDK);
+    yl.store(Yb(b), LDK);
+    if (tid < 64) {
+      lse_s[b][tid] = lse_r * kLog2e;
+      del_s[b][tid] = del_r;
+    }
+  };
+  kl.load(Kg, (je - 1) * 64);
+  vl.load(Vg, (je - 1) * 64);
+  load_qtile((je - 1) * 64 + W - 64 * mt);
   for (int jk = je - 1; jk >= jb; --jk) {
-    const int i0 = jk * 64, key = i0 + kidx;
+    const int i0 = jk * 64, key = i0 + kidx, q0m = i0 + W;
+    const int mlo = mlo_of(i0);
     __syncthreads();
-    kl.load(Kg, i0);
-    vl.load(Vg, i0);
     kl.store(Ks, LDK);
     vl.store(Vs, LDK);
     __syncthreads();
-    frag kf[NKC], vf[NKC];
-#pragma unroll
-    for (int dc = 0; dc < NKC; ++dc) {
-      const bool in = dc * 32 + lg * 8 < D;
-      kf[dc] = in ? M::lds8(Ks + kidx * LDK + dc * 32 + lg * 8) : M::zero();
-      vf[dc] = in ? M::lds8(Vs + kidx * LDK + dc * 32 + lg * 8) : M::zero();
-    }
+    // this wave's shares of dK, dV for its 16 keys
     f32x4 dK[NT], dV[NT];
 #pragma unroll
     for (int dt = 0; dt < NT; ++dt) {
       dK[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       dV[dt] = dK[dt];
     }
-    // ---- memory path, later queries: R(i0+64) v and R(i0+64)^T k ----
+    // ---- memory path, later queries: R(i0+64) v and R(i0+64)^T k (the
+    // pair splits the column tiles dt by parity) ----
     if (i0 + 64 + W < T) {
       const float f = seta * pw[64 - kidx];
       // (R v)[a][key] with RB (lane-fixed a), exchanged through X[key][a]
 #pragma unroll
       for (int o = 0; o < NOWN; ++o) {
-        const int at = wid + 4 * o;
+        const int at = wid + NW * o;
         if (at < NT) {
           f32x4 acc[4];
-          state_times_rows<E, D>(RB, o, Vs, acc, l16, lg);
+          state_times_rows<E, D, NW>(RB, o, Vs, acc, l16, lg);
 #pragma unroll
           for (int g = 0; g < 4; ++g) *(f32x4*)(X + (g * 16 + l16) * LDX + at * 16 + lg * 4) = acc[g];
         }
       }
       __syncthreads();
 #pragma unroll
-      for (int dt = 0; dt < NT; ++dt) dK[dt] += f * *(const f32x4*)(X + kidx * LDX + dt * 16 + lg * 4);
+      for (int dt = 0; dt < NT; ++dt)
+        if ((dt & 1) == half) dK[dt] += f * *(const f32x4*)(X + kidx * LDX + dt * 16 + lg * 4);
       __syncthreads();
       // (R^T k)[c][key] with RA (lane-fixed c)
 #pragma unroll
       for (int o = 0; o < NOWN; ++o) {
-        const int ct = wid + 4 * o;
+        const int ct = wid + NW * o;
         if (ct < NT) {
           f32x4 acc[4];
-          state_times_rows<E, D>(RA, o, Ks, acc, l16, lg);
+          state_times_rows<E, D, NW>(RA, o, Ks, acc, l16, lg);
 #pragma unroll
           for (int g = 0; g < 4; ++g) *(f32x4*)(X + (g * 16 + l16) * LDX + ct * 16 + lg * 4) = acc[g];
         }
       }
       __syncthreads();
 #pragma unroll
-      for (int dt = 0; dt < NT; ++dt) dV[dt] += f * *(const f32x4*)(X + kidx * LDX + dt * 16 + lg * 4);
+      for (int dt = 0; dt < NT; ++dt)
+        if ((dt & 1) == half) dV[dt] += f * *(const f32x4*)(X + kidx * LDX + dt * 16 + lg * 4);
       __syncthreads();
     }
-    // ---- memory path, the queries whose eviction index is in this block ----
-    const int q0m = i0 + W;
-    if (q0m < T) {
-      ql.load(Qg, q0m);
-      yl.load(dYg, q0m);
-      ql.store(Qs, LDK);
-      yl.store(Ys, LDK);
-      __syncthreads();
-      f32x4 Z[4], P[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        Z[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-        P[g] = Z[g];
-#pragma unroll
-        for (int dc = 0; dc < NKC; ++dc) {
-          const bool in = dc * 32 + lg * 8 < D;
-          const frag qa = in ? M::lds8(Qs + (g * 16 + l16) * LDK + dc * 32 + lg * 8) : M::zero();
-          const frag ya = in ? M::lds8(Ys + (g * 16 + l16) * LDK + dc * 32 + lg * 8) : M::zero();
-          Z[g] = M::mma(qa, kf[dc], Z[g]);
-          P[g] = M::mma(ya, vf[dc], P[g]);
-        }
-      }
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        float pv[8], gv[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int g = 2 * p + (jj >> 2);
-          const int cq = g * 16 + lg * 4 + (jj & 3);  // query row in the tile
-          const bool mem = cq >= kidx && q0m + cq < T;
-          const float w = mem ? seta * pw[cq - kidx] : 0.0f;
-          pv[jj] = w * Z[g][jj & 3];
-          gv[jj] = w * P[g][jj & 3];
-        }
-        const frag pf = M::pack(pv), gf = M::pack(gv);
-#pragma unroll
-        for (int dt = 0; dt < NT; ++dt) {
-          dV[dt] = M::mma(ColFrag2<E>::read(Ys + (32 * p + lg * 4) * LDK + dt * 16,
-                                            Ys + (32 * p + 16 + lg * 4) * LDK + dt * 16, LDK, l16),
-                          pf, dV[dt]);
-          dK[dt] = M::mma(ColFrag2<E>::read(Qs + (32 * p + lg * 4) * LDK + dt * 16,
-                                            Qs + (32 * p + 16 + lg * 4) * LDK + dt * 16, LDK, l16),
-                          gf, dK[dt]);
-        }
-      }
-      // R(i0) = lam^64 R(i0+64) + sum_c' lam^c' q^T dy  (both layouts)
-      if (jk > jb) {
-        rank64_update<E, D, false>(RA, pw[64], RA, Qs, Ys, pw, pw, wid, l16, lg);
-        rank64_update<E, D, false>(RB, pw[64], RB, Ys, Qs, pw, pw, wid, l16, lg);
-      }
-      __syncthreads();
-    }
-    // ---- L1 band: query tiles covering rows key .. key + W - 1 ----
-    // (each tile's Q, dY, lse and Delta rows are loaded one tile ahead)
-    const int qt_lo = i0 >> 6;
-    const int qt_hi = min(T - 1, i0 + 62 + W) >> 6;
-    float lse_r = 0.0f, del_r = 0.0f;
-    auto load_qtile = [&](int q0) {
-      ql.load(Qg, q0);
-      yl.load(dYg, q0);
-      if (tid < 64) {
-        const bool ok = q0 + tid < T;
-        const size_t ix = (size_t)bh * T + (ok ? q0 + tid : 0);
-        lse_r = a.lse[ix];
-        del_r = a.delta[ix];
-        if (!ok) {
-          lse_r = __builtin_huge_valf();
-          del_r = 0.0f;
-        }
+    // ---- band query tiles; the last one (m = 0) also carries the memory
+    // weights of the queries that evict this block ----
+    put_qtile(0);
+    __syncthreads();
+    // the next tile, or after the last one the next key block and its first tile
+    auto next_loads = [&](int mn) {
+      if (mn >= mlo) {
+        load_qtile(q0m - 64 * mn);
+      } else if (jk > jb) {
+        kl.load(Kg, i0 - 64);
+        vl.load(Vg, i0 - 64);
+        load_qtile(i0 - 64 + W - 64 * mt);
       }
     };
-    load_qtile(qt_lo * 64);
-    for (int qt = qt_lo; qt <= qt_hi; ++qt) {
-      const int q0 = qt * 64;
-      __syncthreads();
-      if (tid < 64) {
-        lse_s[tid] = lse_r * kLog2e;
-        del_s[tid] = del_r;
+    next_loads(mt - 1);
+    int buf = 0;
+    for (int m = mt; m >= mlo; --m) {
+      const int q0 = q0m - 64 * m;
+      const E* Qs = Qb(buf);
+      const E* Ys = Yb(buf);
+      const float* ls = lse_s[buf];
+      const float* ds = del_s[buf];
+      // Z = Q k, P = dY v for this wave's 32 queries (rows) and this lane's key (column)
+      // (the key's fragments are re-read from LDS each tile: fewer live registers)
+      f32x4 Z[2], P[2];
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        Z[g2] = f32x4{0.f, 0.f, 0.f, 0.f};
+        P[g2] = Z[g2];
       }
-      ql.store(Qs, LDK);
-      yl.store(Ys, LDK);
-      __syncthreads();
-      if (qt < qt_hi) load_qtile(q0 + 64);
-      f32x4 Z[4], P[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        Z[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-        P[g] = Z[g];
+      for (int dc = 0; dc < NKC; ++dc) {
+        const bool in = dc * 32 + lg * 8 < D;
+        const frag kf = in ? M::lds8(Ks + kidx * LDK + dc * 32 + lg * 8) : M::zero();
+        const frag vf = in ? M::lds8(Vs + kidx * LDK + dc * 32 + lg * 8) : M::zero();
 #pragma unroll
-        for (int dc = 0; dc < NKC; ++dc) {
-          const bool in = dc * 32 + lg * 8 < D;
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int g = 2 * half + g2;
           const frag qa = in ? M::lds8(Qs + (g * 16 + l16) * LDK + dc * 32 + lg * 8) : M::zero();
           const frag ya = in ? M::lds8(Ys + (g * 16 + l16) * LDK + dc * 32 + lg * 8) : M::zero();
-          Z[g] = M::mma(qa, kf[dc], Z[g]);
-          P[g] = M::mma(ya, vf[dc], P[g]);
+          Z[g2] = M::mma(qa, kf, Z[g2]);
+          P[g2] = M::mma(ya, vf, P[g2]);
         }
       }
-      const bool full = (i0 + 63 <= q0) && (i0 >= q0 + 64 - W) && (q0 + 63 < T);
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
+      // P and dS^T for the wave's 32 queries, then dV += P^T dY, dK += dS^T Q.
+      // Variants: 0 = tile inside the band, 1 = band edge, 2 = band edge plus
+      // the memory weights of the evicting queries.  Masks enter as an added
+      // -inf or a 0/1 factor, so that no operand load sits under a branch.
+      auto tile_update = [&](auto mode_c) {
+        constexpr int mode = decltype(mode_c)::value;
         float pv[8], gv[8];
+        f32x4 lsv[2], dsv[2];
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          lsv[g2] = *(const f32x4*)(ls + (2 * half + g2) * 16 + lg * 4);
+          dsv[g2] = *(const f32x4*)(ds + (2 * half + g2) * 16 + lg * 4);
+        }
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-          const int g = 2 * p + (jj >> 2);
-          const int rr = g * 16 + lg * 4 + (jj & 3);
+          const int rr = 32 * half + (jj >> 2) * 16 + lg * 4 + (jj & 3);
           const int t = q0 + rr;
-          const bool band = full || (key <= t && key > t - W && t < T);
-          const float pr = band ? fast_exp2(__builtin_fmaf(Z[g][jj & 3], sl2, -lse_s[rr])) : 0.0f;
-          pv[jj] = pr;
-          gv[jj] = tau * pr * (P[g][jj & 3] - del_s[rr]);
+          const float z = Z[jj >> 2][jj & 3], dp = P[jj >> 2][jj & 3];
+          float x = __builtin_fmaf(z, sl2, -lsv[jj >> 2][jj & 3]);
+          if (mode != 0) {
+            const bool in = ((unsigned)(t - key) < (unsigned)W) & (t < T);
+            x += in ? 0.0f : -__builtin_huge_valf();
+          }
+          const float pr = fast_exp2(x);
+          float pvv = pr, gvv = tau * pr * (dp - dsv[jj >> 2][jj & 3]);
+          if (mode == 2) {
+            // query t evicts key i0 + rr: weight sigma eta lambda^(rr - kidx) on keys up to it
+            const int di = rr - kidx;
+            const float w = seta * pw[max(di, 0)] * (((di >= 0) & (t < T)) ? 1.0f : 0.0f);
+            pvv = __builtin_fmaf(w, z, pvv);
+            gvv = __builtin_fmaf(w, dp, gvv);
+          }
+          pv[jj] = pvv;
+          gv[jj] = gvv;
         }
         const frag pf = M::pack(pv), gf = M::pack(gv);
 #pragma unroll
         for (int dt = 0; dt < NT; ++dt) {
-          dV[dt] = M::mma(ColFrag2<E>::read(Ys + (32 * p + lg * 4) * LDK + dt * 16,
-                                            Ys + (32 * p + 16 + lg * 4) * LDK + dt * 16, LDK, l16),
+          dV[dt] = M::mma(ColFrag2<E>::read(Ys + (32 * half + lg * 4) * LDK + dt * 16,
+                                            Ys + (32 * half + 16 + lg * 4) * LDK + dt * 16, LDK, l16),
                           pf, dV[dt]);
-          dK[dt] = M::mma(ColFrag2<E>::read(Qs + (32 * p + lg * 4) * LDK + dt * 16,
-                                            Qs + (32 * p + 16 + lg * 4) * LDK + dt * 16, LDK, l16),
+          dK[dt] = M::mma(ColFrag2<E>::read(Qs + (32 * half + lg * 4) * LDK + dt * 16,
+                                            Qs + (32 * half + 16 + lg * 4) * LDK + dt * 16, LDK, l16),
                           gf, dK[dt]);
         }
+      };
+      if (m == 0)
+        tile_update(Mode<2>{});
+      else if ((i0 + 63 <= q0) && (i0 >= q0 + 64 - W) && (q0 + 63 < T))
+        tile_update(Mode<0>{});
+      else
+        tile_update(Mode<1>{});
+      if (m > mlo) {
+        const int nb = NB == 2 ? buf ^ 1 : 0;
+        if (NB == 1) __syncthreads();
+        put_qtile(nb);
+        __syncthreads();
+        buf = nb;
+        next_loads(m - 2);
       }
     }
+    // R(i0) = lam^64 R(i0+64) + sum_c lam^c q_{q0m+c}^T dy_{q0m+c}  (both layouts)
+    if (mlo == 0 && jk > jb) {
+      rank64_update<E, D, NW, false>(RA, pw[64], RA, Qb(buf), Yb(buf), pw, pw, wid, l16, lg);
+      rank64_update<E, D, NW, false>(RB, pw[64], RB, Yb(buf), Qb(buf), pw, pw, wid, l16, lg);
+    }
+    // the pair's shares: half 0 completes dK, half 1 dV
+    __syncthreads();
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) XK[(dt * NW + wid) * 64 + lane] = half == 0 ? dV[dt] : dK[dt];
+    __syncthreads();
     if (key < T) {
+      E* dst = half == 0 ? dKg : dVg;
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt) {
-        st4(dKg + (size_t)key * D + dt * 16 + lg * 4, dK[dt]);
-        st4(dVg + (size_t)key * D + dt * 16 + lg * 4, dV[dt]);
+        const f32x4 o = (half == 0 ? dK[dt] : dV[dt]) + XK[(dt * NW + (wid ^ 4)) * 64 + lane];
+        st4(dst + (size_t)key * D + dt * 16 + lg * 4, o);
       }
     }
   }
@@ -917,8 +1035,8 @@ static hipError_t launch_bwd_impl(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((bseg_rev_kernel<E, D>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
     hipLaunchKernelGGL((bchain_rev_kernel<D>), dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, s, a);
   }
-  hipLaunchKernelGGL((dq_kernel<E, D>), dim3(BH * a.nseg), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((dkdv_kernel<E, D>), dim3(BH * a.nseg), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((dq_kernel<E, D>), dim3(BH * a.nseg), dim3(64 * kBwdWaves), 0, s, a);
+  hipLaunchKernelGGL((dkdv_kernel<E, D>), dim3(BH * a.nseg), dim3(64 * kBwdWaves), 0, s, a);
   hipLaunchKernelGGL(reduce_kernel, dim3((a.H + 63) / 64), dim3(64), 0, s, a);
   return hipGetLastError();
 }

@@ -98,6 +98,21 @@ def test_backward_multi_segment_walk():
         assert e <= TOL["f32"], (key, e)
 
 
+@pytest.mark.parametrize("W", [333, 64 * 5])
+def test_backward_blocks_per_segment_bf16(W):
+    """bf16, several 64-row blocks per workgroup segment (B*H*blocks > 512),
+    a ragged last block, and windows that are and are not a multiple of 64:
+    the band tiles start at the evicted chunk, so the intra-chunk memory
+    terms share a band tile with the window terms.  Two sampled heads."""
+    say("backward blocks per segment", W)
+    d = tc_inputs.prefill_inputs(5, seed=12, B=2, H=8, T=4096 + 19, D=64, W=W, dtype="bf16",
+                                 with_dy=True)
+    err = compare(d, W, heads=[(0, 3), (1, 7)])
+    say("  errors", err)
+    for key, e in err.items():
+        assert e <= TOL["bf16"], (key, e)
+
+
 def test_backward_config5_full():
     """Full training-backward launch (B=4 H=16 T=8192 D=128 W=512): every
     gradient against the oracle (dlam/deta/dgate summed over the batch)."""
