@@ -224,6 +224,47 @@ __device__ __forceinline__ void rank64_update(StateTiles<D, NW>& acc, float scal
   }
 }
 
+// Write the owned tiles of a state t[o][m] (element [row 16m + 4lg + i]
+// [col 16n + l16]) to LDS transposed, dst[col][row] with leading dimension
+// ld, as matrix-core operands: float32 as is, bf16 as a hi part and the
+// rounding remainder lo (hi + lo carries about 16 significant bits).
+template <int D, int NW>
+__device__ __forceinline__ void put_state_t(const StateTiles<D, NW>& t, float* hi, float* lo, int ld, int wid,
+                                            int l16, int lg) {
+  constexpr int NT = D / 16, NOWN = (NT + NW - 1) / NW;
+  (void)lo;
+#pragma unroll
+  for (int o = 0; o < NOWN; ++o) {
+    const int n = wid + NW * o;
+    if (n < NT) {
+#pragma unroll
+      for (int m = 0; m < NT; ++m) *(f32x4*)(hi + (16 * n + l16) * ld + 16 * m + 4 * lg) = t[o][m];
+    }
+  }
+}
+template <int D, int NW>
+__device__ __forceinline__ void put_state_t(const StateTiles<D, NW>& t, bf16* hi, bf16* lo, int ld, int wid,
+                                            int l16, int lg) {
+  constexpr int NT = D / 16, NOWN = (NT + NW - 1) / NW;
+#pragma unroll
+  for (int o = 0; o < NOWN; ++o) {
+    const int n = wid + NW * o;
+    if (n < NT) {
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        bf16x4 h, l;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          h[i] = (bf16)t[o][m][i];
+          l[i] = (bf16)(t[o][m][i] - (float)h[i]);
+        }
+        *(bf16x4*)(hi + (16 * n + l16) * ld + 16 * m + 4 * lg) = h;
+        *(bf16x4*)(lo + (16 * n + l16) * ld + 16 * m + 4 * lg) = l;
+      }
+    }
+  }
+}
+
 // out[m = x-row (16*o' tiles)][n = 64 rows of R (4 groups)] for one owned
 // state tile column: acc[g] += sum_k St[k][x] * R[16g + l16][k], where the
 // state tiles t[o][*] hold [k = 16*kt + 4lg + i][x = 16*n + l16] and R is a
@@ -751,20 +792,22 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dkdv_kernel(BwdArgs a) {
   using frag = typename M::frag;
   using C = BwdCfg<E, D>;
   constexpr int NW = kBwdWaves, NTH = 64 * NW;
-  constexpr int NT = C::NT, NKC = C::NKC, NOWN = (NT + NW - 1) / NW, LDK = C::LDK, LDX = C::LDX;
+  constexpr int NT = C::NT, NKC = C::NKC, NOWN = (NT + NW - 1) / NW, LDK = C::LDK;
   constexpr int NB = BandBufs<E, D>::N;
-  static_assert(2 * C::TILE >= C::XB, "the exchange area must fit in one query buffer");
+  static_assert((M::kSplit ? 2 : 1) * D * LDK * (int)sizeof(E) <= 2 * NB * C::TILE,
+                "the state copy must fit in the query buffers");
   static_assert(2 * NB * C::TILE >= NT * NW * 64 * 16, "the dk/dv exchange must fit in the query buffers");
   __shared__ __attribute__((aligned(16))) char smem[(2 + 2 * NB) * C::TILE];
   __shared__ float pw[72], dpw[72], lse_s[NB][64], del_s[NB][64];
   E* Ks = (E*)smem;
   E* Vs = (E*)(smem + C::TILE);
-  // query buffer b: Q at (2 + 2b) tiles, dY after it.  X (the state-product
-  // exchange) aliases the last query buffer, which holds no tile while in
-  // use; XK (the pair's dk/dv exchange) all query buffers after the band.
+  // query buffer b: Q at (2 + 2b) tiles, dY after it.  Before the band
+  // they hold R^T as matrix-core operands (RTh, RTl: [c][a]); after it XK,
+  // the pair's dk/dv exchange.
   auto Qb = [&](int b) { return (E*)(smem + (2 + 2 * b) * C::TILE); };
   auto Yb = [&](int b) { return (E*)(smem + (3 + 2 * b) * C::TILE); };
-  float* X = (float*)(smem + 2 * NB * C::TILE);
+  E* RTh = (E*)(smem + 2 * C::TILE);
+  E* RTl = RTh + D * LDK;
   f32x4* XK = (f32x4*)(smem + 2 * C::TILE);
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
@@ -785,17 +828,12 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dkdv_kernel(BwdArgs a) {
   const float tau = a.scale, sl2 = a.scale * kLog2e;
   fill_pow_tables(a.lam[h], pw, dpw);
 
-  // RA tiles [o][at]: element R[a = 16 at + 4lg + i][c = 16 (wid+NW*o) + l16]
-  // RB tiles [o][ct]: element R[a = 16 (wid+NW*o) + l16][c = 16 ct + 4lg + i]
-  StateTiles<D, NW> RA, RB;
-  if (seg == a.nseg - 1) {
+  // R tiles [o][at]: element R[a = 16 at + 4lg + i][c = 16 (wid+NW*o) + l16]
+  StateTiles<D, NW> RA;
+  if (seg == a.nseg - 1)
     zero_tiles<D, NW>(RA);
-    zero_tiles<D, NW>(RB);
-  } else {
-    const float* g = a.rstate + ((size_t)bh * a.nseg + seg) * D * D;
-    load_tiles<D, NW, false>(RA, g, wid, l16, lg);
-    load_tiles<D, NW, true>(RB, g, wid, l16, lg);
-  }
+  else
+    load_tiles<D, NW, false>(RA, a.rstate + ((size_t)bh * a.nseg + seg) * D * D, wid, l16, lg);
   vm_fence_loads();
   const int jb = seg * a.G, je = min(a.nblk, jb + a.G);
   const int kidx = (wid & 3) * 16 + l16;  // this lane's key in the block
@@ -833,9 +871,11 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dkdv_kernel(BwdArgs a) {
   for (int jk = je - 1; jk >= jb; --jk) {
     const int i0 = jk * 64, key = i0 + kidx, q0m = i0 + W;
     const int mlo = mlo_of(i0);
+    const bool later = i0 + 64 + W < T;  // queries evict keys past this block
     __syncthreads();
     kl.store(Ks, LDK);
     vl.store(Vs, LDK);
+    if (later) put_state_t<D, NW>(RA, RTh, RTl, LDK, wid, l16, lg);
     __syncthreads();
     // this wave's shares of dK, dV for its 16 keys
     f32x4 dK[NT], dV[NT];
@@ -844,42 +884,40 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dkdv_kernel(BwdArgs a) {
       dK[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       dV[dt] = dK[dt];
     }
-    // ---- memory path, later queries: R(i0+64) v and R(i0+64)^T k (the
-    // pair splits the column tiles dt by parity) ----
-    if (i0 + 64 + W < T) {
+    // ---- memory path of the later queries: dk += f R(i0+64) v,
+    // dv += f R(i0+64)^T k (the pair splits the column tiles dt by parity) ----
+    if (later) {
       const float f = seta * pw[64 - kidx];
-      // (R v)[a][key] with RB (lane-fixed a), exchanged through X[key][a]
+      frag kf[NKC], vf[NKC];
 #pragma unroll
-      for (int o = 0; o < NOWN; ++o) {
-        const int at = wid + NW * o;
-        if (at < NT) {
-          f32x4 acc[4];
-          state_times_rows<E, D, NW>(RB, o, Vs, acc, l16, lg);
+      for (int dc = 0; dc < NKC; ++dc) {
+        const bool in = dc * 32 + lg * 8 < D;
+        kf[dc] = in ? M::lds8(Ks + kidx * LDK + dc * 32 + lg * 8) : M::zero();
+        vf[dc] = in ? M::lds8(Vs + kidx * LDK + dc * 32 + lg * 8) : M::zero();
+      }
 #pragma unroll
-          for (int g = 0; g < 4; ++g) *(f32x4*)(X + (g * 16 + l16) * LDX + at * 16 + lg * 4) = acc[g];
+      for (int dt = 0; dt < NT; ++dt) {
+        if ((dt & 1) == half) {
+          f32x4 ak = f32x4{0.f, 0.f, 0.f, 0.f}, av = ak;
+#pragma unroll
+          for (int dc = 0; dc < NKC; ++dc) {
+            const bool in = dc * 32 + lg * 8 < D;
+            // (R v)[a][key]: A = R rows a (columns of R^T), B = v.  The
+            // transposing read runs on every lane; for D = 16 the lanes past
+            // the contraction read written (finite) rows and meet v = 0.
+            const E* rc = RTh + ((dc * 32 + lg * 8) & (D >= 32 ? ~0 : 15)) * LDK + dt * 16;
+            ak = M::mma(ColFrag<E>::read(rc, LDK, l16), vf[dc], ak);
+            if (M::kSplit) ak = M::mma(ColFrag<E>::read(rc + D * LDK, LDK, l16), vf[dc], ak);
+            // (R^T k)[c][key]: A = R^T rows c, B = k
+            const E* rr = RTh + (dt * 16 + l16) * LDK + dc * 32 + lg * 8;
+            av = M::mma(in ? M::lds8(rr) : M::zero(), kf[dc], av);
+            if (M::kSplit) av = M::mma(in ? M::lds8(rr + D * LDK) : M::zero(), kf[dc], av);
+          }
+          dK[dt] += f * ak;
+          dV[dt] += f * av;
         }
       }
-      __syncthreads();
-#pragma unroll
-      for (int dt = 0; dt < NT; ++dt)
-        if ((dt & 1) == half) dK[dt] += f * *(const f32x4*)(X + kidx * LDX + dt * 16 + lg * 4);
-      __syncthreads();
-      // (R^T k)[c][key] with RA (lane-fixed c)
-#pragma unroll
-      for (int o = 0; o < NOWN; ++o) {
-        const int ct = wid + NW * o;
-        if (ct < NT) {
-          f32x4 acc[4];
-          state_times_rows<E, D, NW>(RA, o, Ks, acc, l16, lg);
-#pragma unroll
-          for (int g = 0; g < 4; ++g) *(f32x4*)(X + (g * 16 + l16) * LDX + ct * 16 + lg * 4) = acc[g];
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int dt = 0; dt < NT; ++dt)
-        if ((dt & 1) == half) dV[dt] += f * *(const f32x4*)(X + kidx * LDX + dt * 16 + lg * 4);
-      __syncthreads();
+      __syncthreads();  // R^T read before the first query tile lands on it
     }
     // ---- band query tiles; the last one (m = 0) also carries the memory
     // weights of the queries that evict this block ----
@@ -986,11 +1024,8 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dkdv_kernel(BwdArgs a) {
         next_loads(m - 2);
       }
     }
-    // R(i0) = lam^64 R(i0+64) + sum_c lam^c q_{q0m+c}^T dy_{q0m+c}  (both layouts)
-    if (mlo == 0 && jk > jb) {
-      rank64_update<E, D, NW, false>(RA, pw[64], RA, Qb(buf), Yb(buf), pw, pw, wid, l16, lg);
-      rank64_update<E, D, NW, false>(RB, pw[64], RB, Yb(buf), Qb(buf), pw, pw, wid, l16, lg);
-    }
+    // R(i0) = lam^64 R(i0+64) + sum_c lam^c q_{q0m+c}^T dy_{q0m+c}
+    if (mlo == 0 && jk > jb) rank64_update<E, D, NW, false>(RA, pw[64], RA, Qb(buf), Yb(buf), pw, pw, wid, l16, lg);
     // the pair's shares: half 0 completes dK, half 1 dV
     __syncthreads();
 #pragma unroll

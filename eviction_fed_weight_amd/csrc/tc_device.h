@@ -167,6 +167,9 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 template <class E>
 struct ColFrag;
 
+// The bf16 form is a transposing LDS read that exchanges data between the
+// lanes of each 16-lane group: every lane must execute it (never under a
+// lane-dependent condition), and every address must hold written data.
 template <>
 struct ColFrag<bf16> {
   static __device__ __forceinline__ bf16x8 read(const bf16* blk, int ld, int l16) {
