@@ -45,9 +45,7 @@ struct BwdCfg {
   static constexpr int NKC = (D + 31) / 32;
   static constexpr int VE = 16 / (int)sizeof(E);
   static constexpr int LDK = D + VE;
-  static constexpr int LDX = D + 4;
   static constexpr int TILE = 64 * LDK * (int)sizeof(E);
-  static constexpr int XB = 64 * LDX * 4;
 };
 
 // Compile-time variant tag for the per-tile element math.
@@ -90,24 +88,6 @@ struct ColFrag2<float> {
     return r;
   }
 };
-
-// Two runs of four consecutive LDS elements as one fragment.
-template <class E>
-__device__ __forceinline__ typename Mfma<E>::frag frag4x2(const E* p0, const E* p1, bool second);
-template <>
-__device__ __forceinline__ bf16x8 frag4x2<bf16>(const bf16* p0, const bf16* p1, bool second) {
-  const bf16x4 a = *(const bf16x4*)p0;
-  bf16x4 b = *(const bf16x4*)p1;
-  if (!second) b = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
-  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-template <>
-__device__ __forceinline__ f32x8 frag4x2<float>(const float* p0, const float* p1, bool second) {
-  const f32x4 a = *(const f32x4*)p0;
-  f32x4 b = *(const f32x4*)p1;
-  if (!second) b = f32x4{0.f, 0.f, 0.f, 0.f};
-  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
 
 __device__ __forceinline__ void st4(bf16* dst, f32x4 x) {
   bf16x4 r;
@@ -261,38 +241,6 @@ __device__ __forceinline__ void put_state_t(const StateTiles<D, NW>& t, bf16* hi
         *(bf16x4*)(hi + (16 * n + l16) * ld + 16 * m + 4 * lg) = h;
         *(bf16x4*)(lo + (16 * n + l16) * ld + 16 * m + 4 * lg) = l;
       }
-    }
-  }
-}
-
-// out[m = x-row (16*o' tiles)][n = 64 rows of R (4 groups)] for one owned
-// state tile column: acc[g] += sum_k St[k][x] * R[16g + l16][k], where the
-// state tiles t[o][*] hold [k = 16*kt + 4lg + i][x = 16*n + l16] and R is a
-// row-major LDS tile (4-element runs).  Used for q S, S dy, R v, R^T k.
-template <class E, int D, int NW>
-__device__ __forceinline__ void state_times_rows(const StateTiles<D, NW>& t, int o, const E* R, f32x4 (&acc)[4],
-                                                 int l16, int lg) {
-  using M = Mfma<E>;
-  using frag = typename M::frag;
-  constexpr int NT = D / 16, LDK = BwdCfg<E, D>::LDK;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int pp = 0; pp < (NT + 1) / 2; ++pp) {
-    float sv[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = t[o][2 * pp][i];
-      sv[4 + i] = (2 * pp + 1 < NT) ? t[o][(2 * pp + 1) % NT][i] : 0.0f;
-    }
-    frag hi, lo;
-    M::split(sv, hi, lo);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const E* row = R + (g * 16 + l16) * LDK;
-      const frag b = frag4x2<E>(row + 32 * pp + lg * 4, row + (32 * pp + 16 + lg * 4) % D, 32 * pp + 16 < D);
-      acc[g] = M::mma(hi, b, acc[g]);
-      if (M::kSplit) acc[g] = M::mma(lo, b, acc[g]);
     }
   }
 }
@@ -470,22 +418,23 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dq_kernel(BwdArgs a) {
   using frag = typename M::frag;
   using C = BwdCfg<E, D>;
   constexpr int NW = kBwdWaves, NTH = 64 * NW;
-  constexpr int NT = C::NT, NKC = C::NKC, NOWN = (NT + NW - 1) / NW, LDK = C::LDK, LDX = C::LDX, VE = C::VE;
+  constexpr int NT = C::NT, NKC = C::NKC, NOWN = (NT + NW - 1) / NW, LDK = C::LDK, VE = C::VE;
   constexpr int NB = BandBufs<E, D>::N;
   constexpr int NVR = D / VE / 2;  // 16-byte vectors in half a row
   constexpr int NYV = (NVR + 3) / 4;
-  static_assert(2 * C::TILE >= C::XB, "the exchange area must fit in one key buffer");
+  static_assert((M::kSplit ? 2 : 1) * D * LDK * (int)sizeof(E) <= 2 * NB * C::TILE,
+                "a state copy must fit in the key buffers");
   static_assert(2 * NB * C::TILE >= ((NT + 1) / 2) * NW * 64 * 16, "the dq exchange must fit in the key buffers");
   __shared__ __attribute__((aligned(16))) char smem[(2 + 2 * NB) * C::TILE];
-  __shared__ float pw[72], dpw[72], ypart[NW][64], red[NW][2], w1[64], w2[64], dex[2][64];
+  __shared__ float pw[72], dpw[72], red[NW][2], w1[64], w2[64], dex[2][64];
   E* Qs = (E*)smem;
   E* Ys = (E*)(smem + C::TILE);
-  // key buffer b: K at (2 + 2b) tiles, V after it.  X (the state-product
-  // exchange) aliases the last key buffer, which holds no tile while in use;
-  // XQ (the pair's dq exchange) all key buffers once the band is done.
+  // key buffer b: K at (2 + 2b) tiles, V after it.  Before the band they
+  // hold S, then B, as matrix-core operands (SBh: [a][c], hi then lo); after
+  // it XQ, the pair's dq exchange.
   auto Kb = [&](int b) { return (E*)(smem + (2 + 2 * b) * C::TILE); };
   auto Vb = [&](int b) { return (E*)(smem + (3 + 2 * b) * C::TILE); };
-  float* X = (float*)(smem + 2 * NB * C::TILE);
+  E* SBh = (E*)(smem + 2 * C::TILE);
   f32x4* XQ = (f32x4*)(smem + 2 * C::TILE);
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
@@ -581,50 +530,45 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dq_kernel(BwdArgs a) {
     float md = 0.0f, dlr = 0.0f;
 
     if (mlo == 0 && e0 > 0) {
-      // X = S dY (all rows, owned a-tiles) and partial <q, B dY>
-      float yp[4] = {0.f, 0.f, 0.f, 0.f};
+      // S(e0) dy and B(e0) dy for this lane's row over the column tiles dt
+      // with dt % 2 == half, each state copied to LDS in turn: dq gains
+      // sigma eta lambda^(r+1) S dy; <q, S dy> and <q, B dy> feed md and dlr.
+      const float f = pw[r + 1], df = dpw[r + 1];
+      float qx = 0.0f, qy = 0.0f;
 #pragma unroll
-      for (int o = 0; o < NOWN; ++o) {
-        const int at = wid + NW * o;
-        if (at < NT) {
-          f32x4 xa[4], ya[4];
-          state_times_rows<E, D, NW>(S, o, Ys, xa, l16, lg);
-          state_times_rows<E, D, NW>(B, o, Ys, ya, l16, lg);
+      for (int pass = 0; pass < 2; ++pass) {
+        put_state_t<D, NW>(pass == 0 ? S : B, SBh, SBh + D * LDK, LDK, wid, l16, lg);
+        __syncthreads();
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            *(f32x4*)(X + (g * 16 + l16) * LDX + at * 16 + lg * 4) = xa[g];
-            const E* qrow = Qs + (g * 16 + l16) * LDK + at * 16 + lg * 4;
+        for (int dt = 0; dt < NT; ++dt) {
+          if ((dt & 1) == half) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) yp[g] += (float)qrow[i] * ya[g][i];
+            for (int dc = 0; dc < NKC; ++dc) {
+              const bool in = dc * 32 + lg * 8 < D;
+              const frag yf = in ? M::lds8(Ys + r * LDK + dc * 32 + lg * 8) : M::zero();
+              const E* sr = SBh + (dt * 16 + l16) * LDK + dc * 32 + lg * 8;
+              acc = M::mma(in ? M::lds8(sr) : M::zero(), yf, acc);
+              if (M::kSplit) acc = M::mma(in ? M::lds8(sr + D * LDK) : M::zero(), yf, acc);
+            }
+            const E* qrow = Qs + r * LDK + dt * 16 + lg * 4;
+            float qd = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qd += (float)qrow[i] * acc[i];
+            if (pass == 0) {
+              dQ[dt] += (seta * f) * acc;
+              qx += qd;
+            } else {
+              qy += qd;
+            }
           }
         }
-      }
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float v = xsum4(yp[g]);
-        if (lg == 0) ypart[wid][g * 16 + l16] = v;
-      }
-      __syncthreads();
-      // this wave takes the column tiles dt with dt % 2 == half of row r
-      const float f = pw[r + 1], df = dpw[r + 1];
-      float qx = 0.0f;
-#pragma unroll
-      for (int dt = 0; dt < NT; ++dt) {
-        if ((dt & 1) == half) {
-          const f32x4 xv = *(const f32x4*)(X + r * LDX + dt * 16 + lg * 4);
-          const E* qrow = Qs + r * LDK + dt * 16 + lg * 4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) qx += (float)qrow[i] * xv[i];
-          dQ[dt] += (seta * f) * xv;
-        }
+        __syncthreads();  // the copy is read before the next one (or the first key tile) lands on it
       }
       qx = xsum4(qx);
-      float qy = 0.0f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) qy += ypart[w][r];
+      qy = xsum4(qy);
       md += f * qx;
-      dlr += df * qx + (half == 0 ? f * qy : 0.0f);
-      __syncthreads();
+      dlr += df * qx + f * qy;
     }
     put_keys(0);
     __syncthreads();
