@@ -67,7 +67,8 @@ Plan plan_for(const tc_shape_t& s) {
   }
   p.G = bestG;
   p.nseg = (p.nblk + p.G - 1) / p.G;
-  p.state_bytes = (size_t)BH * p.nseg * s.D * s.D * sizeof(float);
+  // segment states, then one last-block local state per (b,h)
+  p.state_bytes = (size_t)BH * (p.nseg + 1) * s.D * s.D * sizeof(float);
   return p;
 }
 

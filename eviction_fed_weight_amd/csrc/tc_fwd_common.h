@@ -136,7 +136,10 @@ __device__ __forceinline__ void store4(float* dst, f32x4 x) { *(f32x4*)dst = x; 
 // per segment (segment m holds the evictions e in [m G BM - W, (m+1) G BM - W)).
 
 // Local states L_m = S over the evictions of segment m, from zero.
-// grid = BH * (nseg - 1); writes seg_state[bh][m + 1].
+// grid = BH * (nseg - 1); writes seg_state[bh][m + 1].  With final_slot the
+// grid is BH * nseg and workgroup m = nseg - 1 of each head forms instead the
+// local state of the last segment's evictions up to step T-1 (for the final
+// state), at seg_state[BH * nseg + bh].
 template <class E, int D, int BM>
 __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
   constexpr int LDK = D + 16 / (int)sizeof(E);
@@ -146,8 +149,9 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
   E* Ks = (E*)smem;
   E* Vs = (E*)(smem + TILE);
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
-  const int nm = a.nseg - 1;
+  const int nm = a.nseg - 1 + a.final_slot;
   const int bh = blockIdx.x / nm, m = blockIdx.x - bh * nm;
+  const bool fin = m == a.nseg - 1;  // the last segment's evictions (final_slot only)
   const int h = bh % a.H;
   const size_t base = (size_t)bh * a.T * D;
   const uint32_t nbytes = (uint32_t)a.T * D * sizeof(E);
@@ -157,8 +161,11 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
   State<E, D> st;
   state_zero(st);
   TileRegs<E, D, 64> kl, vl;
+  const int tb = m * a.G * BM;  // first row of segment m
   const int ntile = a.G * (BM / 64);
-  const int ebase = m * a.G * BM - a.W;
+  const int ebase = tb - a.W;
+  // evictions in tile t: 64, or in the last segment those of rows up to T-1
+  auto tile_len = [&](int t) { return fin ? min(64, a.T - tb - 64 * t) : 64; };
   int t0 = 0;
   while (t0 < ntile && ebase + 64 * t0 + 63 < 0) ++t0;  // tiles wholly before the first token
   kl.load(Kg, ebase + 64 * t0);
@@ -173,9 +180,12 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
       kl.load(Kg, e0 + 64);
       vl.load(Vg, e0 + 64);
     }
-    state_update(st, Ks, LDK, Vs, LDK, pw, 64, e0, wid, l16, lg);
+    const int len = tile_len(t);
+    if (len > 0) state_update(st, Ks, LDK, Vs, LDK, pw, len, e0, wid, l16, lg);
   }
-  state_store(st, a.seg_state + ((size_t)bh * a.nseg + m + 1) * D * D, 1.0f, wid, l16, lg);
+  float* dst = fin ? a.seg_state + ((size_t)a.B * a.H * a.nseg + bh) * D * D
+                   : a.seg_state + ((size_t)bh * a.nseg + m + 1) * D * D;
+  state_store(st, dst, 1.0f, wid, l16, lg);
 }
 
 // Chain over segments, in place: seg_state[0] = 0 and

@@ -502,7 +502,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
             accum_pv(P, std::false_type{}, Vc);
           }
         }
-        if (more || (last && a.A_final)) {
+        if (more || (last && a.A_final && !a.final_slot)) {
           __syncthreads();  // every wave has read S(e0)
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
@@ -526,11 +526,43 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
         for (int dt = 0; dt < NT; ++dt) store4(Yg + (size_t)trow * D + dt * 16 + lg * 4, O[g][dt]);
       }
     }
-    if (last && a.A_final) {
+    if (last && a.A_final && !a.final_slot) {
       float* Af = a.A_final + (size_t)bh * D * D;
       __syncthreads();  // the state updates above are done
       const float eta = a.eta[h];
       for (int x = tid; x < D * D; x += NTH) Af[x] = has_mem ? eta * Sl[(x % D) * LDS + x / D] : 0.0f;
+    }
+  }
+  if (seg == 0 && a.final_slot && a.A_final) {
+    // A after step T-1 = eta (lambda^n S_last + L_final): S_last the state at
+    // the last segment's start, L_final that segment's evictions (n of them)
+    constexpr int PER = (D * D + NTH - 1) / NTH;
+    const int last_seg = a.nseg - 1;
+    const float* g = a.seg_state + (size_t)bh * a.nseg * D * D;
+    const float* Lf = a.seg_state + ((size_t)a.B * a.H * a.nseg + bh) * D * D;
+    float acc[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
+    if (a.prefix_direct) {
+      const float dec = powi(a.lam[h], BM * a.G);
+      for (int m = 1; m <= last_seg; ++m) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+          if ((D * D) % NTH == 0 || tid + NTH * k < D * D)
+            acc[k] = dec * acc[k] + g[(size_t)m * D * D + tid + NTH * k];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < PER; ++k)
+        if ((D * D) % NTH == 0 || tid + NTH * k < D * D) acc[k] = g[(size_t)last_seg * D * D + tid + NTH * k];
+    }
+    const float dn = powi(a.lam[h], T - last_seg * a.G * BM);
+    const float eta = a.eta[h];
+    float* Af = a.A_final + (size_t)bh * D * D;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int x = tid + NTH * k;
+      if ((D * D) % NTH == 0 || x < D * D) Af[x] = eta * __builtin_fmaf(dn, acc[k], Lf[x]);
     }
   }
 }
@@ -551,8 +583,11 @@ static hipError_t launch_rows_impl(const FwdArgs& a0, hipStream_t s) {
   FwdArgs a = a0;
   const int BH = a.B * a.H;
   a.prefix_direct = a.nseg <= kDirectPrefixMaxSeg ? 1 : 0;
+  // the state pass also forms the last block's local state (final state without
+  // a state update at the end of the critical path)
+  a.final_slot = (a.nseg > 1 && a.A_final) ? 1 : 0;
   if (a.nseg > 1) {
-    hipLaunchKernelGGL((seg_state_kernel<E, D, BM>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((seg_state_kernel<E, D, BM>), dim3(BH * (a.nseg - 1 + a.final_slot)), dim3(256), 0, s, a);
     if (!a.prefix_direct)
       hipLaunchKernelGGL((seg_chain_kernel<D, BM>), dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, s, a);
   }

@@ -24,6 +24,10 @@ struct FwdArgs {
   int nseg;  // ceil(nblk / G)
   int prefix_direct;  // fused kernel combines the local segment states itself (no chain kernel)
   float scale;
+  // Set by the rows launcher: the state pass also forms the local state of the
+  // last segment's evictions, at seg_state[B*H*nseg + bh], and the workgroup
+  // of segment 0 (an early finisher) forms A_final from it elementwise.
+  int final_slot;
 };
 
 // Decode: one step for S streams x H heads.
