@@ -572,19 +572,26 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dq_kernel(BwdArgs a) {
     }
     put_keys(0);
     __syncthreads();
-    // the next key tile, or after the last one the next query block's rows and first key tile
-    auto next_loads = [&](int mn) {
-      if (mn <= mt) {
-        load_keys(e0 + 64 * mn);
+    // Tile order: the first tile (the evicted chunk when there is one) first,
+    // then every other block walks the rest backwards, so that a block starts
+    // on the key tiles its predecessor used last (still in L2).
+    const int ntl = mt - mlo + 1;
+    const bool rev = ((j - jb) & 1) != 0;
+    auto m_at = [&](int i) { return (!rev || i == 0) ? mlo + i : mt + 1 - i; };
+    // the tile at position i, or after the last one the next query block's rows and first key tile
+    auto next_loads = [&](int i) {
+      if (i < ntl) {
+        load_keys(e0 + 64 * m_at(i));
       } else if (j + 1 < je) {
         load_rows(j + 1);
         load_keys(e0 + 64 + 64 * mlo_of(e0 + 64));
       }
     };
-    next_loads(mlo + 1);
+    next_loads(1);
     float delta = 0.0f;
     int buf = 0;
-    for (int m = mlo; m <= mt; ++m) {
+    for (int i = 0; i < ntl; ++i) {
+      const int m = m_at(i);
       const int k0 = e0 + 64 * m;
       const E* Ks = Kb(buf);
       const E* Vs = Vb(buf);
@@ -626,7 +633,7 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dq_kernel(BwdArgs a) {
         md += xsum4(mp);
         dlr += xsum4(dp);
       }
-      if (m == mlo) {
+      if (i == 0) {
         // Delta = <dy, y> - sigma eta <dy, mt>, the two halves' shares summed
         if (lg == 0) dex[half][r] = yd - seta * md;
         __syncthreads();
@@ -678,13 +685,13 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dq_kernel(BwdArgs a) {
         // S^T[c][a] += sum_c' V[c'][c] w K[c'][a]
         rank64_update<E, D, NW, true>(S, pw[64], B, Vs, Ks, w1, w2, wid, l16, lg);
       }
-      if (m < mt) {
+      if (i + 1 < ntl) {
         const int nb = NB == 2 ? buf ^ 1 : 0;
         if (NB == 1) __syncthreads();
         put_keys(nb);
         __syncthreads();
         buf = nb;
-        next_loads(m + 2);
+        next_loads(i + 2);
       }
     }
     // the pair's dq shares: half h keeps the tiles dt with dt % 2 == h
