@@ -48,6 +48,12 @@ struct BwdCfg {
   static constexpr int TILE = 64 * LDK * (int)sizeof(E);
 };
 
+// Waves per workgroup of the dq, dk/dv and forward segment-state kernels.
+// In dq and dk/dv, waves w and w ^ 4 share one 16-row group (w & 3) and take
+// one half (w >> 2) of each 64-row band tile each; the D x D states are split
+// over all eight.  The pair's partial sums meet in LDS at the end of each block.
+constexpr int kBwdWaves = 8;
+
 // Compile-time variant tag for the per-tile element math.
 template <int V>
 struct Mode {
@@ -250,8 +256,9 @@ __device__ __forceinline__ void put_state_t(const StateTiles<D, NW>& t, bf16* hi
 // Forward: S and B = dS/dlambda over each segment's evictions (from zero);
 // grid = BH * (nseg-1); writes fstate/tstate[bh][m+1].
 template <class E, int D>
-__global__ void __launch_bounds__(256, 2) bseg_fwd_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(64 * kBwdWaves, 1) bseg_fwd_kernel(BwdArgs a) {
   using C = BwdCfg<E, D>;
+  constexpr int NW = kBwdWaves, NTH = 64 * NW, NOWN = (C::NT + NW - 1) / NW;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::TILE];
   __shared__ float pw[72], dpw[72], w1[64], w2[64];
   E* Ks = (E*)smem;
@@ -265,15 +272,16 @@ __global__ void __launch_bounds__(256, 2) bseg_fwd_kernel(BwdArgs a) {
   const auto Kg = make_rsrc((const E*)a.k + base, nbytes);
   const auto Vg = make_rsrc((const E*)a.v + base, nbytes);
   fill_pow_tables(a.lam[h], pw, dpw);
-  StateTiles<D, 4> S, B;
-  zero_tiles<D, 4>(S);
-  zero_tiles<D, 4>(B);
-  TileRegs<E, D, 64> kl, vl;
-  for (int g = 0; g < a.G; ++g) {
+  StateTiles<D, NW> S, B;
+  zero_tiles<D, NW>(S);
+  zero_tiles<D, NW>(B);
+  TileRegs<E, D, 64, NTH> kl, vl;
+  int g = 0;
+  while (g < a.G && (m * a.G + g) * 64 - a.W + 63 < 0) ++g;  // blocks wholly before the first token
+  kl.load(Kg, (m * a.G + g) * 64 - a.W);
+  vl.load(Vg, (m * a.G + g) * 64 - a.W);
+  for (; g < a.G; ++g) {
     const int e0 = (m * a.G + g) * 64 - a.W;
-    if (e0 + 63 < 0) continue;
-    kl.load(Kg, e0);
-    vl.load(Vg, e0);
     __syncthreads();
     kl.store(Ks, C::LDK);
     vl.store(Vs, C::LDK);
@@ -283,15 +291,19 @@ __global__ void __launch_bounds__(256, 2) bseg_fwd_kernel(BwdArgs a) {
       w2[tid] = ok ? dpw[63 - tid] : 0.0f;
     }
     __syncthreads();
+    if (g + 1 < a.G) {  // the next block's chunk, in flight during the update
+      kl.load(Kg, e0 + 64);
+      vl.load(Vg, e0 + 64);
+    }
     // B <- lam^64 B + 64 lam^63 S + sum w2 k v^T ; S <- lam^64 S + sum w1 k v^T
 #pragma unroll
-    for (int o = 0; o < (C::NT + 3) / 4; ++o)
+    for (int o = 0; o < NOWN; ++o)
 #pragma unroll
       for (int mm = 0; mm < C::NT; ++mm) B[o][mm] = pw[64] * B[o][mm] + dpw[64] * S[o][mm];
-    rank64_update<E, D, 4, true>(S, pw[64], B, Ks, Vs, w1, w2, wid, l16, lg);
+    rank64_update<E, D, NW, true>(S, pw[64], B, Ks, Vs, w1, w2, wid, l16, lg);
   }
-  store_tiles<D, 4>(S, a.fstate + ((size_t)bh * a.nseg + m + 1) * D * D, wid, l16, lg);
-  store_tiles<D, 4>(B, a.tstate + ((size_t)bh * a.nseg + m + 1) * D * D, wid, l16, lg);
+  store_tiles<D, NW>(S, a.fstate + ((size_t)bh * a.nseg + m + 1) * D * D, wid, l16, lg);
+  store_tiles<D, NW>(B, a.tstate + ((size_t)bh * a.nseg + m + 1) * D * D, wid, l16, lg);
 }
 
 // S[0] = B[0] = 0; S[m+1] = L S[m] + Ls_m; B[m+1] = L' S[m] + L B[m] + Lb_m
@@ -349,15 +361,20 @@ __global__ void __launch_bounds__(256, 2) bseg_rev_kernel(BwdArgs a) {
   zero_tiles<D, 4>(R);
   const int jb = m * a.G, je = min(a.nblk, jb + a.G);
   TileRegs<E, D, 64> ql, yl;
-  for (int jk = je - 1; jk >= jb; --jk) {
+  int jk = je - 1;
+  while (jk >= jb && jk * 64 + a.W >= a.T) --jk;  // blocks whose queries lie past the end
+  ql.load(Qg, jk * 64 + a.W);
+  yl.load(Yg, jk * 64 + a.W);
+  for (; jk >= jb; --jk) {
     const int q0 = jk * 64 + a.W;
-    if (q0 >= a.T) continue;
-    ql.load(Qg, q0);
-    yl.load(Yg, q0);
     __syncthreads();
     ql.store(Qs, C::LDK);
     yl.store(Ys, C::LDK);
     __syncthreads();
+    if (jk > jb) {  // the next block's queries, in flight during the update
+      ql.load(Qg, q0 - 64);
+      yl.load(Yg, q0 - 64);
+    }
     // R[a][c] <- lam^64 R + sum_c' Q[c'][a] lam^c' dY[c'][c]  (skipped blocks
     // contribute zero and need no decay: R is zero until the first block)
     rank64_update<E, D, 4, false>(R, pw[64], R, Qs, Ys, pw, pw, wid, l16, lg);
@@ -401,12 +418,6 @@ template <class E, int D>
 struct BandBufs {
   static constexpr int N = 6 * BwdCfg<E, D>::TILE <= 150 * 1024 ? 2 : 1;
 };
-
-// The dq and dk/dv kernels run eight waves: waves w and w ^ 4 share one
-// 16-row group (w & 3) and take one half (w >> 2) of each 64-row band tile
-// each; the D x D states are split over all eight.  The pair's partial sums
-// meet in LDS at the end of each block.
-constexpr int kBwdWaves = 8;
 
 // dq kernel: grid = BH * nseg, one 64-row query block at a time.  Per block:
 // the state part of the memory path (S(e0) dy, B(e0) dy), then the key tiles
@@ -1016,7 +1027,7 @@ template <class E, int D>
 static hipError_t launch_bwd_impl(const BwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
   if (a.nseg > 1) {
-    hipLaunchKernelGGL((bseg_fwd_kernel<E, D>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bseg_fwd_kernel<E, D>), dim3(BH * (a.nseg - 1)), dim3(64 * kBwdWaves), 0, s, a);
     hipLaunchKernelGGL((bchain_fwd_kernel<D>), dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, s, a);
     hipLaunchKernelGGL((bseg_rev_kernel<E, D>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
     hipLaunchKernelGGL((bchain_rev_kernel<D>), dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, s, a);
