@@ -322,18 +322,29 @@ __global__ void __launch_bounds__(256) bchain_fwd_kernel(BwdArgs a) {
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f), b = s;
   ps[0] = s;
   pb[0] = b;
-  for (int m = 1; m < a.nseg; ++m) {
-    const float4 ls = ps[m * stride], lb = pb[m * stride];
-    b.x = Ld * s.x + L * b.x + lb.x;
-    b.y = Ld * s.y + L * b.y + lb.y;
-    b.z = Ld * s.z + L * b.z + lb.z;
-    b.w = Ld * s.w + L * b.w + lb.w;
-    s.x = L * s.x + ls.x;
-    s.y = L * s.y + ls.y;
-    s.z = L * s.z + ls.z;
-    s.w = L * s.w + ls.w;
-    ps[m * stride] = s;
-    pb[m * stride] = b;
+  // (eight segments' local states loaded ahead of the dependent chain)
+  for (int m0 = 1; m0 < a.nseg; m0 += 8) {
+    float4 ls[8], lb[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (m0 + u < a.nseg) {
+        ls[u] = ps[(m0 + u) * stride];
+        lb[u] = pb[(m0 + u) * stride];
+      }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (m0 + u < a.nseg) {
+        b.x = Ld * s.x + L * b.x + lb[u].x;
+        b.y = Ld * s.y + L * b.y + lb[u].y;
+        b.z = Ld * s.z + L * b.z + lb[u].z;
+        b.w = Ld * s.w + L * b.w + lb[u].w;
+        s.x = L * s.x + ls[u].x;
+        s.y = L * s.y + ls[u].y;
+        s.z = L * s.z + ls[u].z;
+        s.w = L * s.w + ls[u].w;
+        ps[(m0 + u) * stride] = s;
+        pb[(m0 + u) * stride] = b;
+      }
   }
 }
 
@@ -342,8 +353,9 @@ __global__ void __launch_bounds__(256) bchain_fwd_kernel(BwdArgs a) {
 // Lr_m = sum_{jk in seg, descending} lambda^(64 (jk - jb)) U(jk),
 // U(jk) = sum_{c<64} lambda^c q_{64jk+W+c}^T dy_{64jk+W+c};  writes rstate[bh][m-1].
 template <class E, int D>
-__global__ void __launch_bounds__(256, 2) bseg_rev_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(64 * kBwdWaves, 1) bseg_rev_kernel(BwdArgs a) {
   using C = BwdCfg<E, D>;
+  constexpr int NW = kBwdWaves, NTH = 64 * NW;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::TILE];
   __shared__ float pw[72], dpw[72];
   E* Qs = (E*)smem;
@@ -357,10 +369,10 @@ __global__ void __launch_bounds__(256, 2) bseg_rev_kernel(BwdArgs a) {
   const auto Qg = make_rsrc((const E*)a.q + base, nbytes);
   const auto Yg = make_rsrc((const E*)a.dy + base, nbytes);
   fill_pow_tables(a.lam[h], pw, dpw);
-  StateTiles<D, 4> R;
-  zero_tiles<D, 4>(R);
+  StateTiles<D, NW> R;
+  zero_tiles<D, NW>(R);
   const int jb = m * a.G, je = min(a.nblk, jb + a.G);
-  TileRegs<E, D, 64> ql, yl;
+  TileRegs<E, D, 64, NTH> ql, yl;
   int jk = je - 1;
   while (jk >= jb && jk * 64 + a.W >= a.T) --jk;  // blocks whose queries lie past the end
   ql.load(Qg, jk * 64 + a.W);
@@ -377,11 +389,11 @@ __global__ void __launch_bounds__(256, 2) bseg_rev_kernel(BwdArgs a) {
     }
     // R[a][c] <- lam^64 R + sum_c' Q[c'][a] lam^c' dY[c'][c]  (skipped blocks
     // contribute zero and need no decay: R is zero until the first block)
-    rank64_update<E, D, 4, false>(R, pw[64], R, Qs, Ys, pw, pw, wid, l16, lg);
+    rank64_update<E, D, NW, false>(R, pw[64], R, Qs, Ys, pw, pw, wid, l16, lg);
   }
   // blocks skipped at the top (q0 >= T) would only scale a zero state;
   // blocks present below them were decayed correctly relative to jb.
-  store_tiles<D, 4>(R, a.rstate + ((size_t)bh * a.nseg + m - 1) * D * D, wid, l16, lg);
+  store_tiles<D, NW>(R, a.rstate + ((size_t)bh * a.nseg + m - 1) * D * D, wid, l16, lg);
 }
 
 // R_end[nseg-1] = 0; R_end[m] = lambda^(64G) R_end[m+1] + Lr_{m+1} (in place).
@@ -395,13 +407,21 @@ __global__ void __launch_bounds__(256) bchain_rev_kernel(BwdArgs a) {
   const size_t stride = (size_t)D * D / 4;
   float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
   p[(a.nseg - 1) * stride] = r;
-  for (int m = a.nseg - 2; m >= 0; --m) {
-    const float4 l = p[m * stride];
-    r.x = L * r.x + l.x;
-    r.y = L * r.y + l.y;
-    r.z = L * r.z + l.z;
-    r.w = L * r.w + l.w;
-    p[m * stride] = r;
+  // (eight segments' local adjoints loaded ahead of the dependent chain)
+  for (int m0 = a.nseg - 2; m0 >= 0; m0 -= 8) {
+    float4 l[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (m0 - u >= 0) l[u] = p[(m0 - u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (m0 - u >= 0) {
+        r.x = L * r.x + l[u].x;
+        r.y = L * r.y + l[u].y;
+        r.z = L * r.z + l[u].z;
+        r.w = L * r.w + l[u].w;
+        p[(m0 - u) * stride] = r;
+      }
   }
 }
 
@@ -1029,7 +1049,7 @@ static hipError_t launch_bwd_impl(const BwdArgs& a, hipStream_t s) {
   if (a.nseg > 1) {
     hipLaunchKernelGGL((bseg_fwd_kernel<E, D>), dim3(BH * (a.nseg - 1)), dim3(64 * kBwdWaves), 0, s, a);
     hipLaunchKernelGGL((bchain_fwd_kernel<D>), dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((bseg_rev_kernel<E, D>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bseg_rev_kernel<E, D>), dim3(BH * (a.nseg - 1)), dim3(64 * kBwdWaves), 0, s, a);
     hipLaunchKernelGGL((bchain_rev_kernel<D>), dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, s, a);
   }
   hipLaunchKernelGGL((dq_kernel<E, D>), dim3(BH * a.nseg), dim3(64 * kBwdWaves), 0, s, a);
