@@ -98,6 +98,18 @@ def test_backward_multi_segment_walk():
         assert e <= TOL["f32"], (key, e)
 
 
+def test_backward_multi_segment_walk_f32_d128():
+    """float32 with D = 128 (single-buffered band tiles, the only path that
+    does not double-buffer) and two blocks per segment, W not a multiple of 64."""
+    say("backward multi-segment f32 D=128")
+    d = tc_inputs.prefill_inputs(5, seed=13, B=1, H=2, T=64 * 260 + 5, D=128, W=70, dtype="f32",
+                                 with_dy=True)
+    err = compare(d, 70)
+    say("  errors", err)
+    for key, e in err.items():
+        assert e <= TOL["f32"], (key, e)
+
+
 @pytest.mark.parametrize("W", [333, 64 * 5])
 def test_backward_blocks_per_segment_bf16(W):
     """bf16, several 64-row blocks per workgroup segment (B*H*blocks > 512),
