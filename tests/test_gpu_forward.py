@@ -122,11 +122,14 @@ def test_forward_segment_prefix_paths(T):
         assert e <= TOL["bf16"], (key, e)
 
 
-def test_forward_blocks_per_segment_bf16():
+@pytest.mark.parametrize("T", [1024, 1024 + 37])
+def test_forward_blocks_per_segment_bf16(T):
     """Many heads, short sequences: each workgroup walks several 128-row
-    blocks, carrying the state through its chunk updates."""
-    say("forward several blocks per segment")
-    d = tc_inputs.prefill_inputs(2, seed=22, B=4, H=64, T=1024, D=64, W=200, dtype="bf16", plants=False)
+    blocks, carrying the state through its chunk updates; the final state
+    comes from the last segment's local state (with a ragged last block for
+    T = 1061)."""
+    say("forward several blocks per segment", T)
+    d = tc_inputs.prefill_inputs(2, seed=22, B=4, H=64, T=T, D=64, W=200, dtype="bf16", plants=False)
     err = run_and_compare(d, 200, heads=[(0, 0), (1, 33), (3, 63)])
     say("  errors", err)
     for key, e in err.items():
