@@ -276,8 +276,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the TC hot path has no multi-GPU mode in this build "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU only: the TC hot path here runs on a single GPU, with no "
+              "multi-GPU mode (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
 
