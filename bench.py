@@ -136,7 +136,7 @@ def prefill_leg(cfg_id, steps, warmup):
         ms_per_call=ms, tokens_per_s=cfg.B * cfg.T / (ms * 1e-3), flops=fl, bytes=by,
         roofline=dict(bound="mfma", achieved=tflops, peak=PEAK_BF16, unit="TFLOP/s", frac=tflops / PEAK_BF16,
                       traffic=measured_traffic().get("prefill" if cfg_id == 2 else "long"),
-                      kernel="one tc_forward call (seg_state_kernel [+ seg_chain_kernel] + fwd_kernel_rows)"),
+                      kernel="one tc_forward call (fwd_kernel_rows; with several blocks per segment also seg_state_kernel [+ seg_chain_kernel])"),
         hbm_gbs=by / (ms * 1e-3) / 1e9,
     )
 

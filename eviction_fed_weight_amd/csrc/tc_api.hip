@@ -1,7 +1,10 @@
 // C ABI of the TC layer: host-side validation, workspace planning and
-// dispatch to the gfx950 kernels.  No allocation, no synchronisation, no
-// global mutable state.
+// dispatch to the gfx950 kernels.  No allocation and no synchronisation;
+// the only global state is a call counter (the forward's flag values).
 #include <math.h>
+
+#include <atomic>
+#include <random>
 #include <stdint.h>
 #include <string.h>
 
@@ -74,6 +77,23 @@ Plan plan_for(const tc_shape_t& s) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Forward workspace: the segment states, then one 64-bit flag per segment.
+size_t fwd_flags_bytes(const tc_shape_t& s, const Plan& p) {
+  return align256((size_t)s.B * s.H * p.nseg * sizeof(unsigned long long));
+}
+
+// Flag value of one forward call: a per-process random salt combined with a
+// call counter, so that flags left in a reused workspace by earlier calls,
+// or arbitrary initial contents, do not match it.
+unsigned long long next_generation() {
+  static std::atomic<unsigned long long> counter{0};
+  static const unsigned long long salt = [] {
+    std::random_device rd;
+    return ((unsigned long long)rd() << 32) ^ ((unsigned long long)rd() << 11) ^ 0x9E3779B97F4A7C15ull;
+  }();
+  return salt ^ (counter.fetch_add(1) + 1);
+}
+
 tc_status_t check_shape(const tc_shape_t* s) {
   if (!s) return TC_ERR_INVALID_ARGUMENT;
   if (s->B < 1 || s->H < 1 || s->T < 1 || s->W < 1 || s->C < 1 || s->D < 1)
@@ -109,7 +129,8 @@ const char* tc_version(void) { return "0.1.0"; }
 
 size_t tc_forward_workspace_size(const tc_shape_t* s) {
   if (check_shape(s) != TC_OK) return 0;
-  return align256(plan_for(*s).state_bytes);
+  const Plan p = plan_for(*s);
+  return align256(p.state_bytes) + fwd_flags_bytes(*s, p);
 }
 
 tc_status_t tc_forward(const tc_shape_t* s, const void* q, const void* k, const void* v,
@@ -133,7 +154,7 @@ tc_status_t tc_forward(const tc_shape_t* s, const void* q, const void* k, const 
       if (overlap(outs[o], outsz[o], outs[p], outsz[p])) return TC_ERR_INVALID_ARGUMENT;
   }
   const Plan p = plan_for(*s);
-  const size_t need = align256(p.state_bytes);
+  const size_t need = align256(p.state_bytes) + fwd_flags_bytes(*s, p);
   if (p.nseg > 1 && (!ws || ws_bytes < need)) return TC_ERR_WORKSPACE;
   if (ws && ws_bytes >= need) {
     for (int o = 0; o < 3; ++o)
@@ -152,6 +173,8 @@ tc_status_t tc_forward(const tc_shape_t* s, const void* q, const void* k, const 
   a.A_final = A_final;
   a.lse = lse;
   a.seg_state = (float*)ws;
+  a.flags = ws && ws_bytes >= need ? (unsigned long long*)((char*)ws + align256(p.state_bytes)) : nullptr;
+  a.gen = next_generation();
   a.B = s->B;
   a.H = s->H;
   a.T = s->T;

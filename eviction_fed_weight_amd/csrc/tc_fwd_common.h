@@ -45,7 +45,8 @@ __device__ __forceinline__ void state_update(State<E, D>& st, const E* Ks, int l
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int c = kc * 32 + lg * 8 + j;
-            const float w = (c < len && e0 + c >= 0) ? pw[len - 1 - c] : 0.0f;
+            // (branch-free: the LDS read is unconditional, at a clamped index)
+        const float w = ((c < len && e0 + c >= 0) ? 1.0f : 0.0f) * pw[max(len - 1 - c, 0)];
             wv[j] = w * vv[j];
           }
         }
@@ -99,6 +100,88 @@ __device__ __forceinline__ void state_store(const State<E, D>& st, float* g, flo
       for (int at = 0; at < NT; ++at)
 #pragma unroll
         for (int i = 0; i < 4; ++i) g[(at * 16 + lg * 4 + i) * D + ct * 16 + l16] = mult * st.s[o][at][i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// States exchanged between workgroups of one launch.  Buffer stores and loads
+// with the sc1 cache policy are coherent across the whole device (they do not
+// stop in a compute unit's or an XCD's cache), the same policy the compiler
+// gives agent-scope atomics; a state is laid out in the accumulator order of
+// State (256 contiguous bytes per wave and tile).
+constexpr int kCoherentPolicy = 16;  // buffer cache-policy bits: sc1
+// Default bound on the polls of one flag (a tenth of a second or more,
+// against waits of microseconds): it guarantees that every wave ends.
+constexpr int kPublishPolls = 1 << 16;
+
+template <class E, int D>
+__device__ __forceinline__ void state_publish(const State<E, D>& st, float* g, int wid, int lane) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  constexpr int NT = D / 16;
+  const auto rs = make_rsrc(g, D * D * 4);
+#pragma unroll
+  for (int o = 0; o < State<E, D>::NOWN; ++o) {
+    const int ct = wid + 4 * o;
+    if (ct < NT) {
+#pragma unroll
+      for (int at = 0; at < NT; ++at)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, st.s[o][at]), rs,
+                                               (uint32_t)(((ct * NT + at) * 64 + lane) * 16), 0, kCoherentPolicy);
+    }
+  }
+}
+
+// acc = sum_{m0 <= m < m1} dec^(m1-1-m) (the state published at g + m D^2),
+// the loads of up to four states in flight at once
+template <class E, int D>
+__device__ __forceinline__ void state_gather_all(State<E, D>& acc, float dec, const float* g, int m0, int m1,
+                                                 int wid, int lane) {
+  constexpr int NT = D / 16, NOWN = State<E, D>::NOWN;
+  const auto rs = make_rsrc(g, (uint32_t)m1 * D * D * 4);
+  for (int mb = m0; mb < m1; mb += 4) {
+    f32x4 x[4][NOWN][NT];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int o = 0; o < NOWN; ++o)
+#pragma unroll
+        for (int at = 0; at < NT; ++at) {
+          const int ct = wid + 4 * o;
+          // (states past m1 and tiles past NT read zeros: offset outside the buffer)
+          const uint32_t off = (mb + u < m1 && ct < NT)
+                                   ? (uint32_t)((mb + u) * D * D * 4 + ((ct * NT + at) * 64 + lane) * 16)
+                                   : 0x80000000u;
+          x[u][o][at] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCoherentPolicy));
+        }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (mb + u < m1)
+#pragma unroll
+        for (int o = 0; o < NOWN; ++o)
+#pragma unroll
+          for (int at = 0; at < NT; ++at) acc.s[o][at] = dec * acc.s[o][at] + x[u][o][at];
+  }
+}
+
+template <class E, int D>
+__device__ __forceinline__ void state_fill(State<E, D>& st, float x) {
+#pragma unroll
+  for (int o = 0; o < State<E, D>::NOWN; ++o)
+#pragma unroll
+    for (int at = 0; at < D / 16; ++at) st.s[o][at] = f32x4{x, x, x, x};
+}
+
+// S^T into LDS: S[a][c] at Sl[c * LDS + a]
+template <class E, int D, int LDS>
+__device__ __forceinline__ void state_to_lds_t(const State<E, D>& st, float* Sl, int wid, int l16, int lg) {
+  constexpr int NT = D / 16;
+#pragma unroll
+  for (int o = 0; o < State<E, D>::NOWN; ++o) {
+    const int ct = wid + 4 * o;
+    if (ct < NT) {
+#pragma unroll
+      for (int at = 0; at < NT; ++at) *(f32x4*)(Sl + (16 * ct + l16) * LDS + 16 * at + 4 * lg) = st.s[o][at];
     }
   }
 }

@@ -34,6 +34,9 @@
 // groups; 4 more give the row sums of P).  The running max is only moved
 // when a row's maximum grows by more than 2^8 (probabilities stay below 256),
 // which leaves most tiles without the rescale of the accumulators.
+#include <stdlib.h>
+
+#include <atomic>
 #include <type_traits>
 
 #include "tc_device.h"
@@ -131,7 +134,8 @@ __device__ __forceinline__ void lds_state_update(float* Sl, const E* Ks, int ldk
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int c = kc * 32 + lg * 8 + j;
-        const float w = (c < len && e0 + c >= 0) ? pw[len - 1 - c] : 0.0f;
+        // (branch-free: the LDS read is unconditional, at a clamped index)
+        const float w = ((c < len && e0 + c >= 0) ? 1.0f : 0.0f) * pw[max(len - 1 - c, 0)];
         wv[j] = w * vv[j];
       }
     }
@@ -148,7 +152,9 @@ __device__ __forceinline__ void lds_state_update(float* Sl, const E* Ks, int ldk
   for (int k = 0; k < AT; ++k) *(f32x4*)(col + 16 * (ar * AT + k)) = st[k];
 }
 
-template <class E, int D, int NW>
+// PUB: one block per segment, local states exchanged through flags (see
+// FwdArgs::publish); otherwise the segment states come from the state pass.
+template <class E, int D, int NW, bool PUB>
 __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdArgs a) {
   using M = Mfma<E>;
   using frag = typename M::frag;
@@ -163,7 +169,12 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   constexpr int LDS = L::LDS;
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
-  const int wg = xcd_remap_paired(blockIdx.x, gridDim.x);
+  // PUB: segment-major order (workgroup b takes segment b / BH of head b % BH),
+  // so a workgroup waits only for workgroups dispatched before it, and with
+  // B*H a multiple of 8 all segments of a head run on one XCD (b % 8).
+  // Otherwise: one head's segments on one XCD, heavy and light segments paired.
+  const int BHn = a.B * a.H;
+  const int wg = PUB ? (blockIdx.x % BHn) * a.nseg + blockIdx.x / BHn : xcd_remap_paired(blockIdx.x, gridDim.x);
   const int bh = wg / a.nseg, seg = wg - bh * a.nseg;
   const int h = bh % a.H;
   const int T = a.T, W = a.W;
@@ -187,8 +198,14 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   // 2 .. ihi first and tiles 0 and 1 last; after the last one (softmax done)
   // both chunk tiles are still in the two LDS buffers for the memory read and
   // the state update, so the chunk costs no items of its own.
+  //
+  // With PUB the evicting block visits its window tiles in order 0 .. ihi
+  // instead (forming and publishing its local state while tiles 0 and 1 are
+  // in the buffers, early enough for the stores to complete under the rest of
+  // the window) and then loads the chunk tiles 0 and 1 once more as nlate
+  // items of their own.
   struct Blk {
-    int t0, kb, ilo, nfront, nlate, nb, nit;
+    int t0, kb, ilo, nfront, nlate, nwin, nb, nit;
     bool mem;
   };
   auto blk = [&](int j) {
@@ -199,14 +216,16 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
     b.mem = b.t0 + BM - 1 >= W;
     if (b.mem) {
       b.nlate = min(2, ihi + 1);
-      b.ilo = 2;
-      b.nfront = ihi + 1 - b.nlate;
+      b.ilo = PUB ? 0 : 2;
+      b.nfront = PUB ? ihi + 1 : ihi + 1 - b.nlate;
+      b.nwin = ihi + 1;
     } else {
       b.nlate = 0;
       b.ilo = (-b.kb - 63 > 0) ? ((-b.kb) >> 6) : 0;  // first tile with a key >= 0
       b.nfront = ihi - b.ilo + 1;
+      b.nwin = b.nfront;
     }
-    b.nb = b.nfront + b.nlate;
+    b.nb = b.nfront + b.nlate;  // key/value items; the first nwin are window tiles
     b.nit = NQ + b.nb;
     return b;
   };
@@ -254,8 +273,10 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
 
   if (tid <= BM) pw[tid] = powi(a.lam[h], tid);
 
-  // S(e0) of the segment's first block -> LDS (transposed)
-  if (seg == 0) {
+  // S(e0) of the segment's first block -> LDS (transposed); with publish it
+  // is gathered after the window, from the earlier segments' published states
+  if (PUB) {
+  } else if (seg == 0) {
     for (int x = tid; x < D * D; x += NTH) Sl[(x % D) * LDS + x / D] = 0.0f;
   } else if (a.prefix_direct) {
     // S at the segment start from the local states L_m (stored at index m+1):
@@ -286,7 +307,8 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
 
   int kv_used = 0;  // key/value items consumed (buffer parity)
   const int rw = 32 * wid;  // first row of this wave within the block
-  for (int j = jb; j < je; ++j) {
+  // (PUB: exactly one block per segment, so no loop for the compiler to hoist out of)
+  for (int j = jb; j < (PUB ? jb + 1 : je); ++j) {
     const Blk cb = blk(j);
     const int t0 = cb.t0, e0 = t0 - W;
     const int nb = cb.nb;
@@ -365,11 +387,19 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
       }
     };
 
+    // One block per segment (PUB): segments m >= m_lo have evictions at or
+    // after token 0 (L_m != 0); S(e0) = sum_{m_lo <= m < seg} lambda^((seg-1-m) BM) L_m.
+    const int m_lo = W / BM;
+    const bool pub = PUB && seg >= m_lo && seg + 1 < a.nseg;
+    const bool fin = PUB && last && a.A_final != nullptr && has_mem;
+    float* const Lt = (float*)Qs;  // L^T of the last block (the Q area is free after qf is read)
+    float* const slots = a.seg_state + (size_t)bh * a.nseg * D * D;
+
     for (int it = 0; it < nb; ++it) {
       const E* Kb = (const E*)(smem + (kv_used & 1) * L::BUF);
       const E* Vb = (const E*)(smem + (kv_used & 1) * L::BUF + L::KT);
 
-      {
+      if (it < cb.nwin) {
         // ---- window tile: keys k0 .. k0+63 ----
         const int k0 = cb.kb + 64 * tile_of(cb, it);
         // (tiles of early blocks may start before token 0: those keys are masked)
@@ -428,94 +458,160 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
             tile(std::false_type{});
         }
       }
-      ++kv_used;
-      step();
-    }
-
-    // ---- after the window: normalise, read S(e0), the evicted chunk, the state ----
-    // (the last step wrote only the Q area: both chunk tiles are still in the buffers)
-      // softmax done: normalise, then add the read of S(e0)
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const float l = Lsum[g][0];
-        const float inv = 1.0f / l;
-#pragma unroll
-        for (int dt = 0; dt < NT; ++dt) O[g][dt] *= inv;
-        const int trow = R0 + 16 * g + l16;
-        if (a.lse && lg == 0 && trow < T) a.lse[(size_t)bh * T + trow] = (mrow[g] + __log2f(l)) * kLn2;
-      }
-      if (has_mem && e0 > 0) {
-        // O += sigma(g) eta lambda^(r+1) q S(e0), S^T read from LDS as hi/lo bf16
-#pragma unroll
-        for (int dt = 0; dt < NT; ++dt) {
-          f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-          for (int dc = 0; dc < NKC; ++dc) {
-            const bool in = dc * 32 + lg * 8 < D;  // D = 16: upper half of the contraction is empty
-            float sv[8];
-            {
-              const float* p = Sl + (dt * 16 + l16) * LDS + dc * 32 + lg * 8;
-              const f32x4 x0 = in ? *(const f32x4*)p : f32x4{0.f, 0.f, 0.f, 0.f};
-              const f32x4 x1 = in ? *(const f32x4*)(p + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                sv[i] = x0[i];
-                sv[4 + i] = x1[i];
-              }
-            }
-            frag shi, slo;
-            M::split(sv, shi, slo);
-            acc[0] = M::mma(shi, qf[0][dc], acc[0]);
-            acc[1] = M::mma(shi, qf[1][dc], acc[1]);
-            if (M::kSplit) {
-              acc[0] = M::mma(slo, qf[0][dc], acc[0]);
-              acc[1] = M::mma(slo, qf[1][dc], acc[1]);
-            }
-          }
-#pragma unroll
-          for (int g = 0; g < 2; ++g) O[g][dt] += (seta * pw[rw + 16 * g + l16 + 1]) * acc[g];
-        }
-      }
-      if (has_mem) {
-        // the evicted chunk: tiles 0 and 1 were the last nlate items, still in the two buffers
+      if (PUB && has_mem && (pub || fin) && it == min(1, cb.nwin - 1)) {
+        // chunk tiles 0 .. it are the window items 0 .. it, still in the two buffers:
+        // L of this block's evictions (the last block: those of rows up to T-1)
+        State<E, D> st;
+        state_zero(st);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          if (c < cb.nlate && 64 * c <= rw + 31) {
-            const int ub = kv_used - cb.nlate + c;  // kv index of chunk tile c
-            const E* Kc = (const E*)(smem + (ub & 1) * L::BUF);
-            const E* Vc = (const E*)(smem + (ub & 1) * L::BUF + L::KT);
-            f32x4 Z[2][4];
-            scores(Z, Kc);
-            float P[2][16];
-#pragma unroll
-            for (int g = 0; g < 2; ++g) {
-              const int r = rw + 16 * g + l16;  // row within the block
-#pragma unroll
-              for (int n = 0; n < 4; ++n)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const int ci = 64 * c + 16 * n + 4 * lg + i;  // index within the chunk
-                  const float w = (ci <= r && e0 + ci >= 0) ? seta * pw[r - ci] : 0.0f;
-                  P[g][8 * (n >> 1) + 4 * (n & 1) + i] = w * Z[g][n][i];
-                }
-            }
-            accum_pv(P, std::false_type{}, Vc);
+          const int len = pub ? 64 : min(64, T - t0 - 64 * c);
+          if (c <= it && len > 0) {
+            const int ub = kv_used - it + c;
+            state_update(st, (const E*)(smem + (ub & 1) * L::BUF), LDK, (const E*)(smem + (ub & 1) * L::BUF + L::KT),
+                         LDV, pw, len, e0 + 64 * c, wid, l16, lg);
           }
         }
-        if (more || (last && a.A_final && !a.final_slot)) {
-          __syncthreads();  // every wave has read S(e0)
+        if (pub)
+          state_publish(st, slots + (size_t)(seg + 1) * D * D, wid, lane);
+        else
+          state_to_lds_t<E, D, LDS>(st, Lt, wid, l16, lg);
+        __syncthreads();  // tile 0 is read by every wave before the step below overwrites its buffer
+      }
+      ++kv_used;
+      const bool flag_now = pub && it == cb.nwin - 1;
+      if (flag_now) __builtin_amdgcn_s_waitcnt(0);  // this thread's published stores are complete
+      step();
+      if (flag_now && tid == 0)  // (after the barrier: every thread's stores are complete)
+        __hip_atomic_store(a.flags + (size_t)bh * a.nseg + seg, a.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ---- after the window: normalise, the evicted chunk, read S(e0), the state ----
+    // (the last step wrote only the Q area: both chunk tiles are still in the buffers)
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int len = more ? 64 : min(64, T - t0 - 64 * c);
-            if (c < cb.nlate && len > 0) {
-              const int ub = kv_used - cb.nlate + c;  // kv index of chunk tile c
-              const E* Kc = (const E*)(smem + (ub & 1) * L::BUF);
-              const E* Vc = (const E*)(smem + (ub & 1) * L::BUF + L::KT);
-              lds_state_update<E, D, NW>(Sl, Kc, LDK, Vc, LDV, pw, len, e0 + 64 * c, wid, l16, lg);
-            }
+    for (int g = 0; g < 2; ++g) {
+      const float l = Lsum[g][0];
+      const float inv = 1.0f / l;
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) O[g][dt] *= inv;
+      const int trow = R0 + 16 * g + l16;
+      if (a.lse && lg == 0 && trow < T) a.lse[(size_t)bh * T + trow] = (mrow[g] + __log2f(l)) * kLn2;
+    }
+    auto chunk_tile = [&](int c, const E*& Kc, const E*& Vc) {
+      const int ub = kv_used - cb.nlate + c;  // kv index of chunk tile c (tiles 0, 1 were the last nlate items)
+      Kc = (const E*)(smem + (ub & 1) * L::BUF);
+      Vc = (const E*)(smem + (ub & 1) * L::BUF + L::KT);
+    };
+    // PUB: the first read of the earlier segments' flags is issued here and
+    // returns while the chunk terms below are computed
+    const bool poller = PUB && seg > m_lo && tid < seg - m_lo;
+    const unsigned long long* const myflag = a.flags + (size_t)bh * a.nseg + m_lo + tid;
+    unsigned long long flag0 = 0;
+    if (poller) flag0 = __hip_atomic_load(myflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (has_mem) {
+      // O += sigma(g) eta sum_{c <= r} lambda^(r-c) <q_r, k_{e0+c}> v_{e0+c}
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if (c < cb.nlate && 64 * c <= rw + 31) {
+          const E *Kc, *Vc;
+          chunk_tile(c, Kc, Vc);
+          f32x4 Z[2][4];
+          scores(Z, Kc);
+          float P[2][16];
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            int r = rw + 16 * g + l16;  // row within the block
+            // (opaque here, so the 16 weights' masks and LDS offsets are formed at
+            // their use instead of being kept, or spilled, across the block loop)
+            asm volatile("" : "+v"(r));
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int ci = 64 * c + 16 * n + 4 * lg + i;  // index within the chunk
+                // (branch-free: the LDS read is unconditional, at a clamped index)
+                const float on = (ci <= r && e0 + ci >= 0) ? seta : 0.0f;
+                P[g][8 * (n >> 1) + 4 * (n & 1) + i] = on * pw[max(r - ci, 0)] * Z[g][n][i];
+              }
           }
+          accum_pv(P, std::false_type{}, Vc);
         }
       }
+    }
+    if (PUB) {
+      if (seg > m_lo) {
+        // wait for the earlier segments' flags (bounded, so that every wave
+        // ends; the workgroups waited for were dispatched earlier and wait for
+        // nothing later, so the bound is not reached; were it reached, the
+        // read would be NaN instead of a stale state)
+        bool seen = !poller || (a.max_polls > 0 && flag0 == a.gen);
+        for (int n = 0; !seen && n < a.max_polls; ++n) {
+          __builtin_amdgcn_s_sleep(1);
+          seen = __hip_atomic_load(myflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.gen;
+        }
+        const bool ran_out = __syncthreads_or(!seen);
+        State<E, D> acc;
+        state_zero(acc);
+        state_gather_all(acc, pw[BM], slots, m_lo + 1, seg + 1, wid, lane);
+        if (ran_out) state_fill(acc, __builtin_nanf(""));
+        state_to_lds_t<E, D, LDS>(acc, Sl, wid, l16, lg);
+      }
+      __syncthreads();  // S(e0) (and L^T of the last block) in LDS for every wave
+      if (last && a.A_final) {
+        // A after step T-1 = eta (lambda^n S(e0) + L), n = T - t0 evictions in this block
+        float* Af = a.A_final + (size_t)bh * D * D;
+        const float dn = pw[T - t0], eta = a.eta[h];
+        const float sm = seg > m_lo ? 1.0f : 0.0f;  // S(e0) = 0 when no earlier segment evicted
+        for (int x = tid; x < D * D; x += NTH) {
+          const int ar = x / D, cc = x % D;
+          Af[x] = fin ? eta * __builtin_fmaf(sm * dn, Sl[cc * LDS + ar], Lt[cc * LDS + ar]) : 0.0f;
+        }
+      }
+    }
+    if (has_mem && e0 > 0) {
+      // O += sigma(g) eta lambda^(r+1) q S(e0), S^T read from LDS as hi/lo bf16
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) {
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int dc = 0; dc < NKC; ++dc) {
+          const bool in = dc * 32 + lg * 8 < D;  // D = 16: upper half of the contraction is empty
+          float sv[8];
+          {
+            const float* p = Sl + (dt * 16 + l16) * LDS + dc * 32 + lg * 8;
+            const f32x4 x0 = in ? *(const f32x4*)p : f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 x1 = in ? *(const f32x4*)(p + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              sv[i] = x0[i];
+              sv[4 + i] = x1[i];
+            }
+          }
+          frag shi, slo;
+          M::split(sv, shi, slo);
+          acc[0] = M::mma(shi, qf[0][dc], acc[0]);
+          acc[1] = M::mma(shi, qf[1][dc], acc[1]);
+          if (M::kSplit) {
+            acc[0] = M::mma(slo, qf[0][dc], acc[0]);
+            acc[1] = M::mma(slo, qf[1][dc], acc[1]);
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g) O[g][dt] += (seta * pw[rw + 16 * g + l16 + 1]) * acc[g];
+      }
+    }
+    if (!PUB && has_mem && (more || (last && a.A_final && !a.final_slot))) {
+      __syncthreads();  // every wave has read S(e0)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int len = more ? 64 : min(64, T - t0 - 64 * c);
+        if (c < cb.nlate && len > 0) {
+          const E *Kc, *Vc;
+          chunk_tile(c, Kc, Vc);
+          lds_state_update<E, D, NW>(Sl, Kc, LDK, Vc, LDV, pw, len, e0 + 64 * c, wid, l16, lg);
+        }
+      }
+    }
 
     // ---- store y ----
 #pragma unroll
@@ -526,14 +622,14 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
         for (int dt = 0; dt < NT; ++dt) store4(Yg + (size_t)trow * D + dt * 16 + lg * 4, O[g][dt]);
       }
     }
-    if (last && a.A_final && !a.final_slot) {
+    if (!PUB && last && a.A_final && !a.final_slot) {
       float* Af = a.A_final + (size_t)bh * D * D;
       __syncthreads();  // the state updates above are done
       const float eta = a.eta[h];
       for (int x = tid; x < D * D; x += NTH) Af[x] = has_mem ? eta * Sl[(x % D) * LDS + x / D] : 0.0f;
     }
   }
-  if (seg == 0 && a.final_slot && a.A_final) {
+  if (!PUB && seg == 0 && a.final_slot && a.A_final) {
     // A after step T-1 = eta (lambda^n S_last + L_final): S_last the state at
     // the last segment's start, L_final that segment's evictions (n of them)
     constexpr int PER = (D * D + NTH - 1) / NTH;
@@ -577,21 +673,55 @@ constexpr int kDirectPrefixMaxSeg = 16;
 // workgroup per unit, which measured slower.)
 constexpr int kRowWaves = 4;
 
+// Workgroups of the rows kernel that the current device holds at once (0 if
+// unknown), kept per device after the first query.
+template <class E, int D, int NW>
+static long long rows_resident_capacity() {
+  static std::atomic<long long> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  long long c = cache[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fwd_kernel_rows<E, D, NW, true>, 64 * NW, 0) != hipSuccess)
+      return 0;
+    c = (long long)cus * per;
+    cache[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
 template <class E, int D>
 static hipError_t launch_rows_impl(const FwdArgs& a0, hipStream_t s) {
   constexpr int NW = kRowWaves, BM = 32 * NW;
   FwdArgs a = a0;
   const int BH = a.B * a.H;
   a.prefix_direct = a.nseg <= kDirectPrefixMaxSeg ? 1 : 0;
-  // the state pass also forms the last block's local state (final state without
-  // a state update at the end of the critical path)
-  a.final_slot = (a.nseg > 1 && a.A_final) ? 1 : 0;
-  if (a.nseg > 1) {
+  // One block per segment and a grid the device holds at once: the
+  // workgroups exchange their local states through flags and no state pass
+  // runs.  (The residency test is for speed only: a workgroup waits only for
+  // workgroups dispatched before it, so the waits end in any case.)
+  a.publish = (a.G == 1 && a.nseg > 1 && a.prefix_direct && a.flags != nullptr &&
+               (long long)BH * a.nseg <= rows_resident_capacity<E, D, NW>())
+                  ? 1
+                  : 0;
+  // otherwise the state pass also forms the last block's local state (final
+  // state without a state update at the end of the critical path)
+  a.final_slot = (!a.publish && a.nseg > 1 && a.A_final) ? 1 : 0;
+  // (TC_FORWARD_MAX_POLLS overrides the poll bound: 0 makes every wait end at
+  // once, which is how the path of a wait that runs out is tested)
+  const char* polls = getenv("TC_FORWARD_MAX_POLLS");
+  a.max_polls = polls ? atoi(polls) : kPublishPolls;
+  if (a.nseg > 1 && !a.publish) {
     hipLaunchKernelGGL((seg_state_kernel<E, D, BM>), dim3(BH * (a.nseg - 1 + a.final_slot)), dim3(256), 0, s, a);
     if (!a.prefix_direct)
       hipLaunchKernelGGL((seg_chain_kernel<D, BM>), dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, s, a);
   }
-  hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW>), dim3(BH * a.nseg), dim3(64 * NW), 0, s, a);
+  if (a.publish)
+    hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, true>), dim3(BH * a.nseg), dim3(64 * NW), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, false>), dim3(BH * a.nseg), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 

@@ -28,6 +28,15 @@ struct FwdArgs {
   // last segment's evictions, at seg_state[B*H*nseg + bh], and the workgroup
   // of segment 0 (an early finisher) forms A_final from it elementwise.
   int final_slot;
+  // Set by the rows launcher when there is one block per segment and the
+  // whole grid is resident at once: instead of a state pass, each workgroup
+  // forms the local state of its evicted chunk after its window work, stores
+  // it at seg_state[bh][seg + 1] and sets flags[bh * nseg + seg] = gen; a
+  // later segment of the head waits for those flags before its memory read.
+  int publish;
+  unsigned long long* flags;  // [B*H][nseg], in the workspace after the states
+  unsigned long long gen;     // this call's flag value
+  int max_polls;              // bound on the polls of one flag (0: no waiting at all)
 };
 
 // Decode: one step for S streams x H heads.

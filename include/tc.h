@@ -78,8 +78,11 @@ typedef struct {
 
 /* Bytes of device workspace tc_forward / tc_backward need for `shape`
  * (0 if the shape is invalid).  The workspace holds the eviction-state
- * checkpoints of the scan and, for the backward, per-row and per-block
- * partial sums; its contents on entry are ignored. */
+ * checkpoints of the scan, for the forward one 64-bit flag per segment and,
+ * for the backward, per-row and per-block partial sums.  Its contents on
+ * entry are ignored: a forward call waits only for a flag value of its own
+ * (a per-process random salt combined with a call count), which stale
+ * contents do not hold. */
 size_t tc_forward_workspace_size(const tc_shape_t* shape);
 size_t tc_backward_workspace_size(const tc_shape_t* shape);
 
@@ -94,8 +97,13 @@ size_t tc_backward_workspace_size(const tc_shape_t* shape);
  *            decode continuing at position T starts from).
  *   lse      [B,H,T] float32, out, nullable: natural-log softmax normaliser
  *            of the scaled window scores (needed by tc_backward).
- *   ws       device workspace of at least tc_forward_workspace_size bytes.
- * Outputs must not overlap the inputs or each other.
+ *   ws       device workspace of at least tc_forward_workspace_size bytes;
+ *            calls that overlap in time must not share one.
+ * Outputs must not overlap the inputs or each other.  With one 128-row block
+ * per segment the workgroups of the launch hand segment states to each other
+ * through flags in the workspace; a wait is bounded (environment variable
+ * TC_FORWARD_MAX_POLLS, default 65536 polls) and one that runs out yields
+ * NaN in the affected rows instead of a stale state.
  */
 tc_status_t tc_forward(const tc_shape_t* shape, const void* q, const void* k, const void* v,
                        const float* lambda, const float* eta, const float* gate, void* y,

@@ -177,3 +177,65 @@ def test_forward_deterministic():
     for o in outs[1:]:
         for a, b in zip(o, outs[0]):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("D", [16, 32, 64])
+def test_forward_state_exchange(D):
+    """One block per segment: each workgroup publishes the local state of its
+    evicted chunk and later segments of the head sum the published states."""
+    say("forward state exchange", D)
+    d = tc_inputs.prefill_inputs(2, seed=31 + D, B=2, H=4, T=1024 + 37, D=D, W=200, dtype="bf16", plants=False)
+    err = run_and_compare(d, 200)
+    say("  errors", err)
+    for key, e in err.items():
+        assert e <= TOL["bf16"], (key, e)
+
+
+def test_forward_flag_wait_runs_out(monkeypatch):
+    """TC_FORWARD_MAX_POLLS=0 ends every flag wait at once: the kernel still
+    finishes, the blocks that needed earlier segments' states come back NaN
+    (never a stale state), and every other row matches the oracle."""
+    say("forward flag wait runs out")
+    monkeypatch.setenv("TC_FORWARD_MAX_POLLS", "0")
+    W, T = 200, 1024 + 37
+    d = tc_inputs.prefill_inputs(2, seed=33, B=2, H=4, T=T, D=64, W=W, dtype="bf16", plants=False)
+    q, k, v = (dev(d[x], "bf16") for x in ("q", "k", "v"))
+    lam, eta, g = (dev(d[x], "f32") for x in ("lam", "eta", "gate"))
+    y, A, _ = tc().tc_forward(q, k, v, lam, eta, g, W)
+    torch.cuda.synchronize()
+    y, A = host(y), host(A)
+    cut = (W // 128 + 1) * 128  # first row of the first block that sums earlier segments' states
+    assert np.isnan(y[:, :, cut:]).all() and np.isnan(A).all()
+    yo, _, _ = oracle.forward(d["q"], d["k"], d["v"], d["lam"], d["eta"], d["gate"], W)
+    e = rel(y[:, :, :cut], yo[:, :, :cut])
+    say("  error of the other rows", e)
+    assert e <= TOL["bf16"], e
+
+
+def test_forward_workspace_reuse():
+    """One workspace filled with arbitrary bytes, then reused by calls on
+    different inputs: flags left by a call (or by the initial contents) must
+    never be taken for those of a later call."""
+    say("forward workspace reuse")
+    T, W = 1024, 256
+    d1 = tc_inputs.prefill_inputs(2, seed=41, B=2, H=4, T=T, D=64, W=W, dtype="bf16", plants=False)
+    d2 = tc_inputs.prefill_inputs(2, seed=42, B=2, H=4, T=T, D=64, W=W, dtype="bf16", plants=False)
+    m = tc()
+    nbytes = m.tc_forward_workspace_size(m.make_shape(2, 4, T, 64, W, 64, 0.0, m.TC_BF16))
+    gen = torch.Generator().manual_seed(7)
+    ws = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=gen).to("cuda")
+    ref = {}
+    for i, d in enumerate((d1, d2, d1, d2)):
+        q, k, v = (dev(d[x], "bf16") for x in ("q", "k", "v"))
+        lam, eta, g = (dev(d[x], "f32") for x in ("lam", "eta", "gate"))
+        y, A, lse = m.tc_forward(q, k, v, lam, eta, g, W, ws=ws)
+        torch.cuda.synchronize()
+        y, A = host(y), host(A)
+        if i < 2:
+            yo, Ao, _ = oracle.forward(d["q"], d["k"], d["v"], d["lam"], d["eta"], d["gate"], W)
+            ey, eA = rel(y, yo), rel(A, Ao)
+            say("  call", i, "errors", ey, eA)
+            assert ey <= TOL["bf16"] and eA <= TOL["bf16"], (i, ey, eA)
+            ref[i] = (y, A)
+        else:
+            assert np.array_equal(y, ref[i - 2][0]) and np.array_equal(A, ref[i - 2][1]), i
