@@ -231,7 +231,9 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   };
   auto tile_of = [&](const Blk& b, int idx) { return idx < b.nfront ? b.ilo + idx : idx - b.nfront; };
   // cursor of the item held in the staging registers
-  int pj = jb, pidx = 0;
+  // (PUB: the Q block is loaded on its own at the start, so its loads and the
+  // first key tile's are in flight together; the item stream starts at the tiles)
+  int pj = jb, pidx = PUB ? NQ : 0;
   Blk pb = blk(jb);
   int kv_stored = 0;  // key/value items written to LDS so far (buffer parity)
   TileRegs<E, D, 64, NTH> kr, vr;
@@ -269,6 +271,8 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
     __syncthreads();
   };
 
+  TileRegs<E, D, BM, NTH> qr;
+  if (PUB) qr.load(Qg, jb * BM);
   load_next();  // the first item's loads overlap the state set-up below
 
   if (tid <= BM) pw[tid] = powi(a.lam[h], tid);
@@ -303,7 +307,12 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
     for (int x = tid; x < D * D; x += NTH) Sl[(x % D) * LDS + x / D] = g[x];
   }
 
-  step();
+  if (PUB) {
+    qr.store(Qs, LDK);
+    __syncthreads();
+  } else {
+    step();
+  }
 
   int kv_used = 0;  // key/value items consumed (buffer parity)
   const int rw = 32 * wid;  // first row of this wave within the block
@@ -318,7 +327,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
     const int R0 = t0 + rw;  // first query row of this wave
 
     // items 0 .. NQ-1: the Q block
-    for (int qi = 1; qi < NQ; ++qi) step();
+    for (int qi = 1; qi < NQ; ++qi) step();  // (NQ = 1 with PUB)
     frag qf[2][NKC];
     frag ones;
     {
