@@ -172,6 +172,22 @@ __device__ __forceinline__ void state_fill(State<E, D>& st, float x) {
     for (int at = 0; at < D / 16; ++at) st.s[o][at] = f32x4{x, x, x, x};
 }
 
+// st <- mult * st + (the state whose transpose is at Sl, S[a][c] at Sl[c * LDS + a])
+template <class E, int D, int LDS>
+__device__ __forceinline__ void state_scale_add_lds_t(State<E, D>& st, float mult, const float* Sl, int wid, int l16,
+                                                      int lg) {
+  constexpr int NT = D / 16;
+#pragma unroll
+  for (int o = 0; o < State<E, D>::NOWN; ++o) {
+    const int ct = wid + 4 * o;
+    if (ct < NT) {
+#pragma unroll
+      for (int at = 0; at < NT; ++at)
+        st.s[o][at] = mult * st.s[o][at] + *(const f32x4*)(Sl + (16 * ct + l16) * LDS + 16 * at + 4 * lg);
+    }
+  }
+}
+
 // S^T into LDS: S[a][c] at Sl[c * LDS + a]
 template <class E, int D, int LDS>
 __device__ __forceinline__ void state_to_lds_t(const State<E, D>& st, float* Sl, int wid, int l16, int lg) {

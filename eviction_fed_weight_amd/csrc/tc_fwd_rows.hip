@@ -548,6 +548,8 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
       }
     }
     if (PUB) {
+      State<E, D> acc;  // S(e0)
+      state_zero(acc);
       if (seg > m_lo) {
         // wait for the earlier segments' flags (bounded, so that every wave
         // ends; the workgroups waited for were dispatched earlier and wait for
@@ -559,23 +561,22 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
           seen = __hip_atomic_load(myflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.gen;
         }
         const bool ran_out = __syncthreads_or(!seen);
-        State<E, D> acc;
-        state_zero(acc);
         state_gather_all(acc, pw[BM], slots, m_lo + 1, seg + 1, wid, lane);
         if (ran_out) state_fill(acc, __builtin_nanf(""));
         state_to_lds_t<E, D, LDS>(acc, Sl, wid, l16, lg);
       }
-      __syncthreads();  // S(e0) (and L^T of the last block) in LDS for every wave
       if (last && a.A_final) {
-        // A after step T-1 = eta (lambda^n S(e0) + L), n = T - t0 evictions in this block
+        // A after step T-1 = eta (lambda^n S(e0) + L), n = T - t0 evictions in
+        // this block (L^T was written to the Q area by this wave's own threads)
         float* Af = a.A_final + (size_t)bh * D * D;
-        const float dn = pw[T - t0], eta = a.eta[h];
-        const float sm = seg > m_lo ? 1.0f : 0.0f;  // S(e0) = 0 when no earlier segment evicted
-        for (int x = tid; x < D * D; x += NTH) {
-          const int ar = x / D, cc = x % D;
-          Af[x] = fin ? eta * __builtin_fmaf(sm * dn, Sl[cc * LDS + ar], Lt[cc * LDS + ar]) : 0.0f;
+        if (fin) {
+          state_scale_add_lds_t<E, D, LDS>(acc, pw[T - t0], Lt, wid, l16, lg);
+          state_store(acc, Af, a.eta[h], wid, l16, lg);
+        } else {
+          for (int x = tid; x < D * D; x += NTH) Af[x] = 0.0f;  // no evictions
         }
       }
+      __syncthreads();  // S(e0) in LDS for every wave
     }
     if (has_mem && e0 > 0) {
       // O += sigma(g) eta lambda^(r+1) q S(e0), S^T read from LDS as hi/lo bf16
