@@ -712,7 +712,11 @@ static hipError_t launch_rows_impl(const FwdArgs& a0, hipStream_t s) {
   // workgroups exchange their local states through flags and no state pass
   // runs.  (The residency test is for speed only: a workgroup waits only for
   // workgroups dispatched before it, so the waits end in any case.)
-  a.publish = (a.G == 1 && a.nseg > 1 && a.prefix_direct && a.flags != nullptr &&
+  // Not under graph capture: a replayed launch repeats this call's flag value,
+  // so flags left by the previous replay would read as current.
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  const bool capturing = hipStreamIsCapturing(s, &capture) != hipSuccess || capture != hipStreamCaptureStatusNone;
+  a.publish = (a.G == 1 && a.nseg > 1 && a.prefix_direct && a.flags != nullptr && !capturing &&
                (long long)BH * a.nseg <= rows_resident_capacity<E, D, NW>())
                   ? 1
                   : 0;

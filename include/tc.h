@@ -103,7 +103,9 @@ size_t tc_backward_workspace_size(const tc_shape_t* shape);
  * per segment the workgroups of the launch hand segment states to each other
  * through flags in the workspace; a wait is bounded (environment variable
  * TC_FORWARD_MAX_POLLS, default 65536 polls) and one that runs out yields
- * NaN in the affected rows instead of a stale state.
+ * NaN in the affected rows instead of a stale state.  A call made while its
+ * stream is being captured into a HIP graph takes the path without flags
+ * (a separate state pass), so graph replays stay correct.
  */
 tc_status_t tc_forward(const tc_shape_t* shape, const void* q, const void* k, const void* v,
                        const float* lambda, const float* eta, const float* gate, void* y,

@@ -239,3 +239,49 @@ def test_forward_workspace_reuse():
             ref[i] = (y, A)
         else:
             assert np.array_equal(y, ref[i - 2][0]) and np.array_equal(A, ref[i - 2][1]), i
+
+
+def test_forward_graph_capture():
+    """tc_forward captured in a HIP graph and replayed on new inputs, with
+    eager calls between the replays: every replay and every eager call
+    matches the oracle.  (Under capture the launcher takes the path without
+    inter-workgroup flags: a replay repeats the captured flag value.)"""
+    say("forward graph capture")
+    B, H, T, D, W = 2, 4, 1024, 64, 256
+    ds = [tc_inputs.prefill_inputs(2, seed=51 + i, B=B, H=H, T=T, D=D, W=W, dtype="bf16", plants=False)
+          for i in range(3)]
+    m = tc()
+    q, k, v = (dev(ds[0][x], "bf16") for x in ("q", "k", "v"))
+    lam, eta, g = (dev(ds[0][x], "f32") for x in ("lam", "eta", "gate"))
+    ws = torch.empty(m.tc_forward_workspace_size(m.make_shape(B, H, T, D, W, 64, 0.0, m.TC_BF16)),
+                     dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(q)
+    A = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        m.tc_forward(q, k, v, lam, eta, g, W, y=y, A_final=A, lse=lse, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        m.tc_forward(q, k, v, lam, eta, g, W, y=y, A_final=A, lse=lse, ws=ws)
+    torch.cuda.synchronize()
+    for i in (1, 2, 0, 1):
+        d = ds[i]
+        for dst, x in ((q, "q"), (k, "k"), (v, "v")):
+            dst.copy_(dev(d[x], "bf16"))
+        for dst, x in ((lam, "lam"), (eta, "eta"), (g, "gate")):
+            dst.copy_(dev(d[x], "f32"))
+        graph.replay()
+        torch.cuda.synchronize()
+        yo, Ao, lo = oracle.forward(d["q"], d["k"], d["v"], d["lam"], d["eta"], d["gate"], W)
+        err = dict(y=rel(host(y), yo), A=rel(host(A), Ao), lse=rel(host(lse), lo))
+        say("  replay on inputs", i, err)
+        for key, e in err.items():
+            assert e <= TOL["bf16"], ("replay", i, key, e)
+        ye, Ae, _ = m.tc_forward(q, k, v, lam, eta, g, W, ws=ws)  # eager call on the same workspace
+        torch.cuda.synchronize()
+        ee = dict(y=rel(host(ye), yo), A=rel(host(Ae), Ao))
+        assert max(ee.values()) <= TOL["bf16"], ("eager", i, ee)
