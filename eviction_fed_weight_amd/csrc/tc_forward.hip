@@ -31,15 +31,24 @@ namespace tck {
 // are stored row-major; operands that contract down their rows are read with
 // transpose reads (ColFrag).  X (float rows x D) aliases the K/V tiles: it is
 // only live between the band loop and the store of the evicted chunk.
+//
+// bf16 with D = 128 keeps the D x D state in LDS as float S^T (row stride
+// LDSS, an odd number of 16-byte chunks: conflict-free 16-lane reads) instead
+// of in registers, which leaves the band loop without register spills; the
+// other instantiations keep it in MFMA accumulators (the float32 D = 128 state
+// would not fit in LDS beside the tiles).
 template <class E, int D>
 struct FwdLds {
+  static constexpr bool LS = std::is_same<E, bf16>::value && D == 128;  // state in LDS
   static constexpr int VE = 16 / sizeof(E);
   static constexpr int LDK = D + VE;  // row stride of K, V, Q tiles
   static constexpr int LDX = D + 4;
+  static constexpr int LDSS = D + 4;
   static constexpr int TILE = 64 * LDK * (int)sizeof(E);
   static constexpr int XB = 64 * LDX * 4;
-  static constexpr int U = (2 * TILE) > XB ? (2 * TILE) : XB;
-  static constexpr int TOTAL = U + TILE;  // + Q block
+  static constexpr int U = (LS || (2 * TILE) > XB) ? (2 * TILE) : XB;
+  static constexpr int SB = LS ? D * LDSS * 4 : 0;
+  static constexpr int TOTAL = U + TILE + SB;  // + Q block (+ S^T)
 };
 
 // ---------------------------------------------------------------------------
@@ -65,6 +74,9 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
   E* Vs = (E*)(smem + L::TILE);
   float* X = (float*)smem;
   E* Qs = (E*)(smem + L::U);
+  float* Sl = (float*)(smem + L::U + L::TILE);  // (LS only)
+  constexpr bool LS = L::LS;
+  constexpr int LDSS = L::LDSS;
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int bh = blockIdx.x / a.nseg, seg = blockIdx.x - bh * a.nseg;
@@ -81,10 +93,15 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
   if (tid <= 64) pw[tid] = powi(a.lam[h], tid);
 
   State<E, D> st;
-  if (seg == 0)
+  if (LS) {
+    // S^T at the segment start -> LDS (read by every wave after the band loop's barriers)
+    const float* g = a.seg_state + ((size_t)bh * a.nseg + seg) * D * D;
+    for (int x = tid; x < D * D; x += 256) Sl[(x % D) * LDSS + x / D] = seg == 0 ? 0.0f : g[x];
+  } else if (seg == 0) {
     state_zero(st);
-  else
+  } else {
     state_load(st, a.seg_state + ((size_t)bh * a.nseg + seg) * D * D, wid, l16, lg);
+  }
   vm_fence_loads();
 
   const int jb = seg * a.G;
@@ -201,7 +218,31 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
     const bool last = (j == a.nblk - 1);
     if (has_mem) {
       __syncthreads();  // every wave is done with the last band tile
-      if (e0 > 0) {
+      if (LS && e0 > 0) {
+        // O += sigma(g) eta lambda^(r+1) q S(e0), S^T read from LDS as hi/lo bf16
+        const float f = seta * pw[r + 1];
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) {
+          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int dc = 0; dc < NKC; ++dc) {
+            float sv[8];
+            const float* sp = Sl + (dt * 16 + l16) * LDSS + dc * 32 + lg * 8;
+            const f32x4 x0 = *(const f32x4*)sp;
+            const f32x4 x1 = *(const f32x4*)(sp + 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              sv[i] = x0[i];
+              sv[4 + i] = x1[i];
+            }
+            frag shi, slo;
+            M::split(sv, shi, slo);
+            acc = M::mma(shi, qf[dc], acc);
+            if (M::kSplit) acc = M::mma(slo, qf[dc], acc);
+          }
+          O[dt] += f * acc;
+        }
+      } else if (e0 > 0) {
         // (QS)^T for this wave's state columns and all 64 rows -> X[row][c]
 #pragma unroll
         for (int o = 0; o < NOWN; ++o) {
@@ -274,11 +315,15 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
         for (int dt = 0; dt < NT; ++dt)
           O[dt] = M::mma(ColFrag<E>::read(Vs + (p * 32 + lg * 8) * LDK + dt * 16, LDK, l16), pf, O[dt]);
       }
-      // carry the state to the next block (or to step T-1 for A_final)
-      if (more) {
-        state_update(st, Ks, L::LDK, Vs, L::LDK, pw, 64, e0, wid, l16, lg);
-      } else if (last && a.A_final) {
-        state_update(st, Ks, LDK, Vs, LDK, pw, T - t0, e0, wid, l16, lg);
+      // carry the state to the next block (or to step T-1 for A_final); with
+      // the state in LDS every wave has read it (the barrier after the chunk
+      // tiles were stored) before the owners of its column tiles update it
+      if (more || (last && a.A_final)) {
+        const int len = more ? 64 : T - t0;
+        if (LS)
+          lds_state_update_cols<E, D, LDSS>(Sl, Ks, LDK, Vs, LDK, pw, len, e0, wid, l16, lg);
+        else
+          state_update(st, Ks, LDK, Vs, LDK, pw, len, e0, wid, l16, lg);
       }
     }
     // ---- store y ----
@@ -288,10 +333,15 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
     }
     if (last && a.A_final) {
       float* Af = a.A_final + (size_t)bh * D * D;
-      if (has_mem)
+      if (LS) {
+        __syncthreads();  // the state update above is done
+        const float eta = a.eta[h];
+        for (int x = tid; x < D * D; x += 256) Af[x] = has_mem ? eta * Sl[(x % D) * LDSS + x / D] : 0.0f;
+      } else if (has_mem) {
         state_store(st, Af, a.eta[h], wid, l16, lg);
-      else
+      } else {
         for (int x = tid; x < D * D; x += 256) Af[x] = 0.0f;
+      }
     }
   }
 }

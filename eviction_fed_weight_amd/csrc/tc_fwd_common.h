@@ -188,6 +188,50 @@ __device__ __forceinline__ void state_scale_add_lds_t(State<E, D>& st, float mul
   }
 }
 
+// S <- lambda^len S + sum_{c<len, e0+c>=0} lambda^(len-1-c) K[c,:]^T V[c,:] on
+// an LDS copy of S (float S^T: S[a][c] at Sl[c * LDSS + a]) for a 64-row
+// chunk whose K and V are row-major in LDS; four waves, wave w updating the
+// column tiles w, w + 4, ... (no state registers outside the update).
+template <class E, int D, int LDSS>
+__device__ __forceinline__ void lds_state_update_cols(float* Sl, const E* Ks, int ldk, const E* Vs, int ldv,
+                                                      const float* pw, int len, int e0, int wid, int l16, int lg) {
+  using M = Mfma<E>;
+  using frag = typename M::frag;
+  constexpr int NT = D / 16;
+  const float decay = pw[len];
+  for (int ct = wid; ct < NT; ct += 4) {
+    f32x4 sc[NT];
+    float* col = Sl + (16 * ct + l16) * LDSS + 4 * lg;
+#pragma unroll
+    for (int at = 0; at < NT; ++at) sc[at] = decay * *(const f32x4*)(col + 16 * at);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      float wv[8];
+      {
+        float vv[8];
+        M::to_f32(ColFrag<E>::read(Vs + (kc * 32 + lg * 8) * ldv + ct * 16, ldv, l16), vv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = kc * 32 + lg * 8 + j;
+          // (branch-free: the LDS read is unconditional, at a clamped index)
+          const float w = ((c < len && e0 + c >= 0) ? 1.0f : 0.0f) * pw[max(len - 1 - c, 0)];
+          wv[j] = w * vv[j];
+        }
+      }
+      frag bhi, blo;
+      M::split(wv, bhi, blo);
+#pragma unroll
+      for (int at = 0; at < NT; ++at) {
+        const frag af = ColFrag<E>::read(Ks + (kc * 32 + lg * 8) * ldk + at * 16, ldk, l16);
+        sc[at] = M::mma(af, bhi, sc[at]);
+        if (M::kSplit) sc[at] = M::mma(af, blo, sc[at]);
+      }
+    }
+#pragma unroll
+    for (int at = 0; at < NT; ++at) *(f32x4*)(col + 16 * at) = sc[at];
+  }
+}
+
 // S^T into LDS: S[a][c] at Sl[c * LDS + a]
 template <class E, int D, int LDS>
 __device__ __forceinline__ void state_to_lds_t(const State<E, D>& st, float* Sl, int wid, int l16, int lg) {
