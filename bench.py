@@ -7,7 +7,7 @@ serving workload (64 streams x 32 heads, D=128, W=4096: tc_decode_step calls
 per second), the long-context prefill and the backward, each with its
 roofline, plus the CPU oracle timed on the host.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--legs prefill,decode,long,backward[,calib]]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--legs prefill,decode,long,backward,train_forward[,calib]]
 """
 from __future__ import annotations
 
@@ -60,7 +60,7 @@ def measured_traffic():
     if kv.get("csrc_sha256") != csrc_digest():
         return {}
     out = {}
-    for leg in ("prefill", "long", "decode", "backward"):
+    for leg in ("prefill", "long", "decode", "backward", "train_forward"):
         key = "%s_bytes_per_call" % leg
         if key in kv:
             out[leg] = float(kv[key])
@@ -114,7 +114,7 @@ def prefill_leg(cfg_id, steps, warmup):
     import tc_inputs
 
     cfg = tc_inputs.CONFIGS[cfg_id]
-    d = tc_inputs.prefill_inputs(cfg_id)
+    d = tc_inputs.prefill_inputs(cfg_id, with_dy=False) if cfg_id == 5 else tc_inputs.prefill_inputs(cfg_id)
     dv = torch.device("cuda")
     q, k, v = (torch.from_numpy(d[x]).to(dv).to(torch.bfloat16).contiguous() for x in ("q", "k", "v"))
     lam, eta, g = (torch.from_numpy(d[x]).to(dv) for x in ("lam", "eta", "gate"))
@@ -132,11 +132,15 @@ def prefill_leg(cfg_id, steps, warmup):
     by = fwd_bytes(cfg.B, cfg.H, cfg.T, cfg.D)
     tflops = fl / (ms * 1e-3) / 1e12
     return dict(
-        workload="prefill B=%d H=%d D=%d T=%d W=%d C=%d bf16" % (cfg.B, cfg.H, cfg.D, cfg.T, cfg.W, cfg.C),
+        workload="%s B=%d H=%d D=%d T=%d W=%d C=%d bf16" % ("forward" if cfg_id == 5 else "prefill", cfg.B, cfg.H, cfg.D,
+                                                           cfg.T, cfg.W, cfg.C),
         ms_per_call=ms, tokens_per_s=cfg.B * cfg.T / (ms * 1e-3), flops=fl, bytes=by,
         roofline=dict(bound="mfma", achieved=tflops, peak=PEAK_BF16, unit="TFLOP/s", frac=tflops / PEAK_BF16,
-                      traffic=measured_traffic().get("prefill" if cfg_id == 2 else "long"),
-                      kernel="one tc_forward call (fwd_kernel_rows; with several blocks per segment also seg_state_kernel [+ seg_chain_kernel])"),
+                      traffic=measured_traffic().get({2: "prefill", 3: "long", 5: "train_forward"}[cfg_id]),
+                      kernel=("one tc_forward call (fwd_kernel_rows; with several blocks per segment also "
+                              "seg_state_kernel [+ seg_chain_kernel])" if cfg.D <= 64 else
+                              "one tc_forward call (seg_state_kernel + seg_chain_kernel + fwd_kernel, D=128: 64-row "
+                              "blocks, state in LDS)")),
         hbm_gbs=by / (ms * 1e-3) / 1e9,
     )
 
@@ -272,7 +276,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--legs", default="prefill,decode,long,backward")
+    ap.add_argument("--legs", default="prefill,decode,long,backward,train_forward")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -317,6 +321,11 @@ def main():
         bw = backward_leg(max(3, args.steps // 5), 2)
         log("  backward", json.dumps(bw))
         out["backward"] = bw
+    if "train_forward" in legs:
+        log("training-shape forward leg ...")
+        tf = prefill_leg(5, max(3, args.steps // 5), 2)
+        log("  train_forward", json.dumps(tf))
+        out["train_forward"] = tf
     out["csrc_sha256"] = csrc_digest()
     if "calib" in legs:
         log("copy calibration leg ...")
