@@ -78,6 +78,17 @@ def test_workspace_sizes():
     assert tc.tc_forward_workspace_size(s2) >= 64 * 64 * 4
 
 
+def test_forward_workspace_layout():
+    """The forward workspace holds nseg + 1 float32 D x D state slots per (b,h)
+    (segment states, and the last segment's local state) followed by one
+    64-bit flag per segment, each part rounded up to 256 bytes.  B=8 H=8
+    T=1024 D=64 runs as eight one-block (128-row) segments per head."""
+    BH, nseg, D = 64, 8, 64
+    states = BH * (nseg + 1) * D * D * 4
+    flags = -(-BH * nseg * 8 // 256) * 256
+    assert tc.tc_forward_workspace_size(tc.make_shape(8, 8, 1024, 64, 256, 64)) == states + flags
+
+
 def test_decode_validation():
     L = tc.lib()
 
