@@ -1,6 +1,7 @@
 // C ABI of the TC layer: host-side validation, workspace planning and
 // dispatch to the gfx950 kernels.  No allocation and no synchronisation;
-// the only global state is a call counter (the forward's flag values).
+// the only global state is a call counter (the forward's flag values) and,
+// in the rows launcher, a per-device count of resident workgroups.
 #include <math.h>
 
 #include <atomic>
