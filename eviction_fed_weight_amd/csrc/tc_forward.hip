@@ -104,8 +104,8 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
   }
   vm_fence_loads();
 
-  const int jb = seg * a.G;
-  const int je = min(a.nblk, jb + a.G);
+  const int jb = seg_first_block(a, seg);
+  const int je = seg_first_block(a, seg + 1);
   const int r = wid * 16 + l16;  // this lane's row within the block
   TileRegs<E, D, 64> ql, kl, vl;
   ql.load(Qg, jb * 64);

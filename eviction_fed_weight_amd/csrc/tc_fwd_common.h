@@ -275,8 +275,9 @@ __device__ __forceinline__ void store4(bf16* dst, f32x4 x) {
 __device__ __forceinline__ void store4(float* dst, f32x4 x) { *(f32x4*)dst = x; }
 
 // ---------------------------------------------------------------------------
-// Segment states for a forward pass with BM query rows per block and G blocks
-// per segment (segment m holds the evictions e in [m G BM - W, (m+1) G BM - W)).
+// Segment states for a forward pass with BM query rows per block and G or
+// G + 1 blocks per segment (segment m holds blocks b_m .. b_{m+1} - 1, b_m =
+// seg_first_block, so its evictions are e in [b_m BM - W, b_{m+1} BM - W)).
 
 // Local states L_m = S over the evictions of segment m, from zero.
 // grid = BH * (nseg - 1); writes seg_state[bh][m + 1].  With final_slot the
@@ -304,8 +305,8 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
   State<E, D> st;
   state_zero(st);
   TileRegs<E, D, 64> kl, vl;
-  const int tb = m * a.G * BM;  // first row of segment m
-  const int ntile = a.G * (BM / 64);
+  const int tb = seg_first_block(a, m) * BM;  // first row of segment m
+  const int ntile = seg_blocks(a, m) * (BM / 64);
   const int ebase = tb - a.W;
   // evictions in tile t: 64, or in the last segment those of rows up to T-1
   auto tile_len = [&](int t) { return fin ? min(64, a.T - tb - 64 * t) : 64; };
@@ -332,7 +333,7 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
 }
 
 // Chain over segments, in place: seg_state[0] = 0 and
-// seg_state[m+1] = lambda^(G BM) seg_state[m] + L_m.
+// seg_state[m+1] = lambda^(BM blocks(m)) seg_state[m] + L_m.
 // grid = (D*D/4 + 255)/256 x BH; each thread owns four consecutive floats and
 // loads eight segments ahead of the dependent chain.
 template <int D, int BM>
@@ -340,7 +341,8 @@ __global__ void __launch_bounds__(256) seg_chain_kernel(FwdArgs a) {
   const int bh = blockIdx.y;
   const int x = blockIdx.x * 256 + threadIdx.x;
   if (x * 4 >= D * D) return;
-  const float decay = powi(a.lam[bh % a.H], BM * a.G);
+  // S_m = lambda^(BM blocks(m-1)) S_{m-1} + L_{m-1}
+  const float decay = powi(a.lam[bh % a.H], BM * a.G), decay1 = decay * powi(a.lam[bh % a.H], BM);
   float4* p = (float4*)(a.seg_state + (size_t)bh * a.nseg * D * D) + x;
   const size_t stride = (size_t)D * D / 4;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -353,10 +355,11 @@ __global__ void __launch_bounds__(256) seg_chain_kernel(FwdArgs a) {
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (m0 + u < a.nseg) {
-        s.x = decay * s.x + l[u].x;
-        s.y = decay * s.y + l[u].y;
-        s.z = decay * s.z + l[u].z;
-        s.w = decay * s.w + l[u].w;
+        const float dm = m0 + u - 1 < a.R ? decay1 : decay;
+        s.x = dm * s.x + l[u].x;
+        s.y = dm * s.y + l[u].y;
+        s.z = dm * s.z + l[u].z;
+        s.w = dm * s.w + l[u].w;
         p[(m0 + u) * stride] = s;
       }
   }

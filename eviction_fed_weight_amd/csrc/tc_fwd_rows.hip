@@ -186,8 +186,8 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   E* Yg = (E*)a.y + base;
   const float seta = sigmoidf(a.gate[h]) * a.eta[h];
   const float sl2 = a.scale * kLog2e;
-  const int jb = seg * a.G;
-  const int je = min(a.nblk, jb + a.G);
+  const int jb = seg_first_block(a, seg);
+  const int je = seg_first_block(a, seg + 1);
 
   // Item stream.  Block j contributes, in order: its Q block (NQ items of
   // 128 rows, each two 64-row halves written to the Q area), its window's key
@@ -284,18 +284,19 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
     for (int x = tid; x < D * D; x += NTH) Sl[(x % D) * LDS + x / D] = 0.0f;
   } else if (a.prefix_direct) {
     // S at the segment start from the local states L_m (stored at index m+1):
-    // S = sum_{m < seg} lambda^((seg-1-m) BM G) L_m, in chain order
+    // S_{m+1} = lambda^(BM blocks(m)) S_m + L_m, in chain order
     constexpr int PER = (D * D + NTH - 1) / NTH;
-    const float dec = powi(a.lam[h], BM * a.G);
+    const float dec = powi(a.lam[h], BM * a.G), dec1 = dec * powi(a.lam[h], BM);
     const float* g = a.seg_state + (size_t)bh * a.nseg * D * D;
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
 #pragma unroll 4
     for (int m = 1; m <= seg; ++m) {
+      const float dm = m - 1 < a.R ? dec1 : dec;
 #pragma unroll
       for (int k = 0; k < PER; ++k)
-        if ((D * D) % NTH == 0 || tid + NTH * k < D * D) acc[k] = dec * acc[k] + g[(size_t)m * D * D + tid + NTH * k];
+        if ((D * D) % NTH == 0 || tid + NTH * k < D * D) acc[k] = dm * acc[k] + g[(size_t)m * D * D + tid + NTH * k];
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
@@ -650,19 +651,20 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
     if (a.prefix_direct) {
-      const float dec = powi(a.lam[h], BM * a.G);
+      const float dec = powi(a.lam[h], BM * a.G), dec1 = dec * powi(a.lam[h], BM);
       for (int m = 1; m <= last_seg; ++m) {
+        const float dm = m - 1 < a.R ? dec1 : dec;
 #pragma unroll
         for (int k = 0; k < PER; ++k)
           if ((D * D) % NTH == 0 || tid + NTH * k < D * D)
-            acc[k] = dec * acc[k] + g[(size_t)m * D * D + tid + NTH * k];
+            acc[k] = dm * acc[k] + g[(size_t)m * D * D + tid + NTH * k];
       }
     } else {
 #pragma unroll
       for (int k = 0; k < PER; ++k)
         if ((D * D) % NTH == 0 || tid + NTH * k < D * D) acc[k] = g[(size_t)last_seg * D * D + tid + NTH * k];
     }
-    const float dn = powi(a.lam[h], T - last_seg * a.G * BM);
+    const float dn = powi(a.lam[h], T - seg_first_block(a, last_seg) * BM);
     const float eta = a.eta[h];
     float* Af = a.A_final + (size_t)bh * D * D;
 #pragma unroll
@@ -716,7 +718,7 @@ static hipError_t launch_rows_impl(const FwdArgs& a0, hipStream_t s) {
   // so flags left by the previous replay would read as current.
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   const bool capturing = hipStreamIsCapturing(s, &capture) != hipSuccess || capture != hipStreamCaptureStatusNone;
-  a.publish = (a.G == 1 && a.nseg > 1 && a.prefix_direct && a.flags != nullptr && !capturing &&
+  a.publish = (a.G == 1 && a.R == 0 && a.nseg > 1 && a.prefix_direct && a.flags != nullptr && !capturing &&
                (long long)BH * a.nseg <= rows_resident_capacity<E, D, NW>())
                   ? 1
                   : 0;

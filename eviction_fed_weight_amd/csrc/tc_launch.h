@@ -20,8 +20,9 @@ struct FwdArgs {
   float* seg_state;  // [B*H][nseg][D*D] segment-start states (eta factored out)
   int B, H, T, W;
   int nblk;  // ceil(T / block rows): 128 (bf16, D <= 64) or 64
-  int G;     // blocks per segment
-  int nseg;  // ceil(nblk / G)
+  int nseg;  // segments: the first R hold G + 1 blocks, the others G
+  int G;
+  int R;
   int prefix_direct;  // fused kernel combines the local segment states itself (no chain kernel)
   float scale;
   // Set by the rows launcher: the state pass also forms the local state of the
@@ -38,6 +39,11 @@ struct FwdArgs {
   unsigned long long gen;     // this call's flag value
   int max_polls;              // bound on the polls of one flag (0: no waiting at all)
 };
+
+// First block of forward segment s (s = nseg gives nblk).
+__host__ __device__ inline int seg_first_block(const FwdArgs& a, int s) { return s * a.G + (s < a.R ? s : a.R); }
+// Blocks of forward segment s.
+__host__ __device__ inline int seg_blocks(const FwdArgs& a, int s) { return a.G + (s < a.R ? 1 : 0); }
 
 // Decode: one step for S streams x H heads.
 struct DecArgs {
