@@ -7,7 +7,8 @@ serving workload (64 streams x 32 heads, D=128, W=4096: tc_decode_step calls
 per second), the long-context prefill and the backward, each with its
 roofline, plus the CPU oracle timed on the host.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--legs prefill,decode,long,backward,train_forward[,calib]]
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+                    [--legs prefill,decode,long,backward,train_forward,continue[,calib]]
 """
 from __future__ import annotations
 
@@ -145,6 +146,52 @@ def prefill_leg(cfg_id, steps, warmup):
     )
 
 
+def continue_leg(steps, warmup, chunk=4096):
+    """Chunked prefill of the long-context workload (B=1 H=12 D=64 T=32768
+    W=1024): the sequence in chunks of `chunk` tokens, each a
+    tc_forward_continue call from the ring and memory the previous one left.
+    One step = the whole sequence (T / chunk calls), timed from an empty state
+    each time."""
+    import torch
+
+    import eviction_fed_weight_amd as tc
+    import tc_inputs
+
+    cfg = tc_inputs.CONFIGS[3]
+    d = tc_inputs.prefill_inputs(3)
+    dv = torch.device("cuda")
+    q, k, v = (torch.from_numpy(d[x]).to(dv).to(torch.bfloat16).contiguous() for x in ("q", "k", "v"))
+    lam, eta, g = (torch.from_numpy(d[x]).to(dv) for x in ("lam", "eta", "gate"))
+    B, H, T, D, W = cfg.B, cfg.H, cfg.T, cfg.D, cfg.W
+    n = (T + chunk - 1) // chunk
+    parts = [tuple(x[:, :, i * chunk:(i + 1) * chunk].contiguous() for x in (q, k, v)) for i in range(n)]
+    ys = [torch.empty_like(p[0]) for p in parts]
+    lses = [torch.empty((B, H, p[0].shape[2]), dtype=torch.float32, device=dv) for p in parts]
+    kr = torch.zeros((B, H, W, D), dtype=torch.bfloat16, device=dv)
+    vr = torch.zeros_like(kr)
+    A = torch.zeros((B, H, D, D), dtype=torch.float32, device=dv)
+    pos = torch.zeros(B, dtype=torch.int64, device=dv)
+    shape = tc.make_shape(B, H, chunk, D, W, cfg.C)
+    ws = torch.empty(tc.tc_continue_workspace_size(shape, W), dtype=torch.uint8, device=dv)
+
+    def call():
+        A.zero_()
+        for i, (qi, ki, vi) in enumerate(parts):
+            tc.tc_forward_continue(qi, ki, vi, lam, eta, g, kr, vr, A, i * chunk, pos=pos, C=cfg.C,
+                                   y=ys[i], lse=lses[i], ws=ws)
+
+    ms = time_calls(call, steps, warmup)
+    fl = fwd_flops(B, H, T, D, W, cfg.C)
+    tflops = fl / (ms * 1e-3) / 1e12
+    return dict(workload="chunked prefill B=%d H=%d D=%d T=%d W=%d C=%d bf16 in %d chunks of %d"
+                % (B, H, D, T, W, cfg.C, n, chunk),
+                ms_per_sequence=ms, tokens_per_s=B * T / (ms * 1e-3), flops=fl,
+                roofline=dict(bound="mfma", achieved=tflops, peak=PEAK_BF16, unit="TFLOP/s", frac=tflops / PEAK_BF16,
+                              traffic=None,
+                              kernel="%d tc_forward_continue calls (gather + initial-state read + forward over "
+                                     "ring prefix and chunk + state/ring update)" % n))
+
+
 def decode_leg(steps, warmup):
     """Serving decode: 64 streams x 32 heads, D=128, W=4096.  The start state
     (ring of the last 4,096 pairs, A after 8,192 prior evictions) is built on
@@ -276,7 +323,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--legs", default="prefill,decode,long,backward,train_forward")
+    ap.add_argument("--legs", default="prefill,decode,long,backward,train_forward,continue")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -321,6 +368,11 @@ def main():
         bw = backward_leg(max(3, args.steps // 5), 2)
         log("  backward", json.dumps(bw))
         out["backward"] = bw
+    if "continue" in legs:
+        log("chunked prefill (continuation) leg ...")
+        cl = continue_leg(max(3, args.steps // 5), 2)
+        log("  continue", json.dumps(cl))
+        out["chunked_prefill"] = cl
     if "train_forward" in legs:
         log("training-shape forward leg ...")
         tf = prefill_leg(5, max(3, args.steps // 5), 2)

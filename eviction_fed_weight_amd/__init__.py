@@ -6,7 +6,8 @@ memory plumbing) and passes raw device pointers plus the current HIP stream.
 If the library has not been built it raises; there is no fallback.
 
 Entry points mirror the C names: ``tc_forward``, ``tc_decode_step``,
-``tc_backward``, ``tc_forward_workspace_size``, ``tc_backward_workspace_size``,
+``tc_forward_continue``, ``tc_backward``, ``tc_forward_workspace_size``,
+``tc_continue_workspace_size``, ``tc_backward_workspace_size``,
 ``tc_status_string``.
 """
 from __future__ import annotations
@@ -58,6 +59,10 @@ def lib() -> ctypes.CDLL:
         L.tc_forward.restype = ctypes.c_int
         L.tc_decode_step.argtypes = [ctypes.POINTER(DecodeShape)] + [_vp] * 12
         L.tc_decode_step.restype = ctypes.c_int
+        L.tc_continue_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.c_int64]
+        L.tc_continue_workspace_size.restype = _sz
+        L.tc_forward_continue.argtypes = [ctypes.POINTER(Shape), ctypes.c_int64] + [_vp] * 13 + [_sz, _vp]
+        L.tc_forward_continue.restype = ctypes.c_int
         L.tc_backward.argtypes = [ctypes.POINTER(Shape)] + [_vp] * 16 + [_sz, _vp]
         L.tc_backward.restype = ctypes.c_int
         L.tc_status_string.argtypes = [ctypes.c_int]
@@ -169,6 +174,36 @@ def tc_decode_step(q, k, v, k_ring, v_ring, A, pos, lam, eta, gate, scale: float
     if st != TC_OK:
         raise TCError(st, "tc_decode_step")
     return y
+
+
+def tc_continue_workspace_size(shape: Shape, pos0: int) -> int:
+    return int(lib().tc_continue_workspace_size(ctypes.byref(shape), int(pos0)))
+
+
+def tc_forward_continue(q, k, v, lam, eta, gate, k_ring, v_ring, A, pos0: int, *, pos=None, C: int = 64,
+                        scale: float = 0.0, want_lse: bool = True, y=None, lse=None, ws=None):
+    """The next T tokens of B sequences that have seen ``pos0`` tokens.
+    q, k, v: [B,H,T,D]; rings [B,H,W,D] and A [B,H,D,D] float32 are updated
+    in place (the decode layout with S = B); pos ([B] int64, optional) is set
+    to pos0 + T.  Returns (y, lse or None)."""
+    torch = _torch()
+    B, H, T, D = q.shape
+    W = k_ring.shape[2]
+    shape = make_shape(B, H, T, D, W, C, scale, _dtype_code(q))
+    dev = q.device
+    if y is None:
+        y = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(tc_continue_workspace_size(shape, pos0), dev, ws)
+    st = lib().tc_forward_continue(ctypes.byref(shape), int(pos0), _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
+                                   _ptr(eta), _ptr(gate), _ptr(k_ring), _ptr(v_ring), _ptr(A),
+                                   _ptr(pos) if pos is not None else None, _ptr(y),
+                                   _ptr(lse) if want_lse else None, _ptr(ws) if ws is not None else None,
+                                   wsb, _stream(dev))
+    if st != TC_OK:
+        raise TCError(st, "tc_forward_continue")
+    return y, (lse if want_lse else None)
 
 
 def tc_backward(q, k, v, y, dy, lse, lam, eta, gate, W: int, C: int = 64, scale: float = 0.0, *,

@@ -25,6 +25,7 @@ UNITS = [
     ("tc_forward.hip", "tc_forward", []),
     ("tc_fwd_rows.hip", "tc_fwd_rows", []),
     ("tc_decode.hip", "tc_decode", []),
+    ("tc_continue.hip", "tc_continue", []),
     # bf16 backward: matrix-core results kept in VGPRs (fewer scratch spills)
     ("tc_backward.hip", "tc_backward_bf16", ["-DTC_BWD_BF16=1", "-mllvm", "-amdgpu-mfma-vgpr-form"]),
     ("tc_backward.hip", "tc_backward_f32", ["-DTC_BWD_BF16=0"]),

@@ -122,6 +122,74 @@ tc_status_t check_shape(const tc_shape_t* s) {
 
 float scale_of(float scale, int D) { return scale > 0.0f ? scale : 1.0f / sqrtf((float)D); }
 
+// One forward launch over shape s (rows >= row0 stored, yadd added to them).
+tc_status_t launch_fwd(const tc_shape_t& s, const Plan& p, const void* q, const void* k, const void* v,
+                       const float* lambda, const float* eta, const float* gate, void* y, float* A_final,
+                       float* lse, void* ws, bool ws_ok, int row0, const float* yadd, hipStream_t stream) {
+  tck::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.lam = lambda;
+  a.eta = eta;
+  a.gate = gate;
+  a.y = y;
+  a.A_final = A_final;
+  a.lse = lse;
+  a.seg_state = (float*)ws;
+  a.flags = ws && ws_ok ? (unsigned long long*)((char*)ws + align256(p.state_bytes)) : nullptr;
+  a.gen = next_generation();
+  a.B = s.B;
+  a.H = s.H;
+  a.T = s.T;
+  a.W = s.W;
+  a.nblk = p.nblk;
+  a.G = p.G;
+  a.R = p.R;
+  a.nseg = p.nseg;
+  a.scale = scale_of(s.scale, s.D);
+  a.row0 = row0;
+  a.yadd = yadd;
+  const bool is_bf16 = s.dtype == TC_BF16;
+  const hipError_t e = fwd_block(s.D, s.dtype) == 128 ? tck::launch_forward_rows(a, s.D, is_bf16, stream)
+                                                       : tck::launch_forward(a, s.D, is_bf16, stream);
+  return e == hipSuccess ? TC_OK : TC_ERR_HIP;
+}
+
+// Continuation workspace: the forward's workspace for the extended shape,
+// the extended q/k/v, the initial-state read and the new evictions' state.
+struct ContPlan {
+  tc_shape_t x;  // extended shape (T = p + new tokens)
+  Plan fp;
+  int p;
+  size_t off_fwd, off_q, off_k, off_v, off_yinit, off_anew, total;
+};
+
+tc_status_t cont_plan_for(const tc_shape_t* s, int64_t pos0, ContPlan& c) {
+  const tc_status_t st = check_shape(s);
+  if (st != TC_OK) return st;
+  if (pos0 < 0) return TC_ERR_INVALID_ARGUMENT;
+  c.p = pos0 < s->W ? (int)pos0 : s->W;
+  c.x = *s;
+  if ((long long)s->T + c.p > (1LL << 30)) return TC_ERR_UNSUPPORTED;
+  c.x.T = s->T + c.p;
+  const tc_status_t sx = check_shape(&c.x);
+  if (sx != TC_OK) return sx;
+  const long long BH = (long long)s->B * s->H;
+  if (BH * ((s->T + 15) / 16) > (1LL << 31) - 1) return TC_ERR_UNSUPPORTED;
+  c.fp = plan_for(c.x);
+  const size_t es = elem_size(s->dtype);
+  const size_t nx = align256((size_t)BH * c.x.T * s->D * es);
+  c.off_fwd = 0;
+  c.off_q = align256(c.fp.state_bytes) + fwd_flags_bytes(c.x, c.fp);
+  c.off_k = c.off_q + nx;
+  c.off_v = c.off_k + nx;
+  c.off_yinit = c.off_v + nx;
+  c.off_anew = c.off_yinit + align256((size_t)BH * s->T * s->D * 4);
+  c.total = c.off_anew + align256((size_t)BH * s->D * s->D * 4);
+  return TC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -174,31 +242,77 @@ tc_status_t tc_forward(const tc_shape_t* s, const void* q, const void* k, const 
     for (int i = 0; i < 6; ++i)
       if (overlap(ws, need, ins[i], insz[i])) return TC_ERR_INVALID_ARGUMENT;
   }
-  tck::FwdArgs a{};
+  return launch_fwd(*s, p, q, k, v, lambda, eta, gate, y, A_final, lse, ws, ws_bytes >= need, 0, nullptr,
+                    (hipStream_t)stream);
+}
+
+size_t tc_continue_workspace_size(const tc_shape_t* s, int64_t pos0) {
+  ContPlan c;
+  if (cont_plan_for(s, pos0, c) != TC_OK) return 0;
+  return c.total;
+}
+
+tc_status_t tc_forward_continue(const tc_shape_t* s, int64_t pos0, const void* q, const void* k, const void* v,
+                                const float* lambda, const float* eta, const float* gate, void* k_ring,
+                                void* v_ring, float* A, int64_t* pos, void* y, float* lse, void* ws,
+                                size_t ws_bytes, void* stream) {
+  ContPlan c;
+  const tc_status_t st = cont_plan_for(s, pos0, c);
+  if (st != TC_OK) return st;
+  if (!q || !k || !v || !lambda || !eta || !gate || !k_ring || !v_ring || !A || !y)
+    return TC_ERR_INVALID_ARGUMENT;
+  const void* al[9] = {q, k, v, k_ring, v_ring, A, y, lse, ws};
+  for (int i = 0; i < 9; ++i)
+    if ((uintptr_t)al[i] % 16) return TC_ERR_INVALID_ARGUMENT;  // 16-byte vector copies
+  if (!ws || ws_bytes < c.total) return TC_ERR_WORKSPACE;
+  const size_t es = elem_size(s->dtype);
+  const size_t n = (size_t)s->B * s->H * s->T * s->D * es;
+  const size_t nr = (size_t)s->B * s->H * s->W * s->D * es;
+  const size_t na = (size_t)s->B * s->H * s->D * s->D * 4;
+  const size_t np = pos ? (size_t)s->B * 8 : 0;
+  const size_t nl = lse ? (size_t)s->B * s->H * s->T * 4 : 0;
+  const size_t nh = (size_t)s->H * 4;
+  const void* ins[6] = {q, k, v, lambda, eta, gate};
+  const size_t insz[6] = {n, n, n, nh, nh, nh};
+  void* outs[7] = {k_ring, v_ring, A, pos, y, lse, ws};
+  const size_t outsz[7] = {nr, nr, na, np, n, nl, c.total};
+  for (int o = 0; o < 7; ++o) {
+    for (int i = 0; i < 6; ++i)
+      if (overlap(outs[o], outsz[o], ins[i], insz[i])) return TC_ERR_INVALID_ARGUMENT;
+    for (int p = o + 1; p < 7; ++p)
+      if (overlap(outs[o], outsz[o], outs[p], outsz[p])) return TC_ERR_INVALID_ARGUMENT;
+  }
+  char* w = (char*)ws;
+  tck::ContArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
+  a.k_ring = k_ring;
+  a.v_ring = v_ring;
+  a.A = A;
+  a.pos = pos;
   a.lam = lambda;
-  a.eta = eta;
   a.gate = gate;
-  a.y = y;
-  a.A_final = A_final;
-  a.lse = lse;
-  a.seg_state = (float*)ws;
-  a.flags = ws && ws_bytes >= need ? (unsigned long long*)((char*)ws + align256(p.state_bytes)) : nullptr;
-  a.gen = next_generation();
+  a.qx = w + c.off_q;
+  a.kx = w + c.off_k;
+  a.vx = w + c.off_v;
+  a.yinit = (float*)(w + c.off_yinit);
+  a.A_new = (const float*)(w + c.off_anew);
+  a.pos0 = pos0;
   a.B = s->B;
   a.H = s->H;
   a.T = s->T;
   a.W = s->W;
-  a.nblk = p.nblk;
-  a.G = p.G;
-  a.R = p.R;
-  a.nseg = p.nseg;
-  a.scale = scale_of(s->scale, s->D);
-  const bool is_bf16 = s->dtype == TC_BF16;
-  const hipError_t e = fwd_block(s->D, s->dtype) == 128 ? tck::launch_forward_rows(a, s->D, is_bf16, (hipStream_t)stream)
-                                              : tck::launch_forward(a, s->D, is_bf16, (hipStream_t)stream);
+  a.D = s->D;
+  a.p = c.p;
+  a.Tx = c.x.T;
+  a.esize = (int)es;
+  hipError_t e = tck::launch_continue_prep(a, (hipStream_t)stream);
+  if (e != hipSuccess) return TC_ERR_HIP;
+  if (launch_fwd(c.x, c.fp, a.qx, a.kx, a.vx, lambda, eta, gate, y, (float*)(w + c.off_anew), lse,
+                 w + c.off_fwd, true, c.p, a.yinit, (hipStream_t)stream) != TC_OK)
+    return TC_ERR_HIP;
+  e = tck::launch_continue_finish(a, (hipStream_t)stream);
   return e == hipSuccess ? TC_OK : TC_ERR_HIP;
 }
 

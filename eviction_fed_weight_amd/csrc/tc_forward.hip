@@ -87,7 +87,8 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
   const auto Qg = make_rsrc((const E*)a.q + base, nbytes);
   const auto Kg = make_rsrc((const E*)a.k + base, nbytes);
   const auto Vg = make_rsrc((const E*)a.v + base, nbytes);
-  E* Yg = (E*)a.y + base;
+  const int Tout = T - a.row0;  // stored rows
+  E* Yg = (E*)a.y + (size_t)bh * Tout * D;
   const float seta = sigmoidf(a.gate[h]) * a.eta[h];
   const float sl2 = a.scale * kLog2e;
   if (tid <= 64) pw[tid] = powi(a.lam[h], tid);
@@ -211,7 +212,8 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
       const float inv = 1.0f / lrow;
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt) O[dt] *= inv;
-      if (a.lse && lg == 0 && trow < T) a.lse[(size_t)bh * T + trow] = (mrow + __log2f(lrow)) * kLn2;
+      if (a.lse && lg == 0 && trow >= a.row0 && trow < T)
+        a.lse[(size_t)bh * Tout + trow - a.row0] = (mrow + __log2f(lrow)) * kLn2;
     }
 
     // ---- L2: read of the eviction state and the evicted chunk ----
@@ -327,9 +329,14 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
       }
     }
     // ---- store y ----
-    if (trow < T) {
+    if (trow >= a.row0 && trow < T) {
+      const size_t o = (size_t)(trow - a.row0) * D + lg * 4;
+      if (a.yadd) {
 #pragma unroll
-      for (int dt = 0; dt < NT; ++dt) store4(Yg + (size_t)trow * D + dt * 16 + lg * 4, O[dt]);
+        for (int dt = 0; dt < NT; ++dt) O[dt] += *(const f32x4*)(a.yadd + (size_t)bh * Tout * D + o + dt * 16);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) store4(Yg + o + dt * 16, O[dt]);
     }
     if (last && a.A_final) {
       float* Af = a.A_final + (size_t)bh * D * D;

@@ -183,7 +183,8 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   const auto Qg = make_rsrc((const E*)a.q + base, nbytes);
   const auto Kg = make_rsrc((const E*)a.k + base, nbytes);
   const auto Vg = make_rsrc((const E*)a.v + base, nbytes);
-  E* Yg = (E*)a.y + base;
+  const int Tout = T - a.row0;  // stored rows
+  E* Yg = (E*)a.y + (size_t)bh * Tout * D;
   const float seta = sigmoidf(a.gate[h]) * a.eta[h];
   const float sl2 = a.scale * kLog2e;
   const int jb = seg_first_block(a, seg);
@@ -505,7 +506,8 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt) O[g][dt] *= inv;
       const int trow = R0 + 16 * g + l16;
-      if (a.lse && lg == 0 && trow < T) a.lse[(size_t)bh * T + trow] = (mrow[g] + __log2f(l)) * kLn2;
+      if (a.lse && lg == 0 && trow >= a.row0 && trow < T)
+        a.lse[(size_t)bh * Tout + trow - a.row0] = (mrow[g] + __log2f(l)) * kLn2;
     }
     auto chunk_tile = [&](int c, const E*& Kc, const E*& Vc) {
       const int ub = kv_used - cb.nlate + c;  // kv index of chunk tile c (tiles 0, 1 were the last nlate items)
@@ -628,9 +630,14 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const int trow = R0 + 16 * g + l16;
-      if (trow < T) {
+      if (trow >= a.row0 && trow < T) {
+        const size_t o = (size_t)(trow - a.row0) * D + lg * 4;
+        if (a.yadd) {
 #pragma unroll
-        for (int dt = 0; dt < NT; ++dt) store4(Yg + (size_t)trow * D + dt * 16 + lg * 4, O[g][dt]);
+          for (int dt = 0; dt < NT; ++dt) O[g][dt] += *(const f32x4*)(a.yadd + (size_t)bh * Tout * D + o + dt * 16);
+        }
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt) store4(Yg + o + dt * 16, O[g][dt]);
       }
     }
     if (!PUB && last && a.A_final && !a.final_slot) {

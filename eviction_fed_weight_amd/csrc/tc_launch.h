@@ -38,6 +38,12 @@ struct FwdArgs {
   unsigned long long* flags;  // [B*H][nseg], in the workspace after the states
   unsigned long long gen;     // this call's flag value
   int max_polls;              // bound on the polls of one flag (0: no waiting at all)
+  // Output rows: query rows t >= row0 are stored at row t - row0 of y and lse
+  // ([B,H,T-row0,...]); rows below row0 (a continuation's re-read prefix) are
+  // computed but not stored.  yadd (nullable, float [B,H,T-row0,D]) is added
+  // to each stored row before rounding.  tc_forward: row0 = 0, yadd = null.
+  int row0;
+  const float* yadd;
 };
 
 // First block of forward segment s (s = nseg gives nblk).
@@ -88,6 +94,32 @@ struct BwdArgs {
   int nblk, G, nseg;
   float scale;
 };
+
+// Continuation of a sequence (T new tokens after pos0 seen ones) through an
+// extended sequence in the workspace: the ring's p = min(pos0, W) tokens in
+// time order, then the new tokens (Tx = p + T rows).
+struct ContArgs {
+  const void* q;  // [B,H,T,D] new tokens
+  const void* k;
+  const void* v;
+  void* k_ring;   // [B,H,W,D] slot = position mod W
+  void* v_ring;
+  float* A;       // [B,H,D,D] memory after step pos0-1 (in), after pos0+T-1 (out)
+  int64_t* pos;   // [B] nullable: set to pos0 + T
+  const float* lam;
+  const float* gate;
+  void* qx;       // [B,H,Tx,D] extended sequence (workspace)
+  void* kx;
+  void* vx;
+  float* yinit;   // [B,H,T,D] sigmoid(g) lambda^n_t q_t A_in (workspace)
+  const float* A_new;  // [B,H,D,D] memory of this call's evictions alone (workspace)
+  long long pos0;
+  int B, H, T, W, D, p, Tx;
+  int esize;      // bytes per element of q/k/v and the rings
+};
+
+hipError_t launch_continue_prep(const ContArgs& a, hipStream_t s);    // extended sequence + initial-state read
+hipError_t launch_continue_finish(const ContArgs& a, hipStream_t s);  // A, ring and pos updates
 
 hipError_t launch_forward(const FwdArgs& a, int D, bool is_bf16, hipStream_t s);     // 64-row blocks: float32, and bf16 with D = 128
 hipError_t launch_forward_rows(const FwdArgs& a, int D, bool is_bf16, hipStream_t s);  // 128-row blocks: bf16 with D <= 64

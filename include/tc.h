@@ -133,6 +133,41 @@ tc_status_t tc_decode_step(const tc_decode_shape_t* shape, const void* q, const 
                            void* stream);
 
 /*
+ * tc_forward_continue -- chunked prefill after earlier tokens, and the
+ * prefill -> decode handoff (Figure 2: a stream's layer state is the ring of
+ * its last W pairs and the memory A; Section 3.2 write-on-evict).  The batch
+ * has seen pos0 tokens per sequence (a host value, the same for all B);
+ * this call takes the next T tokens, positions pos0 .. pos0+T-1, and gives
+ * exactly what T successive tc_decode_step calls give (up to float
+ * rounding), computed with the parallel forward.  With pos0 = 0 the outputs
+ * equal tc_forward's, and the ring/A it leaves are the state a decode at
+ * position T continues from.
+ *   shape    B, H, T (new tokens), D, W, C, scale, dtype as for tc_forward.
+ *   q, k, v  [B,H,T,D] dtype: the new tokens.
+ *   k_ring, v_ring [B,H,W,D] dtype, in/out: token t in slot t mod W (the
+ *            tc_decode_step layout with S = B).  On entry the slots of the
+ *            last min(pos0, W) tokens are read; on return they hold the last
+ *            min(pos0 + T, W) tokens (other slots are left as they are).
+ *   A        [B,H,D,D] float32, in/out: the memory after step pos0-1 on
+ *            entry (zero for pos0 <= W: nothing was evicted), after step
+ *            pos0+T-1 on return.
+ *   pos      [B] int64, out, nullable: set to pos0 + T (the decode position).
+ *   y        [B,H,T,D] dtype, out.   lse [B,H,T] float32, out, nullable.
+ *   ws       device workspace of at least tc_continue_workspace_size(shape,
+ *            pos0) bytes (it holds the ring prefix and the new tokens as one
+ *            extended sequence of min(pos0, W) + T rows).
+ * Every pointer must be 16-byte aligned.  Outputs (rings, A, pos, y, lse,
+ * ws) must not overlap the inputs or each other.  The extended sequence is
+ * subject to the tc_forward size limits (TC_ERR_UNSUPPORTED otherwise).
+ */
+size_t tc_continue_workspace_size(const tc_shape_t* shape, int64_t pos0);
+tc_status_t tc_forward_continue(const tc_shape_t* shape, int64_t pos0, const void* q, const void* k,
+                                const void* v, const float* lambda, const float* eta,
+                                const float* gate, void* k_ring, void* v_ring, float* A,
+                                int64_t* pos, void* y, float* lse, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/*
  * tc_backward -- gradients of L = sum_t <dy_t, y_t> through both levels and
  * the scan (the abstract: decay, write rate and gate are trained end to end).
  *   q, k, v, y, dy [B,H,T,D] dtype: forward inputs, forward output, upstream

@@ -114,6 +114,22 @@ def decode_step(q, k, v, k_ring, v_ring, A, pos, lam, eta, gate, scale: float | 
     return y
 
 
+def forward_continue(q, k, v, k_ring, v_ring, A, pos0: int, lam, eta, gate,
+                     scale: float | None = None):
+    """T tokens of B sequences after ``pos0`` seen ones, by definition: T
+    successive streaming steps (Figure 2), each one ``decode_step`` of the B
+    sequences as streams.  q,k,v: [B,H,T,D]; rings [B,H,W,D] and A [B,H,D,D]
+    (float64) are updated IN PLACE.  Returns y [B,H,T,D]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, T, D = q.shape
+    pos = np.full(B, int(pos0), np.int64)
+    y = np.empty_like(q)
+    for t in range(T):
+        y[:, :, t] = decode_step(q[:, :, t], k[:, :, t], v[:, :, t], k_ring, v_ring, A, pos,
+                                 lam, eta, gate, scale)
+    return y
+
+
 def backward(q, k, v, dy, lam, eta, gate, W: int, scale: float | None = None):
     """Gradients of L = sum <dy, y>.  Returns dq, dk, dv [B,H,T,D] and
     dlam, deta, dgate [H] (summed over the batch)."""

@@ -108,6 +108,38 @@ def test_decode_validation():
     assert call(tc.DecodeShape(1, 1, 64, 8, 0.0, 1), A=FAKE + 0x100000 + 64) == tc.TC_ERR_INVALID_ARGUMENT
 
 
+def test_continue_validation():
+    L = tc.lib()
+    G = 1 << 32  # spacing so the fake buffers do not overlap
+
+    def call(shape, pos0=300, **kw):
+        p = dict(q=G, k=2 * G, v=3 * G, lam=4 * G, eta=4 * G + 256, gate=4 * G + 512, kr=5 * G, vr=6 * G,
+                 A=7 * G, pos=8 * G, y=9 * G, lse=10 * G, ws=11 * G,
+                 wsb=tc.tc_continue_workspace_size(shape, pos0))
+        p.update(kw)
+        return L.tc_forward_continue(ctypes.byref(shape), pos0, p["q"], p["k"], p["v"], p["lam"], p["eta"],
+                                     p["gate"], p["kr"], p["vr"], p["A"], p["pos"], p["y"], p["lse"], p["ws"],
+                                     p["wsb"], None)
+
+    s = tc.make_shape(2, 4, 512, 64, 256, 64)
+    assert tc.tc_continue_workspace_size(s, -1) == 0
+    assert tc.tc_continue_workspace_size(tc.make_shape(1, 1, 64, 48, 8, 8), 0) == 0
+    # the workspace grows with the ring prefix min(pos0, W) that joins the new tokens
+    assert tc.tc_continue_workspace_size(s, 0) < tc.tc_continue_workspace_size(s, 100) \
+        < tc.tc_continue_workspace_size(s, 256) == tc.tc_continue_workspace_size(s, 10 ** 12)
+    assert call(s, pos0=-1) == tc.TC_ERR_INVALID_ARGUMENT
+    assert call(tc.make_shape(2, 4, 512, 48, 256, 64)) == tc.TC_ERR_UNSUPPORTED
+    for name in ("q", "kr", "vr", "A", "y", "gate"):
+        assert call(s, **{name: None}) == tc.TC_ERR_INVALID_ARGUMENT, name
+    assert call(s, ws=None) == tc.TC_ERR_WORKSPACE
+    assert call(s, wsb=tc.tc_continue_workspace_size(s, 300) - 1) == tc.TC_ERR_WORKSPACE
+    assert call(s, y=G + 8) == tc.TC_ERR_INVALID_ARGUMENT           # misaligned
+    assert call(s, kr=2 * G) == tc.TC_ERR_INVALID_ARGUMENT          # ring aliases the input keys
+    assert call(s, A=6 * G + 4096) == tc.TC_ERR_INVALID_ARGUMENT    # memory inside the value ring
+    assert call(s, ws=9 * G + 256) == tc.TC_ERR_INVALID_ARGUMENT    # workspace overlaps y
+    assert call(s, pos=10 * G) == tc.TC_ERR_INVALID_ARGUMENT        # pos inside lse
+
+
 def test_backward_validation():
     L = tc.lib()
     s = tc.make_shape(1, 1, 64, 48, 8, 8)

@@ -311,6 +311,28 @@ def test_decode_steps_reproduce_forward():
         np.testing.assert_allclose(yt, y[:, :, t], rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("cuts", [(0, 23), (0, 3, 23), (0, 5, 6, 17, 23), (0, 11, 12, 23)])
+def test_continuation_in_chunks_reproduces_forward(cuts):
+    """Chunked continuation (each chunk T successive streaming steps from the
+    ring and memory the previous chunk left) equals one forward over the
+    whole sequence, whatever the chunk boundaries (before, at and after the
+    first eviction at t = W)."""
+    B, H, D, W, T = 2, 3, 4, 5, 23
+    rng = np.random.default_rng(12)
+    q, k, v = (rng.standard_normal((B, H, T, D)) for _ in range(3))
+    lam, eta, g = np.array([0.5, 0.9, 0.99]), np.array([0.2, 0.5, 0.9]), np.array([0.3, -0.2, 1.0])
+    y, A, _ = oracle.forward(q, k, v, lam, eta, g, W)
+    kr, vr, Ad = np.zeros((B, H, W, D)), np.zeros((B, H, W, D)), np.zeros((B, H, D, D))
+    parts = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        parts.append(oracle.forward_continue(q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], kr, vr, Ad, a,
+                                             lam, eta, g))
+    np.testing.assert_allclose(np.concatenate(parts, axis=2), y, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(Ad, A, rtol=1e-12, atol=1e-13)
+    for t in range(T - W, T):  # the ring holds the last W pairs at slot t mod W
+        assert np.array_equal(kr[:, :, t % W], k[:, :, t]) and np.array_equal(vr[:, :, t % W], v[:, :, t])
+
+
 def test_state_after_writes_matches_recurrence():
     rng = np.random.default_rng(10)
     n, D = 40, 6
