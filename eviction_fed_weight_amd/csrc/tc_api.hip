@@ -36,7 +36,7 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 struct Plan {
-  int nblk, G, R, nseg;  // segments: the first R of G + 1 blocks, the others of G
+  int nblk, j0, G, R, nseg;  // segments of blocks j0..nblk-1: the first R of G + 1 blocks, the others of G
   size_t state_bytes;  // one [BH][nseg][D*D] float block
 };
 
@@ -58,30 +58,35 @@ long long fwd_slots(int D, int32_t dtype) {
 // follows the blocks of both, and the renumbering of the rows kernel pairs the
 // longer early segments with shorter late ones (B=1 H=12 T=32768: 42 segments
 // of 6 or 7 blocks instead of 37 of 7, the busiest unit 13 blocks instead of 14).
-Plan plan_for(const tc_shape_t& s) {
+//
+// Blocks j0 .. nblk-1 are processed: with row0 > 0 (a continuation's ring
+// prefix, never stored) whole blocks below row0 are skipped.
+Plan plan_for(const tc_shape_t& s, int row0 = 0) {
   Plan p;
   const long long BH = (long long)s.B * s.H;
   const long long slots = fwd_slots(s.D, s.dtype);
   const int bm = fwd_block(s.D, s.dtype);
   p.nblk = (s.T + bm - 1) / bm;
+  p.j0 = row0 / bm;
+  const int nb = p.nblk - p.j0;  // blocks to process
   long long best = -1;
   int bestG = 1;
-  for (int G = 1; G <= p.nblk; ++G) {
-    const long long nseg = (p.nblk + G - 1) / G;
-    if (G > 1 && (p.nblk + G - 2) / (G - 1) == nseg) continue;  // same split as G - 1, more work per segment
+  for (int G = 1; G <= nb; ++G) {
+    const long long nseg = (nb + G - 1) / G;
+    if (G > 1 && (nb + G - 2) / (G - 1) == nseg) continue;  // same split as G - 1, more work per segment
     const long long cost = ((BH * nseg + slots - 1) / slots) * (2 * G + 1) * 100 + nseg;
     if (best < 0 || cost <= best) {
       best = cost;
       bestG = G;
     }
   }
-  p.nseg = (p.nblk + bestG - 1) / bestG;
+  p.nseg = (nb + bestG - 1) / bestG;
   if (BH * p.nseg <= slots) {
-    const long long fill = slots / BH < p.nblk ? slots / BH : p.nblk;
+    const long long fill = slots / BH < nb ? slots / BH : nb;
     if (fill > p.nseg) p.nseg = (int)fill;
   }
-  p.G = p.nblk / p.nseg;
-  p.R = p.nblk - p.G * p.nseg;
+  p.G = nb / p.nseg;
+  p.R = nb - p.G * p.nseg;
   // segment states, then one last-block local state per (b,h)
   p.state_bytes = (size_t)BH * (p.nseg + 1) * s.D * s.D * sizeof(float);
   return p;
@@ -144,6 +149,7 @@ tc_status_t launch_fwd(const tc_shape_t& s, const Plan& p, const void* q, const 
   a.T = s.T;
   a.W = s.W;
   a.nblk = p.nblk;
+  a.j0 = p.j0;
   a.G = p.G;
   a.R = p.R;
   a.nseg = p.nseg;
@@ -176,8 +182,8 @@ tc_status_t cont_plan_for(const tc_shape_t* s, int64_t pos0, ContPlan& c) {
   const tc_status_t sx = check_shape(&c.x);
   if (sx != TC_OK) return sx;
   const long long BH = (long long)s->B * s->H;
-  if (BH * ((s->T + 15) / 16) > (1LL << 31) - 1) return TC_ERR_UNSUPPORTED;
-  c.fp = plan_for(c.x);
+  if (BH * ((s->T + 127) / 128) > (1LL << 31) - 1) return TC_ERR_UNSUPPORTED;
+  c.fp = plan_for(c.x, c.p);
   const size_t es = elem_size(s->dtype);
   const size_t nx = align256((size_t)BH * c.x.T * s->D * es);
   c.off_fwd = 0;

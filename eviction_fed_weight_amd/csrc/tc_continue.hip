@@ -29,10 +29,10 @@ namespace tck {
 // Extended sequence rows, one 16-byte vector per thread: row r < p is ring
 // slot (pos0 - p + r) mod W (its query row is zero: never stored), row
 // r >= p is new token r - p.
-__global__ void __launch_bounds__(256) cont_gather_kernel(ContArgs a) {
+__device__ __forceinline__ void cont_gather(const ContArgs& a, long long blk, long long nblk) {
   const int nv = a.D * a.esize / 16;  // vectors per row
   const long long total = (long long)a.B * a.H * a.Tx * nv;
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
+  for (long long i = blk * 256 + threadIdx.x; i < total; i += nblk * 256) {
     const long long row = i / nv;
     const int c = (int)(i - row * nv);
     const long long bh = row / a.Tx;
@@ -56,62 +56,101 @@ __global__ void __launch_bounds__(256) cont_gather_kernel(ContArgs a) {
   }
 }
 
-// yinit[b,h,t,:] = sigmoid(g_h) lambda_h^n_t q_t A_in[b,h] in float32.
-// One workgroup per (b,h) and 16 rows; A_in and the rows staged in LDS.
+// yinit[b,h,t,:] = sigmoid(g_h) lambda_h^n_t q_t A_in[b,h] in float32, on
+// the matrix cores.  One workgroup (four waves) per (b,h) and 128 rows; A_in
+// is staged transposed in LDS (bf16 inputs: as hi/lo bf16 pairs, keeping
+// ~2^-17 of its float32 precision; float32 inputs: as float32).  Computed
+// transposed, Y^T = A_in^T q^T, so a lane holds one query row: its q
+// fragment is 8 consecutive elements of that row and its result 4
+// consecutive outputs.
 template <class E, int D>
-__global__ void __launch_bounds__(256) cont_init_read_kernel(ContArgs a) {
-  constexpr int ROWS = 16;
-  __shared__ float As[D * D];
-  __shared__ float Qs[ROWS][D];
+__device__ __forceinline__ void cont_init_read(const ContArgs& a, int blk) {
+  using M = Mfma<E>;
+  using frag = typename M::frag;
+  constexpr int ROWS = 128, NT = D / 16, NKC = (D + 31) / 32;
+  constexpr int LDA = D + 16 / (int)sizeof(E);  // row stride of A_in^T in LDS (elements)
+  constexpr int NA = M::kSplit ? 2 : 1;          // hi (and lo) copies
+  __shared__ __attribute__((aligned(16))) E At[NA][D * LDA];
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int tiles = (a.T + ROWS - 1) / ROWS;
-  const int bh = blockIdx.x / tiles, h = bh % a.H;
-  const int t0 = (blockIdx.x - bh * tiles) * ROWS;
+  const int bh = blk / tiles, h = bh % a.H;
+  const int t0 = (blk - bh * tiles) * ROWS;
   const float* Ag = a.A + (size_t)bh * D * D;
-  for (int x = threadIdx.x; x < D * D; x += 256) As[x] = Ag[x];
-  const E* qg = (const E*)a.q + (size_t)bh * a.T * D;
-  for (int x = threadIdx.x; x < ROWS * D; x += 256) {
-    const int t = t0 + x / D;
-    Qs[x / D][x % D] = t < a.T ? (float)qg[(size_t)t * D + x % D] : 0.0f;
+  for (int x = tid; x < D * D; x += 256) {  // A_in[k][m] -> At[m][k]
+    const int k = x / D, m = x % D;
+    const float val = Ag[x];
+    const E hi = (E)val;
+    At[0][m * LDA + k] = hi;
+    if (M::kSplit) At[NA - 1][m * LDA + k] = (E)(val - (float)hi);
   }
   __syncthreads();
   const float sg = sigmoidf(a.gate[h]), lam = a.lam[h];
   const long long first = a.pos0 > a.W ? a.pos0 : (long long)a.W;  // first step of this call that evicts
-  for (int x = threadIdx.x; x < ROWS * D; x += 256) {
-    const int r = x / D, c = x % D, t = t0 + r;
-    if (t >= a.T) continue;
-    float acc = 0.0f;
-#pragma unroll 8
-    for (int j = 0; j < D; ++j) acc = __builtin_fmaf(Qs[r][j], As[j * D + c], acc);
+  const E* qg = (const E*)a.q + (size_t)bh * a.T * D;
+  for (int rg = wid; rg < ROWS / 16; rg += 4) {
+    const int t = t0 + 16 * rg + l16;  // this lane's query row
+    if (t0 + 16 * rg >= a.T) break;
+    frag qf[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      const int k0 = kc * 32 + lg * 8;
+      qf[kc] = (t < a.T && k0 < D) ? *(const frag*)(qg + (size_t)t * D + k0) : M::zero();
+    }
     const long long n = a.pos0 + t + 1 - first;
-    a.yinit[((size_t)bh * a.T + t) * D + c] = sg * powi(lam, n > 0 ? (int)n : 0) * acc;
+    const float f = sg * powi(lam, n > 0 ? (int)n : 0);
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        const int k0 = kc * 32 + lg * 8;
+        const E* row = &At[0][(ct * 16 + l16) * LDA + k0];
+        acc = M::mma(k0 < D ? M::lds8(row) : M::zero(), qf[kc], acc);
+        if (M::kSplit) acc = M::mma(k0 < D ? M::lds8(row + (NA - 1) * D * LDA) : M::zero(), qf[kc], acc);
+      }
+      if (t < a.T) *(f32x4*)(a.yinit + ((size_t)bh * a.T + t) * D + ct * 16 + lg * 4) = f * acc;
+    }
   }
 }
 
-// A <- A_new + lambda^N A (N = evictions in this call), elementwise.
-__global__ void __launch_bounds__(256) cont_state_kernel(ContArgs a) {
-  const long long DD = (long long)a.D * a.D, total = (long long)a.B * a.H * DD;
-  const long long first = a.pos0 > a.W ? a.pos0 : (long long)a.W;
-  const long long N = a.pos0 + a.T - first;
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
-    const int h = (int)((i / DD) % a.H);
-    a.A[i] = __builtin_fmaf(powi(a.lam[h], N > 0 ? (int)N : 0), a.A[i], a.A_new[i]);
-  }
+// One launch for both preparations (they are independent and overlap):
+// workgroups 0 .. nI-1 form the initial-state read, the others copy the
+// extended sequence.
+template <class E, int D>
+__global__ void __launch_bounds__(256) cont_prep_kernel(ContArgs a, int nI) {
+  if ((int)blockIdx.x < nI)
+    cont_init_read<E, D>(a, blockIdx.x);
+  else
+    cont_gather(a, blockIdx.x - nI, gridDim.x - nI);
 }
 
-// The last min(Tx, W) extended rows into their ring slots; pos[b] = pos0 + T.
-__global__ void __launch_bounds__(256) cont_ring_kernel(ContArgs a) {
+// Workgroups 0 .. nA-1: A <- A_new + lambda^N A (N = evictions in this call),
+// elementwise.  The others: the last min(Tx, W) extended rows into their ring
+// slots.  Workgroup 0 also sets pos[b] = pos0 + T.
+__global__ void __launch_bounds__(256) cont_finish_kernel(ContArgs a, int nA) {
+  if (a.pos && blockIdx.x == 0)
+    for (int b = threadIdx.x; b < a.B; b += 256) a.pos[b] = a.pos0 + a.T;
+  if ((int)blockIdx.x < nA) {
+    const long long DD = (long long)a.D * a.D, total = (long long)a.B * a.H * DD;
+    const long long first = a.pos0 > a.W ? a.pos0 : (long long)a.W;
+    const long long N = a.pos0 + a.T - first;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)nA * 256) {
+      const int h = (int)((i / DD) % a.H);
+      a.A[i] = __builtin_fmaf(powi(a.lam[h], N > 0 ? (int)N : 0), a.A[i], a.A_new[i]);
+    }
+    return;
+  }
   const int nv = a.D * a.esize / 16;
   const int keep = a.Tx < a.W ? a.Tx : a.W;
   const long long total = (long long)a.B * a.H * keep * nv;
-  if (a.pos && blockIdx.x == 0)
-    for (int b = threadIdx.x; b < a.B; b += 256) a.pos[b] = a.pos0 + a.T;
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
+  const long long nr = gridDim.x - nA;
+  for (long long i = (long long)(blockIdx.x - nA) * 256 + threadIdx.x; i < total; i += nr * 256) {
     const long long row = i / nv;
-    const int c = (int)(i - row * nv);
+    const int cc = (int)(i - row * nv);
     const long long bh = row / keep;
     const int r = a.Tx - keep + (int)(row - bh * keep);  // extended row
     const long long slot = (a.pos0 - a.p + r) % a.W;
-    const long long src = (bh * a.Tx + r) * nv + c, dst = (bh * a.W + slot) * nv + c;
+    const long long src = (bh * a.Tx + r) * nv + cc, dst = (bh * a.W + slot) * nv + cc;
     ((uint4*)a.k_ring)[dst] = ((const uint4*)a.kx)[src];
     ((uint4*)a.v_ring)[dst] = ((const uint4*)a.vx)[src];
   }
@@ -124,13 +163,15 @@ unsigned copy_grid(long long vectors) {
 }
 
 template <class E>
-hipError_t launch_init_read(const ContArgs& a, hipStream_t s) {
-  const dim3 grid(a.B * a.H * ((a.T + 15) / 16));
+hipError_t launch_prep(const ContArgs& a, hipStream_t s) {
+  const int nI = a.B * a.H * ((a.T + 127) / 128);
+  const unsigned nG = copy_grid((long long)a.B * a.H * a.Tx * (a.D * a.esize / 16));
+  const dim3 grid(nI + nG);
   switch (a.D) {
-    case 16: hipLaunchKernelGGL((cont_init_read_kernel<E, 16>), grid, dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((cont_init_read_kernel<E, 32>), grid, dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((cont_init_read_kernel<E, 64>), grid, dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((cont_init_read_kernel<E, 128>), grid, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((cont_prep_kernel<E, 16>), grid, dim3(256), 0, s, a, nI); break;
+    case 32: hipLaunchKernelGGL((cont_prep_kernel<E, 32>), grid, dim3(256), 0, s, a, nI); break;
+    case 64: hipLaunchKernelGGL((cont_prep_kernel<E, 64>), grid, dim3(256), 0, s, a, nI); break;
+    case 128: hipLaunchKernelGGL((cont_prep_kernel<E, 128>), grid, dim3(256), 0, s, a, nI); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -138,20 +179,15 @@ hipError_t launch_init_read(const ContArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_continue_prep(const ContArgs& a, hipStream_t s) {
-  const int nv = a.D * a.esize / 16;
-  hipLaunchKernelGGL(cont_gather_kernel, dim3(copy_grid((long long)a.B * a.H * a.Tx * nv)), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return a.esize == 2 ? launch_init_read<bf16>(a, s) : launch_init_read<float>(a, s);
+  return a.esize == 2 ? launch_prep<bf16>(a, s) : launch_prep<float>(a, s);
 }
 
 hipError_t launch_continue_finish(const ContArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(cont_state_kernel, dim3(copy_grid((long long)a.B * a.H * a.D * a.D)), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int nv = a.D * a.esize / 16;
   const long long keep = a.Tx < a.W ? a.Tx : a.W;
-  hipLaunchKernelGGL(cont_ring_kernel, dim3(copy_grid((long long)a.B * a.H * keep * nv)), dim3(256), 0, s, a);
+  const unsigned nA = copy_grid((long long)a.B * a.H * a.D * a.D);
+  const unsigned nR = copy_grid((long long)a.B * a.H * keep * nv);
+  hipLaunchKernelGGL(cont_finish_kernel, dim3(nA + nR), dim3(256), 0, s, a, (int)nA);
   return hipGetLastError();
 }
 

@@ -398,9 +398,10 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
       }
     };
 
-    // One block per segment (PUB): segments m >= m_lo have evictions at or
-    // after token 0 (L_m != 0); S(e0) = sum_{m_lo <= m < seg} lambda^((seg-1-m) BM) L_m.
-    const int m_lo = W / BM;
+    // One block per segment (PUB): segments m >= m_lo (blocks j0 + m >= W / BM)
+    // have evictions at or after token 0 (L_m != 0);
+    // S(e0) = sum_{m_lo <= m < seg} lambda^((seg-1-m) BM) L_m.
+    const int m_lo = W / BM - a.j0;
     const bool pub = PUB && seg >= m_lo && seg + 1 < a.nseg;
     const bool fin = PUB && last && a.A_final != nullptr && has_mem;
     float* const Lt = (float*)Qs;  // L^T of the last block (the Q area is free after qf is read)

@@ -20,7 +20,8 @@ struct FwdArgs {
   float* seg_state;  // [B*H][nseg][D*D] segment-start states (eta factored out)
   int B, H, T, W;
   int nblk;  // ceil(T / block rows): 128 (bf16, D <= 64) or 64
-  int nseg;  // segments: the first R hold G + 1 blocks, the others G
+  int j0;    // first query block processed (blocks below it hold only unstored rows < row0)
+  int nseg;  // segments of blocks j0 .. nblk-1: the first R hold G + 1 blocks, the others G
   int G;
   int R;
   int prefix_direct;  // fused kernel combines the local segment states itself (no chain kernel)
@@ -47,7 +48,7 @@ struct FwdArgs {
 };
 
 // First block of forward segment s (s = nseg gives nblk).
-__host__ __device__ inline int seg_first_block(const FwdArgs& a, int s) { return s * a.G + (s < a.R ? s : a.R); }
+__host__ __device__ inline int seg_first_block(const FwdArgs& a, int s) { return a.j0 + s * a.G + (s < a.R ? s : a.R); }
 // Blocks of forward segment s.
 __host__ __device__ inline int seg_blocks(const FwdArgs& a, int s) { return a.G + (s < a.R ? 1 : 0); }
 
