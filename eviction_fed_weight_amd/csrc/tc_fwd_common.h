@@ -335,7 +335,8 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
 // Chain over segments, in place: seg_state[0] = 0 and
 // seg_state[m+1] = lambda^(BM blocks(m)) seg_state[m] + L_m.
 // grid = (D*D/4 + 255)/256 x BH; each thread owns four consecutive floats and
-// loads eight segments ahead of the dependent chain.
+// loads 32 segments ahead of the dependent chain (the chain is bound by load
+// latency, not by its arithmetic).
 template <int D, int BM>
 __global__ void __launch_bounds__(256) seg_chain_kernel(FwdArgs a) {
   const int bh = blockIdx.y;
@@ -347,13 +348,14 @@ __global__ void __launch_bounds__(256) seg_chain_kernel(FwdArgs a) {
   const size_t stride = (size_t)D * D / 4;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   p[0] = s;
-  for (int m0 = 1; m0 < a.nseg; m0 += 8) {
-    float4 l[8];
+  constexpr int AHEAD = 32;
+  for (int m0 = 1; m0 < a.nseg; m0 += AHEAD) {
+    float4 l[AHEAD];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < AHEAD; ++u)
       if (m0 + u < a.nseg) l[u] = p[(m0 + u) * stride];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < AHEAD; ++u)
       if (m0 + u < a.nseg) {
         const float dm = m0 + u - 1 < a.R ? decay1 : decay;
         s.x = dm * s.x + l[u].x;
