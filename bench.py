@@ -61,7 +61,7 @@ def measured_traffic():
     if kv.get("csrc_sha256") != csrc_digest():
         return {}
     out = {}
-    for leg in ("prefill", "long", "decode", "backward", "train_forward"):
+    for leg in ("prefill", "long", "decode", "backward", "train_forward", "continue"):
         key = "%s_bytes_per_call" % leg
         if key in kv:
             out[leg] = float(kv[key])
@@ -187,7 +187,7 @@ def continue_leg(steps, warmup, chunk=4096):
                 % (B, H, D, T, W, cfg.C, n, chunk),
                 ms_per_sequence=ms, tokens_per_s=B * T / (ms * 1e-3), flops=fl,
                 roofline=dict(bound="mfma", achieved=tflops, peak=PEAK_BF16, unit="TFLOP/s", frac=tflops / PEAK_BF16,
-                              traffic=None,
+                              traffic=measured_traffic().get("continue"),
                               kernel="%d tc_forward_continue calls (gather + initial-state read + forward over "
                                      "ring prefix and chunk + state/ring update)" % n))
 

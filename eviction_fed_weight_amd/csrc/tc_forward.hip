@@ -358,7 +358,7 @@ static hipError_t launch_fwd_impl(const FwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
   if (a.nseg > 1) {
     hipLaunchKernelGGL((seg_state_kernel<E, D, 64>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((seg_chain_kernel<D, 64>), dim3((D * D / 4 + 255) / 256, BH), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((seg_chain_kernel<D, 64>), dim3((D * D / 4 + kChainThreads - 1) / kChainThreads, BH), dim3(kChainThreads), 0, s, a);
   }
   hipLaunchKernelGGL((fwd_kernel<E, D>), dim3(BH * a.nseg), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -334,14 +334,15 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
 
 // Chain over segments, in place: seg_state[0] = 0 and
 // seg_state[m+1] = lambda^(BM blocks(m)) seg_state[m] + L_m.
-// grid = (D*D/4 + 63)/64 x BH of one wave each (the pass moves two D x D
+// grid = (D*D/4 + 63)/64 x BH of one wave (kChainThreads) each (the pass moves two D x D
 // states per segment; small workgroups spread it over many compute units);
 // each thread owns four consecutive floats and loads 32 segments ahead of the
 // dependent chain.
+constexpr int kChainThreads = 64;  // workgroup size of seg_chain_kernel (its launches use it too)
 template <int D, int BM>
-__global__ void __launch_bounds__(64) seg_chain_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(kChainThreads) seg_chain_kernel(FwdArgs a) {
   const int bh = blockIdx.y;
-  const int x = blockIdx.x * 64 + threadIdx.x;
+  const int x = blockIdx.x * kChainThreads + threadIdx.x;
   if (x * 4 >= D * D) return;
   // S_m = lambda^(BM blocks(m-1)) S_{m-1} + L_{m-1}
   const float decay = powi(a.lam[bh % a.H], BM * a.G), decay1 = decay * powi(a.lam[bh % a.H], BM);

@@ -769,7 +769,7 @@ static hipError_t launch_rows_impl(const FwdArgs& a0, hipStream_t s) {
   if (a.nseg > 1 && !a.publish) {
     hipLaunchKernelGGL((seg_state_kernel<E, D, BM>), dim3(BH * (a.nseg - 1 + a.final_slot)), dim3(256), 0, s, a);
     if (!a.prefix_direct)
-      hipLaunchKernelGGL((seg_chain_kernel<D, BM>), dim3((D * D / 4 + 63) / 64, BH), dim3(64), 0, s, a);
+      hipLaunchKernelGGL((seg_chain_kernel<D, BM>), dim3((D * D / 4 + kChainThreads - 1) / kChainThreads, BH), dim3(kChainThreads), 0, s, a);
   }
   if (a.publish)
     hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, true>), dim3(BH * a.nseg), dim3(64 * NW), 0, s, a);
