@@ -8,7 +8,7 @@ per second), the long-context prefill and the backward, each with its
 roofline, plus the CPU oracle timed on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
-                    [--legs prefill,decode,long,backward,train_forward,continue[,calib]]
+                    [--legs prefill,decode,long,backward,train_forward,continue,capacity[,calib]]
 """
 from __future__ import annotations
 
@@ -192,6 +192,32 @@ def continue_leg(steps, warmup, chunk=4096):
                                      "ring prefix and chunk + state/ring update)" % n))
 
 
+def capacity_leg(D=128, H=8, Ns=(64, 128, 256, 512, 1024, 2048, 4096)):
+    """Raw memory-capacity diagnostic: N unit-norm keys with N(0,1) values
+    written into A (window 1, lambda = eta = 1), then read back with the
+    stored keys; recall@1 = fraction of reads whose nearest stored value (by
+    cosine) is their own.  One tc_forward call of 2N tokens per N."""
+    import torch
+
+    import eviction_fed_weight_amd as tc
+    import tc_inputs
+
+    dv = torch.device("cuda")
+    out = []
+    for N in Ns:
+        q, k, v, lam, eta, g, vals = tc_inputs.capacity_inputs(N, D, H)
+        Q, K, V = (torch.from_numpy(x).to(dv).to(torch.bfloat16) for x in (q, k, v))
+        L, E, G = (torch.from_numpy(x).to(dv) for x in (lam, eta, g))
+        y, _, _ = tc.tc_forward(Q, K, V, L, E, G, 1, 64, want_state=False, want_lse=False)
+        ms = time_calls(lambda: tc.tc_forward(Q, K, V, L, E, G, 1, 64, y=y, want_state=False, want_lse=False), 5, 2)
+        r = torch.nn.functional.normalize(y[0, :, N:].float(), dim=-1)
+        st = torch.nn.functional.normalize(torch.from_numpy(vals).to(dv).float(), dim=-1)
+        hit = (torch.bmm(r, st.transpose(1, 2).contiguous()).argmax(-1) == torch.arange(N, device=dv)).float()
+        out.append(dict(N=N, N_over_D=N / D, recall_at_1=hit.mean().item(), ms_per_call=ms))
+    return dict(workload="capacity probe D=%d H=%d bf16: N pairs written, then read with their keys" % (D, H),
+                points=out)
+
+
 def decode_leg(steps, warmup):
     """Serving decode: 64 streams x 32 heads, D=128, W=4096.  The start state
     (ring of the last 4,096 pairs, A after 8,192 prior evictions) is built on
@@ -323,7 +349,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--legs", default="prefill,decode,long,backward,train_forward,continue")
+    ap.add_argument("--legs", default="prefill,decode,long,backward,train_forward,continue,capacity")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -373,6 +399,11 @@ def main():
         cl = continue_leg(max(3, args.steps // 5), 2)
         log("  continue", json.dumps(cl))
         out["chunked_prefill"] = cl
+    if "capacity" in legs:
+        log("capacity diagnostic leg ...")
+        cp = capacity_leg()
+        log("  capacity", json.dumps(cp))
+        out["capacity"] = cp
     if "train_forward" in legs:
         log("training-shape forward leg ...")
         tf = prefill_leg(5, max(3, args.steps // 5), 2)

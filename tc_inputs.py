@@ -162,3 +162,33 @@ def decode_stream_inputs(seed: int, s: int, H: int, D: int, W: int, prior: int, 
     k = f(steps, H, D)
     v = f(steps, H, D)
     return dict(prior_k=prior_k, prior_v=prior_v, ring_k=ring_k, ring_v=ring_v, q=q, k=k, v=v)
+
+
+def capacity_inputs(N: int, D: int, H: int = 4, seed: int = 6, dtype: str = "bf16", orthonormal: bool = False):
+    """Raw associative-memory capacity probe (the pages' capacity diagnostic:
+    retrieval as more unrelated associations share the fixed state).  One
+    sequence of 2N tokens per head, for a layer with window W = 1, lambda =
+    eta = 1 and a gate logit of 30 (sigmoid = 1 in float32):
+      tokens 0 .. N-1    write pairs: q = 0, k = k_i (unit norm), v = v_i ~ N(0,1)
+      tokens N .. 2N-1   reads:       q = k_i, k = 0, v = 0
+    With W = 1 every pair leaves the window one step after it enters, so row
+    N + i reads the memory of all N pairs with the key of pair i (the read
+    tokens write zero outer products and their own window value is zero).
+    orthonormal=True (N <= D) draws orthonormal keys.  Returns q, k, v
+    [1, H, 2N, D] in the storage dtype (as float32 arrays), lam, eta, gate [H]
+    and the stored values [H, N, D]."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, N, D])))
+    if orthonormal:
+        assert N <= D
+        keys = np.stack([np.linalg.qr(g.standard_normal((D, D)))[0][:, :N].T for _ in range(H)]).astype(np.float32)
+    else:
+        keys = g.standard_normal((H, N, D), dtype=np.float32)
+        keys /= np.linalg.norm(keys, axis=-1, keepdims=True)
+    keys = _store(keys, dtype)
+    vals = _store(g.standard_normal((H, N, D), dtype=np.float32), dtype)
+    z = np.zeros((H, N, D), np.float32)
+    q = np.concatenate([z, keys], axis=1)[None]
+    k = np.concatenate([keys, z], axis=1)[None]
+    v = np.concatenate([vals, z], axis=1)[None]
+    ones = np.ones(H, np.float32)
+    return q, k, v, ones, ones.copy(), np.full(H, 30.0, np.float32), vals

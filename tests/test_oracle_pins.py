@@ -342,3 +342,25 @@ def test_state_after_writes_matches_recurrence():
     vv = np.vstack([v, np.zeros((1, D))])
     _, A, _ = fwd1(q, kk, vv, 0.93, 0.37, 0.0, 1)
     np.testing.assert_allclose(dense.state_after_writes(k, v, 0.93, 0.37), A, rtol=1e-12, atol=1e-13)
+
+
+def test_capacity_probe_reads_gram_weighted_values():
+    """The capacity probe (window 1, lambda = eta = 1, N write pairs then N
+    reads with the stored keys) reads y_{N+i} = sigmoid(g) sum_j <k_i,k_j> v_j:
+    the Gram matrix of the keys times the values (q (k outer v) = <q,k> v
+    summed over the memory).  With orthonormal keys every value comes back
+    exactly."""
+    import tc_inputs
+
+    for N, D, ortho in [(24, 16, False), (16, 16, True), (5, 8, True)]:
+        q, k, v, lam, eta, g, vals = tc_inputs.capacity_inputs(N, D, H=2, dtype="f32", orthonormal=ortho)
+        y, A, _ = oracle.forward(q, k, v, lam, eta, g, 1)
+        keys = k[0, :, :N].astype(np.float64)
+        sg = 1.0 / (1.0 + np.exp(-30.0))
+        want = sg * np.einsum("hij,hjd->hid", keys @ keys.transpose(0, 2, 1), vals.astype(np.float64))
+        np.testing.assert_allclose(y[0, :, N:], want, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(A[0], np.einsum("hja,hjc->hac", keys, vals.astype(np.float64)), rtol=1e-12,
+                                   atol=1e-13)
+        if ortho:
+            np.testing.assert_allclose(y[0, :, N:], vals, rtol=0, atol=1e-5)
+
