@@ -24,7 +24,7 @@ def tc():
 
 def sequence(seed, B, H, T, D, dtype):
     rng = np.random.default_rng(seed)
-    x = [rng.standard_normal((B, H, T, D)).astype(np.float32) / np.sqrt(D) for _ in range(3)]
+    x = [(rng.standard_normal((B, H, T, D)) / np.sqrt(D)).astype(np.float32) for _ in range(3)]
     if dtype == "bf16":
         x = [tc_inputs.bf16_round(a) for a in x]
     lam, eta, g = tc_inputs.head_params(rng, rng, rng, H)
@@ -58,6 +58,9 @@ CASES = [
     (2, 1, 40, 1, 64, 64, "bf16"),       # one token: a decode step
     (1, 2, 70, 20, 32, 100, "bf16"),     # pos0 + T < W: no eviction at all
     (1, 2, 3000, 2500, 64, 1024, "bf16"),
+    (1, 2, 300, 200, 64, 100, "bf16"),   # 128-row kernel, W not a multiple of the block (prefix 100 rows)
+    (2, 2, 50, 70, 16, 32, "bf16"),      # D = 16 bf16
+    (1, 1, 600, 150, 128, 256, "f32"),   # float32 D = 128
 ]
 
 
@@ -149,3 +152,55 @@ def test_continue_rejects_bad_arguments():
         tc().tc_forward_continue(x, x, x, p, p, p, kr, vr, A, -1)
     with pytest.raises(tc().TCError):  # the output ring aliases the input keys
         tc().tc_forward_continue(x, kr[:, :, :T], x, p, p, p, kr, vr, A, 4)
+
+
+def test_continue_graph_capture():
+    """tc_forward_continue captured in a HIP graph (pos0 is part of the
+    captured call) and replayed from restored states on changed inputs, with
+    an eager call between the replays: every replay matches the streaming-step
+    oracle.  (No memset nodes; the forward takes its capture-safe path.)"""
+    B, H, T0, T1, D, W, dtype = 1, 2, 700, 300, 64, 256, "bf16"
+    m = tc()
+    seqs = [sequence(90 + i, B, H, T0 + T1, D, dtype) for i in range(3)]
+    sl = slice(T0, T0 + T1)
+    states = [state_at(*x[0], *x[1:], T0, W) for x in seqs]
+    q, k, v = (dev(seqs[0][0][j][:, :, sl], dtype) for j in range(3))
+    lam, eta, g = (dev(x) for x in seqs[0][1:])
+    kr, vr, A = dev(states[0][0], dtype), dev(states[0][1], dtype), dev(states[0][2], "f32")
+    y = torch.empty_like(q)
+    lse = torch.empty((B, H, T1), dtype=torch.float32, device="cuda")
+    shape = m.make_shape(B, H, T1, D, W, 64, 0.0, m.TC_BF16)
+    ws = torch.empty(m.tc_continue_workspace_size(shape, T0), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        m.tc_forward_continue(q, k, v, lam, eta, g, kr, vr, A, T0, y=y, lse=lse, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        m.tc_forward_continue(q, k, v, lam, eta, g, kr, vr, A, T0, y=y, lse=lse, ws=ws)
+    torch.cuda.synchronize()
+    for i in (1, 2, 0):
+        (qq, kk, vv), la, et, ga = seqs[i]
+        okr, ovr, oA = (x.copy() for x in states[i])
+        yo = oracle.forward_continue(qq[:, :, sl], kk[:, :, sl], vv[:, :, sl], okr, ovr, oA, T0, la, et, ga)
+        for dst, x in ((q, qq), (k, kk), (v, vv)):
+            dst.copy_(dev(x[:, :, sl], dtype))
+        for dst, x in ((lam, la), (eta, et), (g, ga)):
+            dst.copy_(dev(x))
+        for dst, x, dt in ((kr, states[i][0], dtype), (vr, states[i][1], dtype), (A, states[i][2], "f32")):
+            dst.copy_(dev(x, dt))
+        graph.replay()
+        torch.cuda.synchronize()
+        err = dict(y=rel(host(y), yo), A=rel(host(A), oA))
+        say("  replay", i, err)
+        assert max(err.values()) <= TOL[dtype], ("replay", i, err)
+        assert np.array_equal(host(kr), okr)
+        # an eager call from the same restored state on the same workspace
+        for dst, x, dt in ((kr, states[i][0], dtype), (vr, states[i][1], dtype), (A, states[i][2], "f32")):
+            dst.copy_(dev(x, dt))
+        ye, _ = m.tc_forward_continue(q, k, v, lam, eta, g, kr, vr, A, T0, ws=ws)
+        torch.cuda.synchronize()
+        assert rel(host(ye), yo) <= TOL[dtype]
+
