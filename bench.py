@@ -347,8 +347,8 @@ def cpu_baseline(budget_s=12.0, max_runs=400):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--legs", default="prefill,decode,long,backward,train_forward,continue,capacity")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()

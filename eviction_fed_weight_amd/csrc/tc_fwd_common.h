@@ -133,16 +133,16 @@ __device__ __forceinline__ void state_publish(const State<E, D>& st, float* g, i
 }
 
 // acc = sum_{m0 <= m < m1} dec^(m1-1-m) (the state published at g + m D^2),
-// the loads of up to eight states in flight at once
+// the loads of up to four states in flight at once
 template <class E, int D>
 __device__ __forceinline__ void state_gather_all(State<E, D>& acc, float dec, const float* g, int m0, int m1,
                                                  int wid, int lane) {
   constexpr int NT = D / 16, NOWN = State<E, D>::NOWN;
   const auto rs = make_rsrc(g, (uint32_t)m1 * D * D * 4);
-  for (int mb = m0; mb < m1; mb += 8) {
-    f32x4 x[8][NOWN][NT];
+  for (int mb = m0; mb < m1; mb += 4) {
+    f32x4 x[4][NOWN][NT];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int o = 0; o < NOWN; ++o)
 #pragma unroll
@@ -155,7 +155,7 @@ __device__ __forceinline__ void state_gather_all(State<E, D>& acc, float dec, co
           x[u][o][at] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCoherentPolicy));
         }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 4; ++u)
       if (mb + u < m1)
 #pragma unroll
         for (int o = 0; o < NOWN; ++o)

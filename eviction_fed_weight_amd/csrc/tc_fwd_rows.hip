@@ -265,13 +265,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
     }
   };
   // publish the staged item, stage the next one, barrier
-  int hold = 0;  // PUB: the next step only synchronises (its item is already in LDS)
   auto step = [&]() {
-    if (PUB && hold) {
-      hold = 0;
-      __syncthreads();
-      return;
-    }
     if (pj < je) store_next();
     advance();
     load_next();
@@ -281,17 +275,6 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   TileRegs<E, D, BM, NTH> qr;
   if (PUB) qr.load(Qg, jb * BM);
   load_next();  // the first item's loads overlap the state set-up below
-  // PUB: the second key tile's loads are issued with the first (the block's
-  // first tiles come from HBM, and the window then waits for one latency
-  // instead of two); the first step stores both, the step after tile 0 only
-  // synchronises, and from there the pipeline runs as usual, one item ahead.
-  TileRegs<E, D, 64, NTH> kr1, vr1;
-  const bool pre2 = PUB && pb.nb >= 3;
-  if (pre2) {
-    const int r1 = pb.kb + 64 * tile_of(pb, 1);
-    kr1.load(Kg, r1);
-    vr1.load(Vg, r1);
-  }
 
   if (tid <= BM) pw[tid] = powi(a.lam[h], tid);
 
@@ -360,19 +343,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
 #pragma unroll
       for (int dc = 0; dc < NKC; ++dc)
         qf[g][dc] = (dc * 32 + lg * 8 < D) ? M::lds8(Qs + (rw + 16 * g + l16) * LDK + dc * 32 + lg * 8) : M::zero();
-    if (pre2) {
-      store_next();  // tile 0 -> buffer 0
-      kr1.store((E*)(smem + L::BUF), LDK);  // tile 1 -> buffer 1
-      vr1.store((E*)(smem + L::BUF + L::KT), LDV);
-      ++kv_stored;
-      advance();
-      advance();
-      load_next();  // tile 2
-      __syncthreads();
-      hold = 1;
-    } else {
-      step();
-    }
+    step();
 
     f32x4 O[2][NT];
     float mrow[2];
