@@ -108,6 +108,28 @@ def time_calls(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps  # ms per call
 
 
+def cold_ms(fn, n, flush_mib=512):
+    """Median time of n single calls, each after a 512 MiB device write so
+    that no input is left in the 256 MB Infinity Cache (inputs in HBM)."""
+    import torch
+
+    buf = torch.empty(flush_mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+    times = []
+    for i in range(n):
+        buf.fill_(float(i))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    del buf
+    return times[len(times) // 2]
+
+
 def prefill_leg(cfg_id, steps, warmup):
     import torch
 
@@ -132,6 +154,7 @@ def prefill_leg(cfg_id, steps, warmup):
     fl = fwd_flops(cfg.B, cfg.H, cfg.T, cfg.D, cfg.W, cfg.C)
     by = fwd_bytes(cfg.B, cfg.H, cfg.T, cfg.D)
     tflops = fl / (ms * 1e-3) / 1e12
+    cold = cold_ms(call, 20) if cfg_id in (2, 3) else None
     return dict(
         workload="%s B=%d H=%d D=%d T=%d W=%d C=%d bf16" % ("forward" if cfg_id == 5 else "prefill", cfg.B, cfg.H, cfg.D,
                                                            cfg.T, cfg.W, cfg.C),
@@ -143,6 +166,10 @@ def prefill_leg(cfg_id, steps, warmup):
                               "one tc_forward call (seg_state_kernel + seg_chain_kernel + fwd_kernel, D=128: 64-row "
                               "blocks, state in LDS)")),
         hbm_gbs=by / (ms * 1e-3) / 1e9,
+        cold=None if cold is None else dict(
+            ms_per_call=cold, tokens_per_s=cfg.B * cfg.T / (cold * 1e-3), tflops=fl / (cold * 1e-3) / 1e12,
+            frac=fl / (cold * 1e-3) / 1e12 / PEAK_BF16,
+            note="median of 20 single calls, each after writing 512 MiB (the 256 MB Infinity Cache holds no input)"),
     )
 
 
@@ -378,6 +405,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": pre["workload"], "B": 8, "H": 8, "D": 64, "T": 1024, "W": 256, "C": 64},
         "roofline": pre["roofline"],
+        "cold": pre["cold"],
     }
     if "decode" in legs:
         log("decode leg ...")
