@@ -366,9 +366,23 @@ def cpu_baseline(budget_s=12.0, max_runs=400):
         oracle.forward(d["q"], d["k"], d["v"], d["lam"], d["eta"], d["gate"], cfg.W)
         times.append(time.time() - t)
     sec = float(np.median(times))
-    return dict(value=cfg.B * cfg.T / sec, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+    cores = oracle.num_threads()
+    # the same oracle on one thread, over one (b,h) sequence of the batch (scaled to the batch: the
+    # batch is 64 such independent sequences)
+    oracle.set_num_threads(1)
+    one = []
+    for _ in range(3):
+        t = time.time()
+        oracle.forward(d["q"][:1, :1], d["k"][:1, :1], d["v"][:1, :1], d["lam"][:1], d["eta"][:1], d["gate"][:1],
+                       cfg.W)
+        one.append(time.time() - t)
+    oracle.set_num_threads(cores)
+    sec1 = float(np.median(one)) * cfg.B * cfg.H
+    return dict(value=cfg.B * cfg.T / sec, unit="tokens/s", cores=cores, kind="oracle",
                 sample="full prefill batch (B=8 H=8 T=1024 W=256 D=64), float64 per-token recurrence, "
-                       "median of %d runs" % len(times), seconds_per_batch=sec)
+                       "median of %d runs" % len(times), seconds_per_batch=sec,
+                single_thread=dict(value=cfg.B * cfg.T / sec1, unit="tokens/s", seconds_per_batch=sec1,
+                                   sample="one (b,h) sequence of the same batch on one thread, median of 3, x64"))
 
 
 def main():

@@ -57,12 +57,19 @@ def _load():
         lib.tco_memory_f32_sequential.argtypes = [_i] * 3 + [ctypes.c_float] * 2 + [_F] * 5
         lib.tco_memory_f32_chunked.argtypes = [_i] * 4 + [ctypes.c_float] * 2 + [_F] * 5
         lib.tco_num_threads.restype = ctypes.c_int
+        lib.tco_set_num_threads.argtypes = [_i]
         _lib = lib
     return _lib
 
 
 def num_threads() -> int:
     return int(_load().tco_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of the following calls (timing only; results do not
+    depend on it: the work is split per (b, h) and each is computed alone)."""
+    _load().tco_set_num_threads(int(n))
 
 
 def _f64(x) -> np.ndarray:

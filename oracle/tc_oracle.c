@@ -49,6 +49,15 @@ static double dot(const double* a, const double* b, int n) {
   return s;
 }
 
+/* Threads for the following calls (the CPU baseline also times one thread). */
+void tco_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* Number of threads OpenMP will use (reported by the CPU baseline). */
 int tco_num_threads(void) {
 #ifdef _OPENMP
