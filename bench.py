@@ -220,7 +220,9 @@ def continue_leg(steps, warmup, chunk=4096):
 
 
 def capacity_leg(D=128, H=8, Ns=(64, 128, 256, 512, 1024, 2048, 4096)):
-    """Raw memory-capacity diagnostic: N unit-norm keys with N(0,1) values
+    """Raw memory-capacity diagnostic (the "memory-capacity diagnostics" of the
+    abstract of "Tensor Cache: Eviction-conditioned Associative Memory for
+    Transformers"; parameters are not given there): N unit-norm keys with N(0,1) values
     written into A (window 1, lambda = eta = 1), then read back with the
     stored keys; recall@1 = fraction of reads whose nearest stored value (by
     cosine) is their own.  One tc_forward call of 2N tokens per N."""

@@ -165,8 +165,12 @@ def decode_stream_inputs(seed: int, s: int, H: int, D: int, W: int, prior: int, 
 
 
 def capacity_inputs(N: int, D: int, H: int = 4, seed: int = 6, dtype: str = "bf16", orthonormal: bool = False):
-    """Raw associative-memory capacity probe (the pages' capacity diagnostic:
-    retrieval as more unrelated associations share the fixed state).  One
+    """Raw associative-memory capacity probe.  The abstract of "Tensor Cache:
+    Eviction-conditioned Associative Memory for Transformers" lists
+    memory-capacity diagnostics among its experiments; its technical summary
+    (results) reports only that retrieval falls as more unrelated associations
+    share the fixed state, with no parameters, so this probe is one reading of
+    it.  One
     sequence of 2N tokens per head, for a layer with window W = 1, lambda =
     eta = 1 and a gate logit of 30 (sigmoid = 1 in float32):
       tokens 0 .. N-1    write pairs: q = 0, k = k_i (unit norm), v = v_i ~ N(0,1)
