@@ -182,7 +182,8 @@ tc_status_t cont_plan_for(const tc_shape_t* s, int64_t pos0, ContPlan& c) {
   const tc_status_t sx = check_shape(&c.x);
   if (sx != TC_OK) return sx;
   const long long BH = (long long)s->B * s->H;
-  if (BH * ((s->T + 127) / 128) > (1LL << 31) - 1) return TC_ERR_UNSUPPORTED;
+  // grid of the preparation kernel: one workgroup per (b,h) and 128 new rows, plus up to 8192 copy workgroups
+  if (BH * ((s->T + 127) / 128) > (1LL << 31) - 1 - 8192) return TC_ERR_UNSUPPORTED;
   c.fp = plan_for(c.x, c.p);
   const size_t es = elem_size(s->dtype);
   const size_t nx = align256((size_t)BH * c.x.T * s->D * es);

@@ -164,7 +164,7 @@ unsigned copy_grid(long long vectors) {
 
 template <class E>
 hipError_t launch_prep(const ContArgs& a, hipStream_t s) {
-  const int nI = a.B * a.H * ((a.T + 127) / 128);
+  const int nI = (int)((long long)a.B * a.H * ((a.T + 127) / 128));  // (bounded on the host)
   const unsigned nG = copy_grid((long long)a.B * a.H * a.Tx * (a.D * a.esize / 16));
   const dim3 grid(nI + nG);
   switch (a.D) {
