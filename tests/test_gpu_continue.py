@@ -204,3 +204,33 @@ def test_continue_graph_capture():
         torch.cuda.synchronize()
         assert rel(host(ye), yo) <= TOL[dtype]
 
+
+
+def test_continue_from_a_late_position_with_a_given_memory():
+    """pos0 = 10^12 + 7 (slot and decay counts in 64-bit) and an arbitrary
+    memory handed in: the ring holds the last W tokens at slot position mod W
+    (ring order != time order), and the result equals the streaming steps."""
+    B, H, T1, D, W, dtype = 2, 2, 300, 64, 128, "bf16"
+    pos0 = 10 ** 12 + 7
+    rng = np.random.default_rng(21)
+    (q, k, v), lam, eta, g = sequence(22, B, H, W + T1, D, dtype)  # tokens pos0-W .. pos0+T1-1
+    kr, vr = np.zeros((B, H, W, D)), np.zeros((B, H, W, D))
+    for i in range(W):
+        kr[:, :, (pos0 - W + i) % W] = k[:, :, i]
+        vr[:, :, (pos0 - W + i) % W] = v[:, :, i]
+    A0 = (rng.standard_normal((B, H, D, D)) * 0.3).astype(np.float32).astype(np.float64)
+    okr, ovr, oA = kr.copy(), vr.copy(), A0.copy()
+    sl = slice(W, W + T1)
+    yo = oracle.forward_continue(q[:, :, sl], k[:, :, sl], v[:, :, sl], okr, ovr, oA, pos0, lam, eta, g)
+    _, _, lo = oracle.forward(q, k, v, lam, eta, g, W)  # the window rows see only the ring and the new tokens
+    gk, gv, gA = dev(kr, dtype), dev(vr, dtype), dev(A0, "f32")
+    pos = torch.zeros(B, dtype=torch.int64, device="cuda")
+    y, lse = tc().tc_forward_continue(dev(q[:, :, sl], dtype), dev(k[:, :, sl], dtype), dev(v[:, :, sl], dtype),
+                                      dev(lam), dev(eta), dev(g), gk, gv, gA, pos0, pos=pos)
+    torch.cuda.synchronize()
+    err = dict(y=rel(host(y), yo), A=rel(host(gA), oA), lse=rel(host(lse), lo[:, :, sl]))
+    say("late position", err)
+    for name, e in err.items():
+        assert e <= TOL[dtype], (name, e)
+    assert np.array_equal(host(gk), okr) and np.array_equal(host(gv), ovr)
+    assert np.all(pos.cpu().numpy() == pos0 + T1)
