@@ -285,3 +285,32 @@ def test_forward_graph_capture():
         torch.cuda.synchronize()
         ee = dict(y=rel(host(ye), yo), A=rel(host(Ae), Ao))
         assert max(ee.values()) <= TOL["bf16"], ("eager", i, ee)
+
+
+def test_forward_concurrent_streams():
+    """Two forwards of the state-exchange shape on two streams at once (each
+    with its own workspace), several times over: both match the oracle.  The
+    other stream's kernel holds compute units, so the grid need not be
+    resident; a workgroup waits only for earlier-dispatched workgroups of its
+    own launch, so every wait still ends."""
+    B, H, T, D, W = 8, 8, 1024, 64, 256
+    m = tc()
+    ds = [tc_inputs.prefill_inputs(2, seed=71 + i, B=B, H=H, T=T, D=D, W=W, dtype="bf16", plants=False)
+          for i in range(2)]
+    ins = [[dev(d[x], "bf16") for x in ("q", "k", "v")] + [dev(d[x], "f32") for x in ("lam", "eta", "gate")]
+           for d in ds]
+    shape = m.make_shape(B, H, T, D, W, 64, 0.0, m.TC_BF16)
+    wss = [torch.empty(m.tc_forward_workspace_size(shape), dtype=torch.uint8, device="cuda") for _ in ds]
+    outs = [[torch.empty_like(x[0]), torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")] for x in ins]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(5):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                m.tc_forward(*ins[i], W, y=outs[i][0], A_final=outs[i][1], want_lse=False, ws=wss[i])
+        torch.cuda.synchronize()
+    for i, d in enumerate(ds):
+        yo, Ao, _ = oracle.forward(d["q"], d["k"], d["v"], d["lam"], d["eta"], d["gate"], W)
+        ey, eA = rel(host(outs[i][0]), yo), rel(host(outs[i][1]), Ao)
+        say("  stream", i, ey, eA)
+        assert ey <= TOL["bf16"] and eA <= TOL["bf16"]
