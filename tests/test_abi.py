@@ -89,6 +89,25 @@ def test_forward_workspace_layout():
     assert tc.tc_forward_workspace_size(tc.make_shape(8, 8, 1024, 64, 256, 64)) == states + flags
 
 
+def test_continue_workspace_layout():
+    """The continuation workspace is a forward workspace for the extended
+    shape (p = min(pos0, W) ring rows + T new rows; whole blocks inside the
+    prefix are not planned, so it is at most tc_forward's for that shape),
+    then the extended q, k and v, the float32 initial-state read [B,H,T,D] and
+    the float32 state of this call's evictions [B,H,D,D], each part rounded up
+    to 256 bytes."""
+    up = lambda n: -(-n // 256) * 256  # noqa: E731
+    for (B, H, T, D, W, pos0, es, dt) in [(2, 4, 512, 64, 256, 1000, 2, tc.TC_BF16), (1, 3, 100, 16, 8, 5, 4, tc.TC_F32),
+                                          (1, 2, 300, 128, 128, 0, 2, tc.TC_BF16)]:
+        p = min(pos0, W)
+        tail = 3 * up(B * H * (T + p) * D * es) + up(B * H * T * D * 4) + up(B * H * D * D * 4)
+        fwd = tc.tc_continue_workspace_size(tc.make_shape(B, H, T, D, W, 64, 0.0, dt), pos0) - tail
+        assert fwd > 0 and fwd % 256 == 0
+        assert fwd <= tc.tc_forward_workspace_size(tc.make_shape(B, H, T + p, D, W, 64, 0.0, dt))
+        if p == 0:  # nothing skipped: exactly the forward's workspace
+            assert fwd == tc.tc_forward_workspace_size(tc.make_shape(B, H, T, D, W, 64, 0.0, dt))
+
+
 def test_decode_validation():
     L = tc.lib()
 
