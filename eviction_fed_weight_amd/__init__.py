@@ -1,14 +1,16 @@
 """Python binding of the TC C ABI (include/tc.h) -- argument marshalling only.
 
 Every step of the layer runs in the HIP kernels of ``libtc.so``; this module
-only checks tensor metadata, allocates outputs/workspaces with torch (device
-memory plumbing) and passes raw device pointers plus the current HIP stream.
+only checks tensor metadata against the documented layouts (shape, dtype,
+device, contiguity: the library receives bare pointers and cannot check
+sizes), allocates outputs/workspaces with torch (device memory plumbing) and
+passes raw device pointers plus the current HIP stream.
 If the library has not been built it raises; there is no fallback.
 
 Entry points mirror the C names: ``tc_forward``, ``tc_decode_step``,
 ``tc_forward_continue``, ``tc_backward``, ``tc_forward_workspace_size``,
 ``tc_continue_workspace_size``, ``tc_backward_workspace_size``,
-``tc_status_string``.
+``tc_forward_status``, ``tc_status_string``.
 """
 from __future__ import annotations
 
@@ -18,7 +20,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtc.so")
 
-TC_OK, TC_ERR_INVALID_ARGUMENT, TC_ERR_UNSUPPORTED, TC_ERR_WORKSPACE, TC_ERR_HIP = range(5)
+TC_OK, TC_ERR_INVALID_ARGUMENT, TC_ERR_UNSUPPORTED, TC_ERR_WORKSPACE, TC_ERR_HIP, TC_ERR_STATE_EXCHANGE = range(6)
 TC_F32, TC_BF16 = 0, 1
 
 
@@ -63,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.tc_continue_workspace_size.restype = _sz
         L.tc_forward_continue.argtypes = [ctypes.POINTER(Shape), ctypes.c_int64] + [_vp] * 13 + [_sz, _vp]
         L.tc_forward_continue.restype = ctypes.c_int
+        L.tc_forward_status.argtypes = [ctypes.POINTER(Shape), ctypes.c_int64, _vp, _sz, _vp]
+        L.tc_forward_status.restype = ctypes.c_int
         L.tc_backward.argtypes = [ctypes.POINTER(Shape)] + [_vp] * 16 + [_sz, _vp]
         L.tc_backward.restype = ctypes.c_int
         L.tc_status_string.argtypes = [ctypes.c_int]
@@ -105,6 +109,32 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _want(t, name, shape, dtype, device=None):
+    """Check one tensor argument against the layout the C ABI documents for
+    it (the library receives bare pointers and cannot check sizes itself):
+    exact shape, element type, contiguity and, once the first tensor's
+    device is known, the same device.  Raises ValueError naming the tensor."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError("%s: shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s: dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s: must be contiguous" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s: on %s, expected %s (the device of q)" % (name, t.device, device))
+
+
+def _want_params(H, dev, **params):
+    """lambda, eta, gate: float32 vectors of H elements."""
+    torch = _torch()
+    for name, t in params.items():
+        if t is None:
+            raise ValueError("%s is required" % name)
+        _want(t, name, (H,), torch.float32, dev)
+
+
 def _stream(device=None):
     torch = _torch()
     return torch.cuda.current_stream(device).cuda_stream
@@ -128,6 +158,8 @@ def _workspace(nbytes, device, ws):
         return None, 0
     if ws is None:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.device != device or not ws.is_contiguous():
+        raise ValueError("ws: must be a contiguous tensor on %s" % device)
     if ws.numel() * ws.element_size() < nbytes:
         raise ValueError("workspace too small: %d < %d bytes" % (ws.numel() * ws.element_size(), nbytes))
     return ws, ws.numel() * ws.element_size()
@@ -139,9 +171,16 @@ def tc_forward(q, k, v, lam, eta, gate, W: int, C: int = 64, scale: float = 0.0,
     """Prefill/training forward.  q, k, v: [B,H,T,D] (bf16 or fp32, CUDA);
     lam, eta, gate: [H] float32.  Returns (y, A_final or None, lse or None)."""
     torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q: expected [B,H,T,D], got shape %s" % (tuple(q.shape),))
     B, H, T, D = q.shape
     shape = make_shape(B, H, T, D, W, C, scale, _dtype_code(q))
     dev = q.device
+    for name, t in (("k", k), ("v", v), ("y", y)):
+        _want(t, name, q.shape, q.dtype, dev)
+    _want_params(H, dev, lam=lam, eta=eta, gate=gate)
+    _want(A_final, "A_final", (B, H, D, D), torch.float32, dev)
+    _want(lse, "lse", (B, H, T), torch.float32, dev)
     if y is None:
         y = torch.empty_like(q)
     if want_state and A_final is None:
@@ -163,9 +202,21 @@ def tc_decode_step(q, k, v, k_ring, v_ring, A, pos, lam, eta, gate, scale: float
     (updated in place); A [S,H,D,D] float32 (in place); pos [S] int64 (+1).
     Returns y [S,H,D]."""
     torch = _torch()
+    if q.dim() != 3:
+        raise ValueError("q: expected [S,H,D], got shape %s" % (tuple(q.shape),))
+    if k_ring.dim() != 4:
+        raise ValueError("k_ring: expected [S,H,W,D], got shape %s" % (tuple(k_ring.shape),))
     S, H, D = q.shape
     W = k_ring.shape[2]
     shape = DecodeShape(S, H, D, W, float(scale), _dtype_code(q))
+    dv = q.device
+    for name, t in (("k", k), ("v", v), ("y", y)):
+        _want(t, name, q.shape, q.dtype, dv)
+    _want(k_ring, "k_ring", (S, H, W, D), q.dtype, dv)
+    _want(v_ring, "v_ring", (S, H, W, D), q.dtype, dv)
+    _want(A, "A", (S, H, D, D), torch.float32, dv)
+    _want(pos, "pos", (S,), torch.int64, dv)
+    _want_params(H, dv, lam=lam, eta=eta, gate=gate)
     if y is None:
         y = torch.empty_like(q)
     st = lib().tc_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(k_ring),
@@ -187,10 +238,22 @@ def tc_forward_continue(q, k, v, lam, eta, gate, k_ring, v_ring, A, pos0: int, *
     in place (the decode layout with S = B); pos ([B] int64, optional) is set
     to pos0 + T.  Returns (y, lse or None)."""
     torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q: expected [B,H,T,D], got shape %s" % (tuple(q.shape),))
+    if k_ring.dim() != 4:
+        raise ValueError("k_ring: expected [B,H,W,D], got shape %s" % (tuple(k_ring.shape),))
     B, H, T, D = q.shape
     W = k_ring.shape[2]
     shape = make_shape(B, H, T, D, W, C, scale, _dtype_code(q))
     dev = q.device
+    for name, t in (("k", k), ("v", v), ("y", y)):
+        _want(t, name, q.shape, q.dtype, dev)
+    _want(k_ring, "k_ring", (B, H, W, D), q.dtype, dev)
+    _want(v_ring, "v_ring", (B, H, W, D), q.dtype, dev)
+    _want(A, "A", (B, H, D, D), torch.float32, dev)
+    _want(pos, "pos", (B,), torch.int64, dev)
+    _want(lse, "lse", (B, H, T), torch.float32, dev)
+    _want_params(H, dev, lam=lam, eta=eta, gate=gate)
     if y is None:
         y = torch.empty_like(q)
     if want_lse and lse is None:
@@ -206,13 +269,32 @@ def tc_forward_continue(q, k, v, lam, eta, gate, k_ring, v_ring, A, pos0: int, *
     return y, (lse if want_lse else None)
 
 
+def tc_forward_status(shape: Shape, ws, pos0: int = 0) -> int:
+    """Status of the last forward call (tc_forward: pos0 = 0, or
+    tc_forward_continue with its pos0) that used workspace ``ws`` (a torch
+    tensor or None): TC_OK, or TC_ERR_STATE_EXCHANGE when one of its flag
+    waits ran out.  Synchronises the current stream."""
+    p = _ptr(ws) if ws is not None else None
+    n = ws.numel() * ws.element_size() if ws is not None else 0
+    dev = ws.device if ws is not None else None
+    return int(lib().tc_forward_status(ctypes.byref(shape), int(pos0), p, n, _stream(dev)))
+
+
 def tc_backward(q, k, v, y, dy, lse, lam, eta, gate, W: int, C: int = 64, scale: float = 0.0, *,
                 dq=None, dk=None, dv=None, ws=None):
     """Gradients of sum <dy, y>.  Returns dq, dk, dv, dlam, deta, dgate."""
     torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q: expected [B,H,T,D], got shape %s" % (tuple(q.shape),))
     B, H, T, D = q.shape
     shape = make_shape(B, H, T, D, W, C, scale, _dtype_code(q))
     dev = q.device
+    for name, t in (("k", k), ("v", v), ("y", y), ("dy", dy), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _want(t, name, q.shape, q.dtype, dev)
+    if y is None or dy is None or lse is None:
+        raise ValueError("y, dy and lse are required")
+    _want(lse, "lse", (B, H, T), torch.float32, dev)
+    _want_params(H, dev, lam=lam, eta=eta, gate=gate)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv

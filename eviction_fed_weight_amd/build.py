@@ -22,7 +22,9 @@ LIB = os.path.join(HERE, "libtc.so")
 # (source, object name, extra flags)
 UNITS = [
     ("tc_api.hip", "tc_api", []),
-    ("tc_forward.hip", "tc_forward", []),
+    ("tc_forward.hip", "tc_forward_bf16", ["-DTC_FWD_F32=0"]),
+    # float32 forward: matrix-core results kept in VGPRs (no AGPR accumulators)
+    ("tc_forward.hip", "tc_forward_f32", ["-DTC_FWD_F32=1", "-mllvm", "-amdgpu-mfma-vgpr-form"]),
     ("tc_fwd_rows.hip", "tc_fwd_rows", []),
     ("tc_decode.hip", "tc_decode", []),
     ("tc_continue.hip", "tc_continue", []),

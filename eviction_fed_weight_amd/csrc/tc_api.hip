@@ -1,11 +1,13 @@
 // C ABI of the TC layer: host-side validation, workspace planning and
-// dispatch to the gfx950 kernels.  No allocation and no synchronisation;
-// the only global state is a call counter (the forward's flag values) and,
-// in the rows launcher, a per-device count of resident workgroups.
+// dispatch to the gfx950 kernels.  No device allocation and no
+// synchronisation (except in the explicit status query); the only global
+// state is a call counter (the forward's flag values) and, in the rows
+// launcher, a per-device count of resident workgroups.
 #include <math.h>
 
 #include <atomic>
 #include <random>
+#include <vector>
 #include <stdint.h>
 #include <string.h>
 
@@ -17,9 +19,9 @@ namespace {
 constexpr int kBlock = 64;  // backward: query rows per block = tokens per scan chunk
 
 // Query rows per block of the forward kernels: 128 (four waves of 32 rows)
-// for bf16 with D <= 64, else 64 (four waves of 16 rows).  The float32 path keeps the 64-row kernel: it runs at two
-// workgroups per compute unit with every accumulator in VGPRs (see the
-// 16x16x4 float32 note in tc_forward.hip).
+// for bf16 with D <= 64, else 64 (four waves of 16 rows).  float32 inputs
+// run on the 64-row kernel, whose float32 build keeps every matrix-core
+// result in VGPRs (see the 16x16x4 float32 note in tc_forward.hip).
 int fwd_block(int D, int32_t dtype) { return (D <= 64 && dtype == TC_BF16) ? 128 : 64; }
 
 bool supported_d(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
@@ -94,10 +96,12 @@ Plan plan_for(const tc_shape_t& s, int row0 = 0) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Forward workspace: the segment states, then one 64-bit flag per segment.
+// Forward workspace: the segment states, then one 64-bit flag per segment,
+// then one 64-bit status word per workgroup (one workgroup per segment).
 size_t fwd_flags_bytes(const tc_shape_t& s, const Plan& p) {
   return align256((size_t)s.B * s.H * p.nseg * sizeof(unsigned long long));
 }
+size_t fwd_ws_bytes(const tc_shape_t& s, const Plan& p) { return align256(p.state_bytes) + 2 * fwd_flags_bytes(s, p); }
 
 // Flag value of one forward call: a per-process random salt combined with a
 // call counter, so that flags left in a reused workspace by earlier calls,
@@ -143,6 +147,7 @@ tc_status_t launch_fwd(const tc_shape_t& s, const Plan& p, const void* q, const 
   a.lse = lse;
   a.seg_state = (float*)ws;
   a.flags = ws && ws_ok ? (unsigned long long*)((char*)ws + align256(p.state_bytes)) : nullptr;
+  a.status = a.flags ? (unsigned long long*)((char*)a.flags + fwd_flags_bytes(s, p)) : nullptr;
   a.gen = next_generation();
   a.B = s.B;
   a.H = s.H;
@@ -188,7 +193,7 @@ tc_status_t cont_plan_for(const tc_shape_t* s, int64_t pos0, ContPlan& c) {
   const size_t es = elem_size(s->dtype);
   const size_t nx = align256((size_t)BH * c.x.T * s->D * es);
   c.off_fwd = 0;
-  c.off_q = align256(c.fp.state_bytes) + fwd_flags_bytes(c.x, c.fp);
+  c.off_q = fwd_ws_bytes(c.x, c.fp);
   c.off_k = c.off_q + nx;
   c.off_v = c.off_k + nx;
   c.off_yinit = c.off_v + nx;
@@ -202,12 +207,18 @@ tc_status_t cont_plan_for(const tc_shape_t* s, int64_t pos0, ContPlan& c) {
 extern "C" {
 
 const char* tc_status_string(tc_status_t st) {
-  switch (st) {
+  // (read as an int: callers from other languages may pass any integer, and
+  // loading an out-of-range value as the enum type is undefined in C++)
+  int v = 0;
+  static_assert(sizeof(st) == sizeof(v), "tc_status_t is int-sized");
+  memcpy(&v, &st, sizeof(v));
+  switch (v) {
     case TC_OK: return "ok";
     case TC_ERR_INVALID_ARGUMENT: return "invalid argument";
     case TC_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case TC_ERR_WORKSPACE: return "workspace missing or too small";
     case TC_ERR_HIP: return "HIP launch failed";
+    case TC_ERR_STATE_EXCHANGE: return "a wait for another workgroup's state ran out (outputs hold NaN)";
   }
   return "unknown status";
 }
@@ -216,8 +227,7 @@ const char* tc_version(void) { return "0.1.0"; }
 
 size_t tc_forward_workspace_size(const tc_shape_t* s) {
   if (check_shape(s) != TC_OK) return 0;
-  const Plan p = plan_for(*s);
-  return align256(p.state_bytes) + fwd_flags_bytes(*s, p);
+  return fwd_ws_bytes(*s, plan_for(*s));
 }
 
 tc_status_t tc_forward(const tc_shape_t* s, const void* q, const void* k, const void* v,
@@ -241,7 +251,7 @@ tc_status_t tc_forward(const tc_shape_t* s, const void* q, const void* k, const 
       if (overlap(outs[o], outsz[o], outs[p], outsz[p])) return TC_ERR_INVALID_ARGUMENT;
   }
   const Plan p = plan_for(*s);
-  const size_t need = align256(p.state_bytes) + fwd_flags_bytes(*s, p);
+  const size_t need = fwd_ws_bytes(*s, p);
   if (p.nseg > 1 && (!ws || ws_bytes < need)) return TC_ERR_WORKSPACE;
   if (ws && ws_bytes >= need) {
     for (int o = 0; o < 3; ++o)
@@ -257,6 +267,25 @@ size_t tc_continue_workspace_size(const tc_shape_t* s, int64_t pos0) {
   ContPlan c;
   if (cont_plan_for(s, pos0, c) != TC_OK) return 0;
   return c.total;
+}
+
+tc_status_t tc_forward_status(const tc_shape_t* s, int64_t pos0, const void* ws, size_t ws_bytes, void* stream) {
+  ContPlan c;
+  const tc_status_t st = cont_plan_for(s, pos0, c);
+  if (st != TC_OK) return st;
+  // the status words sit after the states and flags of the forward part
+  // (for pos0 = 0 this is exactly tc_forward's workspace layout)
+  const size_t n = (size_t)s->B * s->H * c.fp.nseg;
+  const size_t off = align256(c.fp.state_bytes) + fwd_flags_bytes(c.x, c.fp);
+  if (!ws) return c.fp.nseg > 1 ? TC_ERR_WORKSPACE : TC_OK;  // one segment: no waits, no workspace needed
+  if (ws_bytes < off + n * sizeof(unsigned long long)) return TC_ERR_WORKSPACE;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TC_ERR_HIP;
+  std::vector<unsigned long long> w(n);
+  if (hipMemcpy(w.data(), (const char*)ws + off, n * sizeof(unsigned long long), hipMemcpyDeviceToHost) != hipSuccess)
+    return TC_ERR_HIP;
+  for (size_t i = 1; i < n; ++i)
+    if (w[i] != w[0]) return TC_ERR_STATE_EXCHANGE;
+  return TC_OK;
 }
 
 tc_status_t tc_forward_continue(const tc_shape_t* s, int64_t pos0, const void* q, const void* k, const void* v,

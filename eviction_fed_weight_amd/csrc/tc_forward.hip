@@ -21,6 +21,10 @@
 // (seg_state_kernel) and a short chain over segments (seg_chain_kernel).
 #include <type_traits>
 
+#ifndef TC_FWD_F32
+#error "compile with -DTC_FWD_F32=0 (bf16 kernels) or -DTC_FWD_F32=1 (float32 kernels)"
+#endif
+
 #include "tc_device.h"
 #include "tc_fwd_common.h"
 #include "tc_launch.h"
@@ -32,14 +36,17 @@ namespace tck {
 // transpose reads (ColFrag).  X (float rows x D) aliases the K/V tiles: it is
 // only live between the band loop and the store of the evicted chunk.
 //
-// bf16 with D = 128 keeps the D x D state in LDS as float S^T (row stride
-// LDSS, an odd number of 16-byte chunks: conflict-free 16-lane reads) instead
-// of in registers, which leaves the band loop without register spills; the
-// other instantiations keep it in MFMA accumulators (the float32 D = 128 state
-// would not fit in LDS beside the tiles).
+// With D = 128 the D x D state lives in LDS as float S^T (row stride LDSS,
+// an odd number of 16-byte chunks: conflict-free 16-lane reads) instead of in
+// registers, which leaves the band loop without register spills; with D <= 64
+// it is kept in MFMA accumulators.  For float32 with D = 128 the Q block is
+// staged in the K tile's buffer (QA: it is read into registers once per block,
+// before the first key tile is stored), so that the tiles and the float32
+// state fit in the 160 KB of LDS.
 template <class E, int D>
 struct FwdLds {
-  static constexpr bool LS = std::is_same<E, bf16>::value && D == 128;  // state in LDS
+  static constexpr bool LS = D == 128;                                  // state in LDS
+  static constexpr bool QA = LS && !std::is_same<E, bf16>::value;       // Q staged in the K buffer
   static constexpr int VE = 16 / sizeof(E);
   static constexpr int LDK = D + VE;  // row stride of K, V, Q tiles
   static constexpr int LDX = D + 4;
@@ -48,21 +55,22 @@ struct FwdLds {
   static constexpr int XB = 64 * LDX * 4;
   static constexpr int U = (LS || (2 * TILE) > XB) ? (2 * TILE) : XB;
   static constexpr int SB = LS ? D * LDSS * 4 : 0;
-  static constexpr int TOTAL = U + TILE + SB;  // + Q block (+ S^T)
+  static constexpr int TOTAL = U + (QA ? 0 : TILE) + SB;  // + Q block (+ S^T)
 };
 
 // ---------------------------------------------------------------------------
 // Note on float32 inputs.  On gfx950 a VALU read of a float32 16x16x4 MFMA
 // result needs 10 wait states, and a v_accvgpr_mov_b32 copy of it more than
-// 8 (measured).  Where a kernel runs at one workgroup per compute unit the
+// 8 (measured).  Where a kernel may use more than 256 registers per lane the
 // compiler keeps accumulators in AGPRs and, at some control-flow joins, copies
-// them with v_accvgpr_mov_b32 too soon, which reads a stale element.  This
-// kernel at two workgroups per unit (D <= 64) keeps every accumulator in
-// VGPRs, so the library runs float32 inputs of D <= 64 here.
+// them with v_accvgpr_mov_b32 too soon, which reads a stale element.  Every
+// float32 instantiation is therefore bounded to 256 registers (the launch
+// bound of two workgroups per unit; with D = 128 the LDS still holds only
+// one), which keeps every accumulator in VGPRs and uses no AGPR at all.
 //
 // Fused forward: grid = BH * nseg, 256 threads (4 waves x 16 query rows).
 template <class E, int D>
-__global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a) {
   using M = Mfma<E>;
   using frag = typename M::frag;
   using L = FwdLds<E, D>;
@@ -73,9 +81,9 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
   E* Ks = (E*)smem;
   E* Vs = (E*)(smem + L::TILE);
   float* X = (float*)smem;
-  E* Qs = (E*)(smem + L::U);
-  float* Sl = (float*)(smem + L::U + L::TILE);  // (LS only)
-  constexpr bool LS = L::LS;
+  constexpr bool LS = L::LS, QA = L::QA;
+  E* Qs = QA ? Ks : (E*)(smem + L::U);
+  float* Sl = (float*)(smem + L::U + (QA ? 0 : L::TILE));  // (LS only)
   constexpr int LDSS = L::LDSS;
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
@@ -108,10 +116,17 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
   const int jb = seg_first_block(a, seg);
   const int je = seg_first_block(a, seg + 1);
   const int r = wid * 16 + l16;  // this lane's row within the block
+  if (a.status && tid == 0) a.status[blockIdx.x] = a.gen;  // (no flag waits in this kernel)
   TileRegs<E, D, 64> ql, kl, vl;
-  ql.load(Qg, jb * 64);
-  kl.load(Kg, (max(0, jb * 64 - W + 1) >> 6) * 64);
-  vl.load(Vg, (max(0, jb * 64 - W + 1) >> 6) * 64);
+  if (!QA) ql.load(Qg, jb * 64);
+  // Tiles are loaded one item ahead (in flight while the current one is
+  // computed), except for float32 with D = 128 (QA), where the staging
+  // registers of a prefetch would push the kernel past 256 registers: there
+  // each tile is loaded right before it is stored.
+  if (!QA) {
+    kl.load(Kg, (max(0, jb * 64 - W + 1) >> 6) * 64);
+    vl.load(Vg, (max(0, jb * 64 - W + 1) >> 6) * 64);
+  }
   for (int j = jb; j < je; ++j) {
     const int t0 = j * 64;
     const int trow = t0 + r;
@@ -120,8 +135,9 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
     const bool more = j + 1 < je;
     const int next_k0 = (max(0, t0 + 64 - W + 1) >> 6) * 64;
     __syncthreads();
+    if (QA) ql.load(Qg, t0);  // (float32 D = 128: no registers to spare for a prefetch)
     ql.store(Qs, LDK);
-    ql.load(Qg, t0 + 64);  // next block's queries, in flight during this block
+    if (!QA) ql.load(Qg, t0 + 64);  // next block's queries, in flight during this block
     __syncthreads();
     frag qf[NKC];
 #pragma unroll
@@ -138,11 +154,15 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
     const int kt_hi = min(T - 1, t0 + 63) >> 6;
     for (int kt = kt_lo; kt <= kt_hi; ++kt) {
       const int k0 = kt * 64;
-      if (kt > kt_lo) __syncthreads();
+      if (kt > kt_lo || QA) __syncthreads();  // (QA: every wave has read its Q rows from the K buffer)
+      if (QA) {
+        kl.load(Kg, k0);
+        vl.load(Vg, k0);
+      }
       kl.store(Ks, LDK);
       vl.store(Vs, LDK);
       __syncthreads();
-      {
+      if (!QA) {
         // next tile of this block, else the evicted chunk, else the next block's first tile
         const int nr = (kt < kt_hi) ? k0 + 64 : (has_mem ? e0 : next_k0);
         kl.load(Kg, nr);
@@ -287,11 +307,17 @@ __global__ void __launch_bounds__(256, (D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a)
         __syncthreads();
       }
       // evicted chunk e0 .. e0+63 (prefetched during the last band tile)
+      if (QA) {
+        kl.load(Kg, e0);
+        vl.load(Vg, e0);
+      }
       kl.store(Ks, LDK);
       vl.store(Vs, LDK);
       __syncthreads();
-      kl.load(Kg, next_k0);
-      vl.load(Vg, next_k0);
+      if (!QA) {
+        kl.load(Kg, next_k0);
+        vl.load(Vg, next_k0);
+      }
       f32x4 Z[4];
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
@@ -364,8 +390,15 @@ static hipError_t launch_fwd_impl(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_forward(const FwdArgs& a, int D, bool is_bf16, hipStream_t s) {
-  if (is_bf16) return D == 128 ? launch_fwd_impl<bf16, 128>(a, s) : hipErrorInvalidValue;
+// This file is compiled twice: TC_FWD_F32=0 builds the bf16 D = 128 kernels
+// (default register form), TC_FWD_F32=1 the float32 kernels with matrix-core
+// results in VGPRs (-mllvm -amdgpu-mfma-vgpr-form): the float32 D = 128
+// kernel needs a few more than 256 registers, and in the default form the
+// compiler would then keep its accumulators in AGPRs (see the note on
+// float32 inputs above); in the VGPR form AGPRs hold only spilled integer
+// indices, never a matrix-core result.
+#if TC_FWD_F32
+hipError_t launch_forward_f32(const FwdArgs& a, int D, hipStream_t s) {
   switch (D) {
     case 16: return launch_fwd_impl<float, 16>(a, s);
     case 32: return launch_fwd_impl<float, 32>(a, s);
@@ -374,5 +407,10 @@ hipError_t launch_forward(const FwdArgs& a, int D, bool is_bf16, hipStream_t s) 
   }
   return hipErrorInvalidValue;
 }
+#else
+hipError_t launch_forward_bf16(const FwdArgs& a, int D, hipStream_t s) {
+  return D == 128 ? launch_fwd_impl<bf16, 128>(a, s) : hipErrorInvalidValue;
+}
+#endif
 
 }  // namespace tck

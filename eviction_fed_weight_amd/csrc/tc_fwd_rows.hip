@@ -317,6 +317,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   }
 
   int kv_used = 0;  // key/value items consumed (buffer parity)
+  bool timed_out = false;  // a flag wait of this workgroup ran out (uniform in the workgroup)
   const int rw = 32 * wid;  // first row of this wave within the block
   // (PUB: exactly one block per segment, so no loop for the compiler to hoist out of)
   for (int j = jb; j < (PUB ? jb + 1 : je); ++j) {
@@ -567,6 +568,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
         const bool ran_out = __syncthreads_or(!seen);
         state_gather_all(acc, pw[BM], slots, m_lo + 1, seg + 1, wid, lane);
         if (ran_out) state_fill(acc, __builtin_nanf(""));
+        timed_out = ran_out;
         state_to_lds_t<E, D, LDS>(acc, Sl, wid, l16, lg);
       }
       if (last && a.A_final) {
@@ -648,6 +650,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
       for (int x = tid; x < D * D; x += NTH) Af[x] = has_mem ? eta * Sl[(x % D) * LDS + x / D] : 0.0f;
     }
   }
+  if (a.status && tid == 0) a.status[wg] = timed_out ? ~a.gen : a.gen;
   if (!PUB && seg == 0 && a.final_slot && a.A_final) {
     // A after step T-1 = eta (lambda^n S_last + L_final): S_last the state at
     // the last segment's start, L_final that segment's evictions (n of them)

@@ -39,6 +39,11 @@ struct FwdArgs {
   unsigned long long* flags;  // [B*H][nseg], in the workspace after the states
   unsigned long long gen;     // this call's flag value
   int max_polls;              // bound on the polls of one flag (0: no waiting at all)
+  // [B*H][nseg] (nullable), in the workspace after the flags: every
+  // workgroup of the call writes gen to its word, or ~gen when one of its
+  // flag waits ran out (its rows and the final state are then NaN).  The
+  // host reads them with tc_forward_status.
+  unsigned long long* status;
   // Output rows: query rows t >= row0 are stored at row t - row0 of y and lse
   // ([B,H,T-row0,...]); rows below row0 (a continuation's re-read prefix) are
   // computed but not stored.  yadd (nullable, float [B,H,T-row0,D]) is added
@@ -122,7 +127,11 @@ struct ContArgs {
 hipError_t launch_continue_prep(const ContArgs& a, hipStream_t s);    // extended sequence + initial-state read
 hipError_t launch_continue_finish(const ContArgs& a, hipStream_t s);  // A, ring and pos updates
 
-hipError_t launch_forward(const FwdArgs& a, int D, bool is_bf16, hipStream_t s);     // 64-row blocks: float32, and bf16 with D = 128
+hipError_t launch_forward_bf16(const FwdArgs& a, int D, hipStream_t s);  // 64-row blocks: bf16 with D = 128
+hipError_t launch_forward_f32(const FwdArgs& a, int D, hipStream_t s);   // 64-row blocks: float32
+inline hipError_t launch_forward(const FwdArgs& a, int D, bool is_bf16, hipStream_t s) {
+  return is_bf16 ? launch_forward_bf16(a, D, s) : launch_forward_f32(a, D, s);
+}
 hipError_t launch_forward_rows(const FwdArgs& a, int D, bool is_bf16, hipStream_t s);  // 128-row blocks: bf16 with D <= 64
 hipError_t launch_decode(const DecArgs& a, int D, bool is_bf16, hipStream_t s);
 hipError_t launch_backward_bf16(const BwdArgs& a, int D, hipStream_t s);

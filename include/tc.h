@@ -34,9 +34,13 @@
  *     returns TC_ERR_INVALID_ARGUMENT / TC_ERR_UNSUPPORTED / TC_ERR_WORKSPACE
  *     and writes nothing.  A failed kernel launch returns TC_ERR_HIP.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
- *     default stream).  Nothing synchronises.  The library keeps no global
- *     mutable state; calls on different streams with disjoint buffers may run
- *     concurrently.  Results are deterministic (no floating-point atomics).
+ *     default stream).  Nothing synchronises except tc_forward_status, which
+ *     is a query.  The library's only global mutable state is a call counter
+ *     (it makes each forward call's flag value unique) and a per-device cache
+ *     of how many forward workgroups the device holds at once; both are
+ *     updated atomically, so calls on different streams or host threads with
+ *     disjoint buffers may run concurrently.  Results are deterministic (no
+ *     floating-point atomics).
  */
 #ifndef TC_H_
 #define TC_H_
@@ -53,7 +57,10 @@ typedef enum {
   TC_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, aliased output */
   TC_ERR_UNSUPPORTED = 2,      /* head dim or dtype not built */
   TC_ERR_WORKSPACE = 3,        /* workspace missing or too small */
-  TC_ERR_HIP = 4               /* a HIP launch failed */
+  TC_ERR_HIP = 4,              /* a HIP launch (or the status query's copy) failed */
+  TC_ERR_STATE_EXCHANGE = 5    /* tc_forward_status: a wait for another workgroup's
+                                  segment state ran out; the affected rows and the
+                                  final state were written as NaN */
 } tc_status_t;
 
 typedef enum { TC_F32 = 0, TC_BF16 = 1 } tc_dtype_t;
@@ -78,11 +85,11 @@ typedef struct {
 
 /* Bytes of device workspace tc_forward / tc_backward need for `shape`
  * (0 if the shape is invalid).  The workspace holds the eviction-state
- * checkpoints of the scan, for the forward one 64-bit flag per segment and,
- * for the backward, per-row and per-block partial sums.  Its contents on
- * entry are ignored: a forward call waits only for a flag value of its own
- * (a per-process random salt combined with a call count), which stale
- * contents do not hold. */
+ * checkpoints of the scan, for the forward one 64-bit flag per segment and
+ * one 64-bit status word per workgroup and, for the backward, per-row and
+ * per-block partial sums.  Its contents on entry are ignored: a forward call
+ * waits only for a flag value of its own (a per-process random salt combined
+ * with a call count), which stale contents do not hold. */
 size_t tc_forward_workspace_size(const tc_shape_t* shape);
 size_t tc_backward_workspace_size(const tc_shape_t* shape);
 
@@ -103,9 +110,12 @@ size_t tc_backward_workspace_size(const tc_shape_t* shape);
  * per segment the workgroups of the launch hand segment states to each other
  * through flags in the workspace; a wait is bounded (environment variable
  * TC_FORWARD_MAX_POLLS, default 65536 polls) and one that runs out yields
- * NaN in the affected rows instead of a stale state.  A call made while its
- * stream is being captured into a HIP graph takes the path without flags
- * (a separate state pass), so graph replays stay correct.
+ * NaN in the affected rows instead of a stale state, and leaves a mark in
+ * the workspace that tc_forward_status reports.  (The waits are only for
+ * workgroups dispatched earlier, which wait for nothing later, so they end
+ * well inside the bound.)  A call made while its stream is being captured
+ * into a HIP graph takes the path without flags (a separate state pass), so
+ * graph replays stay correct.
  */
 tc_status_t tc_forward(const tc_shape_t* shape, const void* q, const void* k, const void* v,
                        const float* lambda, const float* eta, const float* gate, void* y,
@@ -166,6 +176,24 @@ tc_status_t tc_forward_continue(const tc_shape_t* shape, int64_t pos0, const voi
                                 const float* gate, void* k_ring, void* v_ring, float* A,
                                 int64_t* pos, void* y, float* lse, void* ws, size_t ws_bytes,
                                 void* stream);
+
+/*
+ * tc_forward_status -- whether every flag wait of the last forward call that
+ * used workspace `ws` completed (the state exchange of tc_forward, Section
+ * 3.2: each row must read the true state of all evictions before it).
+ *   shape, pos0   the call's shape; pos0 = 0 for tc_forward, the call's pos0
+ *                 for tc_forward_continue (its workspace holds a forward
+ *                 workspace of the extended sequence at offset 0).
+ *   ws, ws_bytes  that call's workspace.
+ * Synchronises `stream` (the call's stream), copies the per-workgroup status
+ * words to the host and returns TC_OK, or TC_ERR_STATE_EXCHANGE when a wait
+ * ran out (the call's NaN rows).  TC_OK as well when the shape needs no
+ * workspace (one segment per sequence: nothing to wait for).  Validation
+ * errors as for the call itself; TC_ERR_HIP if the synchronisation or the
+ * copy fails.  Calls that wrote the same workspace later overwrite the words.
+ */
+tc_status_t tc_forward_status(const tc_shape_t* shape, int64_t pos0, const void* ws, size_t ws_bytes,
+                              void* stream);
 
 /*
  * tc_backward -- gradients of L = sum_t <dy_t, y_t> through both levels and

@@ -29,8 +29,8 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(5):
-        assert tc.tc_status_string(s)
+    for s in range(6):
+        assert tc.tc_status_string(s) != "unknown status"
     assert tc.tc_status_string(99) == "unknown status"
 
 
@@ -81,12 +81,32 @@ def test_workspace_sizes():
 def test_forward_workspace_layout():
     """The forward workspace holds nseg + 1 float32 D x D state slots per (b,h)
     (segment states, and the last segment's local state) followed by one
-    64-bit flag per segment, each part rounded up to 256 bytes.  B=8 H=8
+    64-bit flag per segment and one 64-bit status word per workgroup (one
+    workgroup per segment), each part rounded up to 256 bytes.  B=8 H=8
     T=1024 D=64 runs as eight one-block (128-row) segments per head."""
     BH, nseg, D = 64, 8, 64
     states = BH * (nseg + 1) * D * D * 4
     flags = -(-BH * nseg * 8 // 256) * 256
-    assert tc.tc_forward_workspace_size(tc.make_shape(8, 8, 1024, 64, 256, 64)) == states + flags
+    assert tc.tc_forward_workspace_size(tc.make_shape(8, 8, 1024, 64, 256, 64)) == states + 2 * flags
+
+
+def test_forward_status_validation():
+    """tc_forward_status checks its arguments on the host first: a shape that
+    needs no workspace (one segment) reports TC_OK without one; a shape that
+    needs one reports a missing or short workspace; bad shapes and pos0 are
+    rejected.  (None of these touches a device.)"""
+    L = tc.lib()
+    one = tc.make_shape(1, 1, 100, 64, 32, 64)
+    assert tc.tc_forward_workspace_size(one) > 0
+    assert L.tc_forward_status(ctypes.byref(one), 0, None, 0, None) == tc.TC_OK
+    big = tc.make_shape(8, 8, 1024, 64, 256, 64)
+    need = tc.tc_forward_workspace_size(big)
+    assert L.tc_forward_status(ctypes.byref(big), 0, None, 0, None) == tc.TC_ERR_WORKSPACE
+    assert L.tc_forward_status(ctypes.byref(big), 0, FAKE, need - 1, None) == tc.TC_ERR_WORKSPACE
+    assert L.tc_forward_status(ctypes.byref(big), -1, FAKE, need, None) == tc.TC_ERR_INVALID_ARGUMENT
+    assert L.tc_forward_status(ctypes.byref(tc.make_shape(1, 1, 64, 48, 8, 8)), 0, FAKE, need, None) \
+        == tc.TC_ERR_UNSUPPORTED
+    assert L.tc_forward_status(None, 0, FAKE, need, None) == tc.TC_ERR_INVALID_ARGUMENT
 
 
 def test_continue_workspace_layout():
@@ -175,3 +195,49 @@ def test_binding_refuses_host_tensors():
     q = torch.zeros(1, 1, 8, 16)
     with pytest.raises(ValueError):
         tc.tc_forward(q, q, q, torch.zeros(1), torch.zeros(1), torch.zeros(1), 4)
+
+
+def test_binding_checks_layouts_before_the_library():
+    """The binding compares every tensor with the layout include/tc.h
+    documents for it (the C ABI only sees pointers, so a short output or a
+    wrong element type would be written out of bounds): wrong shapes, dtypes
+    and lengths raise ValueError naming the tensor, before any device check."""
+    torch = pytest.importorskip("torch")
+    bf, f32 = torch.bfloat16, torch.float32
+    q = torch.zeros(1, 2, 8, 16, dtype=bf)
+    p = torch.zeros(2)
+
+    def raises(fn, name):
+        with pytest.raises(ValueError) as e:
+            fn()
+        assert str(e.value).startswith(name), (name, str(e.value))
+
+    # forward: short y, bf16 A_final, lse of the wrong length, lam of the wrong length or dtype, k of another dtype
+    raises(lambda: tc.tc_forward(q, q, q, p, p, p, 4, y=torch.zeros(1, 2, 7, 16, dtype=bf)), "y")
+    raises(lambda: tc.tc_forward(q, q, q, p, p, p, 4, A_final=torch.zeros(1, 2, 16, 16, dtype=bf)), "A_final")
+    raises(lambda: tc.tc_forward(q, q, q, p, p, p, 4, lse=torch.zeros(1, 2, 9)), "lse")
+    raises(lambda: tc.tc_forward(q, q, q, torch.zeros(3), p, p, 4), "lam")
+    raises(lambda: tc.tc_forward(q, q, q, p, p, torch.zeros(2, dtype=torch.float64), 4), "gate")
+    raises(lambda: tc.tc_forward(q, q.float(), q, p, p, p, 4), "k")
+    # decode: int32 pos, bf16 A, ring of another width than q
+    S, H, W, D = 2, 2, 8, 16
+    qd = torch.zeros(S, H, D, dtype=bf)
+    ring = torch.zeros(S, H, W, D, dtype=bf)
+    A = torch.zeros(S, H, D, D)
+    pos = torch.zeros(S, dtype=torch.int64)
+    raises(lambda: tc.tc_decode_step(qd, qd, qd, ring, ring, A, pos.int(), p, p, p), "pos")
+    raises(lambda: tc.tc_decode_step(qd, qd, qd, ring, ring, A.to(bf), pos, p, p, p), "A")
+    raises(lambda: tc.tc_decode_step(qd, qd, qd, ring, torch.zeros(S, H, W, 32, dtype=bf), A, pos, p, p, p),
+           "v_ring")
+    raises(lambda: tc.tc_decode_step(qd, qd, qd, ring, ring, A, pos, p, p, p, y=torch.zeros(S, H, D, dtype=f32)),
+           "y")
+    # continuation: memory of another batch, pos as int32
+    raises(lambda: tc.tc_forward_continue(q, q, q, p, p, p, torch.zeros(1, 2, W, 16, dtype=bf),
+                                          torch.zeros(1, 2, W, 16, dtype=bf), torch.zeros(2, 2, 16, 16), 0), "A")
+    raises(lambda: tc.tc_forward_continue(q, q, q, p, p, p, torch.zeros(1, 2, W, 16, dtype=bf),
+                                          torch.zeros(1, 2, W, 16, dtype=bf), torch.zeros(1, 2, 16, 16), 0,
+                                          pos=torch.zeros(1, dtype=torch.int32)), "pos")
+    # backward: lse of the wrong dtype, short dq
+    lse = torch.zeros(1, 2, 8)
+    raises(lambda: tc.tc_backward(q, q, q, q, q, lse.double(), p, p, p, 4), "lse")
+    raises(lambda: tc.tc_backward(q, q, q, q, q, lse, p, p, p, 4, dq=torch.zeros(1, 2, 8, 8, dtype=bf)), "dq")
