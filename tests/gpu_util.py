@@ -3,8 +3,20 @@ import numpy as np
 import torch
 
 # Parity bars: relative L2 error against the float64 oracle run on the same
-# (bf16-rounded) inputs.
+# (bf16-rounded) inputs, over the whole tensor ...
 TOL = {"f32": 1e-5, "bf16": 5e-3}
+# ... and, for every tensor of per-token rows, the worst single row: max over
+# rows of ||row - ref row|| / ||ref row||.  A correct bf16 row carries the
+# bf16 rounding of its output (about 1.1e-3 relative rms, the largest of
+# thousands of 64-element rows about 2.5e-3) and of the probabilities; a row
+# off by 2 % or more is a fault the whole-tensor norm can hide at 10^5-10^6
+# rows (one wholly wrong row in 524,288 moves it by 1.4e-3).
+ROWTOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def bar(key: str, dtype: str) -> float:
+    """The bar of an error entry: keys ending in "_row" are worst-row errors."""
+    return ROWTOL[dtype] if key.endswith("_row") else TOL[dtype]
 
 
 def tdtype(dtype: str):
@@ -26,6 +38,34 @@ def rel(a, b) -> float:
     if nb == 0:
         return float(np.linalg.norm(a))
     return float(np.linalg.norm(a - b) / nb)
+
+
+def rowrel(a, b, per_element=False) -> float:
+    """Worst relative L2 error of one row (the last axis), or of one element
+    (per_element: for per-token scalars such as lse).  A reference row of
+    norm below 1e-3 times the median row norm is measured against that floor
+    instead of its own norm, so an all-zero row cannot divide by zero."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if per_element or a.ndim == 1:
+        a = a.reshape(-1, 1)
+        b = b.reshape(-1, 1)
+    else:
+        a = a.reshape(-1, a.shape[-1])
+        b = b.reshape(-1, b.shape[-1])
+    nb = np.linalg.norm(b, axis=1)
+    floor = 1e-3 * max(float(np.median(nb)), 1e-30)
+    return float(np.max(np.linalg.norm(a - b, axis=1) / np.maximum(nb, floor)))
+
+
+def errors(**pairs) -> dict:
+    """Whole-tensor and worst-row errors of (gpu, reference) pairs: name ->
+    rel, name_row -> rowrel ("lse" per element)."""
+    out = {}
+    for name, (a, b) in pairs.items():
+        out[name] = rel(a, b)
+        out[name + "_row"] = rowrel(a, b, per_element=(name == "lse"))
+    return out
 
 
 def say(*a):
