@@ -1,14 +1,18 @@
 """Benchmark of the TC layer hot path on one MI355X.
 
 Headline (the JSON line's "value"): prefill tokens/s of tc_forward on the
-training-shape workload B=8 H=8 D=64 T=1024 W=256 C=64 bf16 (B*T tokens per
-call, inputs resident in HBM).  The same line carries the decode rate of the
-serving workload (64 streams x 32 heads, D=128, W=4096: tc_decode_step calls
-per second), the long-context prefill and the backward, each with its
-roofline, plus the CPU oracle timed on the host.
+long-context workload B=1 H=12 D=64 T=32768 W=1024 C=128 bf16 (the largest
+prefill that one GPU holds; B*T tokens per call, inputs resident in HBM).
+The same line carries the training-shape prefill (B=8 H=8 T=1024), the
+decode rate of the serving workload (64 streams x 32 heads, D=128, W=4096:
+tc_decode_step calls per second), the backward and the training-shape
+forward, each with its roofline, plus the CPU oracle timed on the host on
+bounded samples of the same workloads.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
-                    [--legs prefill,decode,long,backward,train_forward,continue,capacity[,calib]]
+                    [--legs prefill,decode,backward,train_forward,continue,capacity[,calib]]
+
+The long-context prefill (the headline) always runs; --legs picks the others.
 """
 from __future__ import annotations
 
@@ -66,6 +70,21 @@ def measured_traffic():
         if key in kv:
             out[leg] = float(kv[key])
     return out
+
+
+def kernel_chunk(D, dtype="bf16"):
+    """Evictions per read chunk of the forward kernels: a query block of 128
+    rows (bf16, D <= 64) or 64 rows (otherwise) reads q S(e0) for the state
+    before the block's evicted chunk plus the decayed triangle over that
+    chunk, so the kernel's intra-chunk term is that of C = 128 or 64."""
+    return 128 if (dtype == "bf16" and D <= 64) else 64
+
+
+def roofline_chunk(C, D, dtype="bf16"):
+    """The chunk the algorithmic flops are charged with: the workload's C,
+    but never more than the kernel's read chunk (a larger C would charge
+    intra-chunk work the kernel does not do)."""
+    return min(C, kernel_chunk(D, dtype))
 
 
 def fwd_flops(B, H, T, D, W, C):
@@ -151,7 +170,7 @@ def prefill_leg(cfg_id, steps, warmup):
         tc.tc_forward(q, k, v, lam, eta, g, cfg.W, cfg.C, y=y, A_final=A, lse=lse, ws=ws)
 
     ms = time_calls(call, steps, warmup)
-    fl = fwd_flops(cfg.B, cfg.H, cfg.T, cfg.D, cfg.W, cfg.C)
+    fl = fwd_flops(cfg.B, cfg.H, cfg.T, cfg.D, cfg.W, roofline_chunk(cfg.C, cfg.D))
     by = fwd_bytes(cfg.B, cfg.H, cfg.T, cfg.D)
     tflops = fl / (ms * 1e-3) / 1e12
     cold = cold_ms(call, 20) if cfg_id in (2, 3) else None
@@ -208,7 +227,7 @@ def continue_leg(steps, warmup, chunk=4096):
                                    y=ys[i], lse=lses[i], ws=ws)
 
     ms = time_calls(call, steps, warmup)
-    fl = fwd_flops(B, H, T, D, W, cfg.C)
+    fl = fwd_flops(B, H, T, D, W, roofline_chunk(cfg.C, D))
     tflops = fl / (ms * 1e-3) / 1e12
     return dict(workload="chunked prefill B=%d H=%d D=%d T=%d W=%d C=%d bf16 in %d chunks of %d"
                 % (B, H, D, T, W, cfg.C, n, chunk),
@@ -329,7 +348,7 @@ def backward_leg(steps, warmup):
         tc.tc_backward(q, k, v, y, dy, lse, lam, eta, g, cfg.W, cfg.C, dq=dq, dk=dk, dv=dvv, ws=ws)
 
     ms = time_calls(call, steps, warmup)
-    fl = bwd_flops(cfg.B, cfg.H, cfg.T, cfg.D, cfg.W, cfg.C)
+    fl = bwd_flops(cfg.B, cfg.H, cfg.T, cfg.D, cfg.W, min(cfg.C, 64))
     tflops = fl / (ms * 1e-3) / 1e12
     return dict(workload="backward B=%d H=%d D=%d T=%d W=%d C=%d bf16" % (cfg.B, cfg.H, cfg.D, cfg.T, cfg.W, cfg.C),
                 ms_per_call=ms, tokens_per_s=cfg.B * cfg.T / (ms * 1e-3), flops=fl,
@@ -355,39 +374,112 @@ def calib_leg(steps, warmup, mib=256):
                 ms_per_call=ms, gbs=2 * n * 4 / (ms * 1e-3) / 1e9)
 
 
-def cpu_baseline(budget_s=12.0, max_runs=400):
-    """The oracle (unmodified) on the prefill workload, on the host cores."""
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _timed(fn, n=1):
+    """Median wall time of n runs of fn."""
+    import numpy as np
+
+    ts = []
+    for _ in range(n):
+        t = time.time()
+        fn()
+        ts.append(time.time() - t)
+    return float(np.median(ts))
+
+
+def cpu_baseline():
+    """The oracle (unmodified: the float64 per-token recurrence, OpenMP over
+    independent (b,h) or (stream, head) pairs) timed on the host cores on
+    bounded samples of the workloads, about 30 s in all; each rate is scaled
+    from its sample to the whole workload (the pairs are independent and
+    equal in work).  The headline entry is the long-context prefill."""
     import numpy as np
 
     import oracle
     import tc_inputs
 
-    cfg = tc_inputs.CONFIGS[2]
-    d = tc_inputs.prefill_inputs(2)
-    times = []
-    t_start = time.time()
-    while time.time() - t_start < budget_s and len(times) < max_runs:
-        t = time.time()
-        oracle.forward(d["q"], d["k"], d["v"], d["lam"], d["eta"], d["gate"], cfg.W)
-        times.append(time.time() - t)
-    sec = float(np.median(times))
     cores = oracle.num_threads()
-    # the same oracle on one thread, over one (b,h) sequence of the batch (scaled to the batch: the
-    # batch is 64 such independent sequences)
+    out = {}
+    # long-context prefill: all 12 heads on all cores; one head on one thread
+    c3 = tc_inputs.CONFIGS[3]
+    d = tc_inputs.prefill_inputs(3)
+    sec = _timed(lambda: oracle.forward(d["q"], d["k"], d["v"], d["lam"], d["eta"], d["gate"], c3.W))
     oracle.set_num_threads(1)
-    one = []
-    for _ in range(3):
-        t = time.time()
-        oracle.forward(d["q"][:1, :1], d["k"][:1, :1], d["v"][:1, :1], d["lam"][:1], d["eta"][:1], d["gate"][:1],
-                       cfg.W)
-        one.append(time.time() - t)
+    sec1 = _timed(lambda: oracle.forward(d["q"][:, :1], d["k"][:, :1], d["v"][:, :1], d["lam"][:1], d["eta"][:1],
+                                         d["gate"][:1], c3.W)) * c3.B * c3.H
     oracle.set_num_threads(cores)
-    sec1 = float(np.median(one)) * cfg.B * cfg.H
-    return dict(value=cfg.B * cfg.T / sec, unit="tokens/s", cores=cores, kind="oracle",
-                sample="full prefill batch (B=8 H=8 T=1024 W=256 D=64), float64 per-token recurrence, "
-                       "median of %d runs" % len(times), seconds_per_batch=sec,
-                single_thread=dict(value=cfg.B * cfg.T / sec1, unit="tokens/s", seconds_per_batch=sec1,
-                                   sample="one (b,h) sequence of the same batch on one thread, median of 3, x64"))
+    out["long_prefill"] = dict(value=c3.B * c3.T / sec, unit="tokens/s", seconds=sec,
+                               sample="the whole workload (B=1 H=12 T=32768 W=1024 D=64), one run",
+                               single_thread=dict(value=c3.B * c3.T / sec1, unit="tokens/s", seconds=sec1,
+                                                  sample="one head on one thread, x12"))
+    del d
+    # training-shape prefill: the whole batch, median of runs within 3 s; one (b,h) on one thread
+    c2 = tc_inputs.CONFIGS[2]
+    d = tc_inputs.prefill_inputs(2)
+    f2 = lambda: oracle.forward(d["q"], d["k"], d["v"], d["lam"], d["eta"], d["gate"], c2.W)  # noqa: E731
+    n2 = max(3, min(50, int(3.0 / max(_timed(f2), 1e-3))))
+    sec = _timed(f2, n2)
+    oracle.set_num_threads(1)
+    sec1 = _timed(lambda: oracle.forward(d["q"][:1, :1], d["k"][:1, :1], d["v"][:1, :1], d["lam"][:1], d["eta"][:1],
+                                         d["gate"][:1], c2.W), 3) * c2.B * c2.H
+    oracle.set_num_threads(cores)
+    out["prefill"] = dict(value=c2.B * c2.T / sec, unit="tokens/s", seconds=sec,
+                          sample="the whole batch (B=8 H=8 T=1024 W=256 D=64), median of %d runs" % n2,
+                          single_thread=dict(value=c2.B * c2.T / sec1, unit="tokens/s", seconds=sec1,
+                                             sample="one (b,h) sequence on one thread, median of 3, x64"))
+    # serving decode: 4 of the 64 streams (all 32 heads) for 256 consecutive steps on all cores;
+    # one stream for 8 steps on one thread
+    c4 = tc_inputs.CONFIGS[4]
+    lam, eta, g = tc_inputs.decode_params(4, c4.H)
+    ns, nsteps = 4, 256
+    ins = [tc_inputs.decode_stream_inputs(4, s, c4.H, c4.D, c4.W, 16, nsteps) for s in range(ns)]
+    kr = np.stack([x["ring_k"] for x in ins]).astype(np.float64)
+    vr = np.stack([x["ring_v"] for x in ins]).astype(np.float64)
+    A = np.zeros((ns, c4.H, c4.D, c4.D))
+    pos = np.full(ns, c4.prior + c4.W, np.int64)
+    qs, ks, vs = (np.stack([x[n] for x in ins], axis=1) for n in ("q", "k", "v"))
+
+    def dec(nst, ns_):
+        for t in range(nst):
+            oracle.decode_step(qs[t, :ns_], ks[t, :ns_], vs[t, :ns_], kr[:ns_], vr[:ns_], A[:ns_], pos[:ns_], lam, eta, g)
+
+    sec = _timed(lambda: dec(nsteps, ns)) / nsteps * (c4.S / ns)
+    oracle.set_num_threads(1)
+    sec1 = _timed(lambda: dec(8, 1)) / 8 * c4.S
+    oracle.set_num_threads(cores)
+    out["decode"] = dict(value=1.0 / sec, unit="steps/s", seconds_per_step=sec,
+                         sample="4 of the 64 streams (all 32 heads, W=4096 D=128) for 256 consecutive steps, "
+                                "scaled to 64 streams",
+                         single_thread=dict(value=1.0 / sec1, unit="steps/s", seconds_per_step=sec1,
+                                            sample="one stream for 8 steps on one thread, x64"))
+    del ins, kr, vr, A, qs, ks, vs
+    # training backward: one batch row (16 of the 64 (b,h) pairs) on all cores; one pair on one thread
+    c5 = tc_inputs.CONFIGS[5]
+    d = tc_inputs.prefill_inputs(5)
+    sl = lambda x, n: x[:1, :n]  # noqa: E731
+    sec = _timed(lambda: oracle.backward(sl(d["q"], c5.H), sl(d["k"], c5.H), sl(d["v"], c5.H), sl(d["dy"], c5.H),
+                                         d["lam"], d["eta"], d["gate"], c5.W)) * c5.B
+    oracle.set_num_threads(1)
+    sec1 = _timed(lambda: oracle.backward(sl(d["q"], 1), sl(d["k"], 1), sl(d["v"], 1), sl(d["dy"], 1), d["lam"][:1],
+                                          d["eta"][:1], d["gate"][:1], c5.W)) * c5.B * c5.H
+    oracle.set_num_threads(cores)
+    out["backward"] = dict(value=c5.B * c5.T / sec, unit="tokens/s", seconds=sec,
+                           sample="batch row 0 (16 of the 64 (b,h) pairs, T=8192 W=512 D=128) on all cores, x4",
+                           single_thread=dict(value=c5.B * c5.T / sec1, unit="tokens/s", seconds=sec1,
+                                              sample="one (b,h) pair on one thread, x64"))
+    head = out.pop("long_prefill")
+    return dict(value=head["value"], unit=head["unit"], cores=cores, kind="oracle", sample=head["sample"],
+                seconds=head["seconds"], single_thread=head["single_thread"], cpu_model=cpu_model(), legs=out)
 
 
 def main():
@@ -395,7 +487,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--legs", default="prefill,decode,long,backward,train_forward,continue,capacity")
+    ap.add_argument("--legs", default="prefill,decode,backward,train_forward,continue,capacity")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -406,36 +498,37 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     legs = args.legs.split(",")
-    log("prefill leg ...")
-    pre = prefill_leg(2, args.steps, args.warmup)
-    log("  prefill", json.dumps(pre))
+    log("long prefill leg (headline) ...")
+    lp = prefill_leg(3, args.steps, args.warmup)
+    log("  long", json.dumps(lp))
+    c3 = {"workload": lp["workload"], "B": 1, "H": 12, "D": 64, "T": 32768, "W": 1024, "C": 128}
     out = {
-        "metric": "TC-layer prefill tokens/s (training-shape prefill, tc_forward)",
-        "value": pre["tokens_per_s"],
+        "metric": "TC-layer prefill tokens/s (long-context prefill, tc_forward)",
+        "value": lp["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": pre["ms_per_call"],
+        "ms_per_step": lp["ms_per_call"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": pre["workload"], "B": 8, "H": 8, "D": 64, "T": 1024, "W": 256, "C": 64},
-        "roofline": pre["roofline"],
-        "cold": pre["cold"],
+        "config": c3,
+        "roofline": lp["roofline"],
+        "cold": lp["cold"],
     }
+    if "prefill" in legs:
+        log("training-shape prefill leg ...")
+        pre = prefill_leg(2, args.steps, args.warmup)
+        log("  prefill", json.dumps(pre))
+        out["prefill"] = pre
     if "decode" in legs:
         log("decode leg ...")
         dec = decode_leg(args.steps, args.warmup)
         log("  decode", json.dumps(dec))
         out["decode"] = dec
-    if "long" in legs:
-        log("long prefill leg ...")
-        lp = prefill_leg(3, max(3, args.steps // 5), 2)
-        log("  long", json.dumps(lp))
-        out["long_prefill"] = lp
     if "backward" in legs:
         log("backward leg ...")
         bw = backward_leg(max(3, args.steps // 5), 2)
