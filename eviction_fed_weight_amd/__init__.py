@@ -10,7 +10,7 @@ If the library has not been built it raises; there is no fallback.
 Entry points mirror the C names: ``tc_forward``, ``tc_decode_step``,
 ``tc_forward_continue``, ``tc_backward``, ``tc_forward_workspace_size``,
 ``tc_continue_workspace_size``, ``tc_backward_workspace_size``,
-``tc_forward_status``, ``tc_status_string``.
+``tc_forward_status``, ``tc_forward_noalloc``, ``tc_status_string``.
 """
 from __future__ import annotations
 
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.tc_continue_workspace_size.restype = _sz
         L.tc_forward_continue.argtypes = [ctypes.POINTER(Shape), ctypes.c_int64] + [_vp] * 13 + [_sz, _vp]
         L.tc_forward_continue.restype = ctypes.c_int
+        L.tc_forward_noalloc.argtypes = [ctypes.POINTER(Shape)] + [_vp] * 10
+        L.tc_forward_noalloc.restype = ctypes.c_int
         L.tc_forward_status.argtypes = [ctypes.POINTER(Shape), ctypes.c_int64, _vp, _sz, _vp]
         L.tc_forward_status.restype = ctypes.c_int
         L.tc_backward.argtypes = [ctypes.POINTER(Shape)] + [_vp] * 16 + [_sz, _vp]
@@ -195,6 +197,35 @@ def tc_forward(q, k, v, lam, eta, gate, W: int, C: int = 64, scale: float = 0.0,
     if st != TC_OK:
         raise TCError(st, "tc_forward")
     return y, (A_final if want_state else None), (lse if want_lse else None)
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # the static device scratch of tc_forward_noalloc
+
+
+def tc_forward_noalloc(q, k, v, lam, eta, gate, W: int, C: int = 64, scale: float = 0.0, *, y, A_final=None,
+                       lse=None):
+    """tc_forward without a workspace: the library uses its static 16 MiB
+    device scratch (no device allocation in the call).  The outputs are
+    passed in (y required; A_final and lse optional).  Returns (y, A_final,
+    lse)."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q: expected [B,H,T,D], got shape %s" % (tuple(q.shape),))
+    if y is None:
+        raise ValueError("y is required")
+    B, H, T, D = q.shape
+    shape = make_shape(B, H, T, D, W, C, scale, _dtype_code(q))
+    dev = q.device
+    for name, t in (("k", k), ("v", v), ("y", y)):
+        _want(t, name, q.shape, q.dtype, dev)
+    _want_params(H, dev, lam=lam, eta=eta, gate=gate)
+    _want(A_final, "A_final", (B, H, D, D), torch.float32, dev)
+    _want(lse, "lse", (B, H, T), torch.float32, dev)
+    st = lib().tc_forward_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(eta),
+                                  _ptr(gate), _ptr(y), _ptr(A_final), _ptr(lse), _stream(dev))
+    if st != TC_OK:
+        raise TCError(st, "tc_forward_noalloc")
+    return y, A_final, lse
 
 
 def tc_decode_step(q, k, v, k_ring, v_ring, A, pos, lam, eta, gate, scale: float = 0.0, *, y=None):

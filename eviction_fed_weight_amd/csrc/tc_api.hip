@@ -1,11 +1,13 @@
 // C ABI of the TC layer: host-side validation, workspace planning and
 // dispatch to the gfx950 kernels.  No device allocation and no
 // synchronisation (except in the explicit status query); the only global
-// state is a call counter (the forward's flag values) and, in the rows
-// launcher, a per-device count of resident workgroups.
+// state is a call counter (the forward's flag values), in the rows launcher
+// a per-device count of resident workgroups, and the per-device address of
+// the allocation-free forward's static scratch.
 #include <math.h>
 
 #include <atomic>
+#include <mutex>
 #include <random>
 #include <vector>
 #include <stdint.h>
@@ -13,6 +15,12 @@
 
 #include "../../include/tc.h"
 #include "tc_launch.h"
+
+constexpr size_t kScratchBytes = (size_t)16 << 20;  // 16 MiB per device
+constexpr int kMaxDevices = 64;
+
+// The allocation-free forward's workspace (see scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -167,6 +175,59 @@ tc_status_t launch_fwd(const tc_shape_t& s, const Plan& p, const void* q, const 
   return e == hipSuccess ? TC_OK : TC_ERR_HIP;
 }
 
+// Byte extents of tc_forward's buffers, in the order q, k, v, lambda, eta,
+// gate, y, A_final, lse (0 for a null optional output).
+struct FwdExtents {
+  size_t sz[9];
+};
+FwdExtents fwd_extents(const tc_shape_t& s, const float* A_final, const float* lse) {
+  const size_t n = (size_t)s.B * s.H * s.T * s.D * elem_size(s.dtype);
+  const size_t nh = (size_t)s.H * 4;
+  return FwdExtents{{n, n, n, nh, nh, nh, n, A_final ? (size_t)s.B * s.H * s.D * s.D * 4 : 0,
+                     lse ? (size_t)s.B * s.H * s.T * 4 : 0}};
+}
+
+// Argument checks of tc_forward and tc_forward_noalloc (everything but the
+// workspace): the shape, required pointers, and no output overlapping an
+// input or another output.
+tc_status_t check_fwd_args(const tc_shape_t* s, const void* q, const void* k, const void* v, const float* lambda,
+                           const float* eta, const float* gate, const void* y, const float* A_final,
+                           const float* lse) {
+  const tc_status_t st = check_shape(s);
+  if (st != TC_OK) return st;
+  if (!q || !k || !v || !lambda || !eta || !gate || !y) return TC_ERR_INVALID_ARGUMENT;
+  const FwdExtents x = fwd_extents(*s, A_final, lse);
+  const void* bufs[9] = {q, k, v, lambda, eta, gate, y, A_final, lse};
+  for (int o = 6; o < 9; ++o) {
+    for (int i = 0; i < 6; ++i)
+      if (overlap(bufs[o], x.sz[o], bufs[i], x.sz[i])) return TC_ERR_INVALID_ARGUMENT;
+    for (int p = o + 1; p < 9; ++p)
+      if (overlap(bufs[o], x.sz[o], bufs[p], x.sz[p])) return TC_ERR_INVALID_ARGUMENT;
+  }
+  return TC_OK;
+}
+
+// Scratch of tc_forward_noalloc, for callers that cannot allocate: the
+// forward workspace of any shape that needs at most kScratchBytes, in the
+// device's own copy of `scratch`.  Host code never passes the array's name
+// to a kernel (on the host it names a stand-in, not device memory): it takes
+// the device address from hipGetSymbolAddress, once per device, with that
+// device current, and keeps it per device.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 // Continuation workspace: the forward's workspace for the extended shape,
 // the extended q/k/v, the initial-state read and the new evictions' state.
 struct ContPlan {
@@ -233,34 +294,31 @@ size_t tc_forward_workspace_size(const tc_shape_t* s) {
 tc_status_t tc_forward(const tc_shape_t* s, const void* q, const void* k, const void* v,
                        const float* lambda, const float* eta, const float* gate, void* y,
                        float* A_final, float* lse, void* ws, size_t ws_bytes, void* stream) {
-  const tc_status_t st = check_shape(s);
+  const tc_status_t st = check_fwd_args(s, q, k, v, lambda, eta, gate, y, A_final, lse);
   if (st != TC_OK) return st;
-  if (!q || !k || !v || !lambda || !eta || !gate || !y) return TC_ERR_INVALID_ARGUMENT;
-  const size_t n = (size_t)s->B * s->H * s->T * s->D * elem_size(s->dtype);
-  const size_t na = A_final ? (size_t)s->B * s->H * s->D * s->D * 4 : 0;
-  const size_t nl = lse ? (size_t)s->B * s->H * s->T * 4 : 0;
-  const size_t nh = (size_t)s->H * 4;
-  const void* ins[6] = {q, k, v, lambda, eta, gate};
-  const size_t insz[6] = {n, n, n, nh, nh, nh};
-  void* outs[3] = {y, A_final, lse};
-  const size_t outsz[3] = {n, na, nl};
-  for (int o = 0; o < 3; ++o) {
-    for (int i = 0; i < 6; ++i)
-      if (overlap(outs[o], outsz[o], ins[i], insz[i])) return TC_ERR_INVALID_ARGUMENT;
-    for (int p = o + 1; p < 3; ++p)
-      if (overlap(outs[o], outsz[o], outs[p], outsz[p])) return TC_ERR_INVALID_ARGUMENT;
-  }
   const Plan p = plan_for(*s);
   const size_t need = fwd_ws_bytes(*s, p);
   if (p.nseg > 1 && (!ws || ws_bytes < need)) return TC_ERR_WORKSPACE;
   if (ws && ws_bytes >= need) {
-    for (int o = 0; o < 3; ++o)
-      if (overlap(ws, need, outs[o], outsz[o])) return TC_ERR_INVALID_ARGUMENT;
-    for (int i = 0; i < 6; ++i)
-      if (overlap(ws, need, ins[i], insz[i])) return TC_ERR_INVALID_ARGUMENT;
+    const FwdExtents x = fwd_extents(*s, A_final, lse);
+    const void* bufs[9] = {q, k, v, lambda, eta, gate, y, A_final, lse};
+    for (int i = 0; i < 9; ++i)
+      if (overlap(ws, need, bufs[i], x.sz[i])) return TC_ERR_INVALID_ARGUMENT;
   }
   return launch_fwd(*s, p, q, k, v, lambda, eta, gate, y, A_final, lse, ws, ws_bytes >= need, 0, nullptr,
                     (hipStream_t)stream);
+}
+
+tc_status_t tc_forward_noalloc(const tc_shape_t* s, const void* q, const void* k, const void* v,
+                               const float* lambda, const float* eta, const float* gate, void* y,
+                               float* A_final, float* lse, void* stream) {
+  const tc_status_t st = check_fwd_args(s, q, k, v, lambda, eta, gate, y, A_final, lse);
+  if (st != TC_OK) return st;
+  const Plan p = plan_for(*s);
+  if (fwd_ws_bytes(*s, p) > kScratchBytes) return TC_ERR_WORKSPACE;
+  void* w = scratch_ptr();
+  if (!w) return TC_ERR_HIP;
+  return launch_fwd(*s, p, q, k, v, lambda, eta, gate, y, A_final, lse, w, true, 0, nullptr, (hipStream_t)stream);
 }
 
 size_t tc_continue_workspace_size(const tc_shape_t* s, int64_t pos0) {

@@ -122,6 +122,32 @@ tc_status_t tc_forward(const tc_shape_t* shape, const void* q, const void* k, co
                        float* A_final, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * tc_forward_noalloc -- tc_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and results.  Instead of a caller's workspace it uses a static
+ * device array of 16 MiB that the library holds on each GPU it runs on until
+ * the process ends; it calls no hipMalloc, hipFree or other allocating
+ * routine.  The array belongs to the current device (the stream must be one
+ * of its streams); its address is looked up once per device on the first
+ * call there.
+ *   Limit: the shape's forward workspace (tc_forward_workspace_size) must be
+ *   at most 16 MiB (16777216 bytes), else TC_ERR_WORKSPACE and nothing runs;
+ *   e.g. B=8 H=8 T=1024 D=64 needs 9.4 MB and B=1 H=12 T=32768 D=64 8.5 MB.
+ *   Every call on one GPU shares its array and leaves its contents there (no
+ *   part of it needs clearing: stale flags never match a later call's flag
+ *   value).  Calls that overlap in time on one GPU (other streams, other
+ *   host threads) race on it and must be serialised by the caller.
+ *   tc_forward_status cannot be queried for these calls; a flag wait that
+ *   ran out shows only as NaN rows.
+ * Other errors as for tc_forward; TC_ERR_HIP also when the array's device
+ * address cannot be looked up.
+ */
+tc_status_t tc_forward_noalloc(const tc_shape_t* shape, const void* q, const void* k, const void* v,
+                               const float* lambda, const float* eta, const float* gate, void* y,
+                               float* A_final, float* lse, void* stream);
+
+/*
  * tc_decode_step -- one streaming step (Figure 2, steps 1-5) for S streams.
  *   q, k, v  [S,H,D] dtype: the incoming token of every (stream, head).
  *   k_ring, v_ring [S,H,W,D] dtype, in/out: token t lives in slot t mod W.
