@@ -9,6 +9,8 @@ and never touches a GPU.
 Contents
   * ``forward``, ``decode_step``, ``backward`` -- the per-token recurrence in
     IEEE double (``tc_oracle.c``), OpenMP over independent (b,h) pairs.
+  * ``forward_chunk_mean`` -- the chunk-mean shortcut the exact scan
+    replaces (one mean write per chunk of C evicted pairs), for the ablation.
   * ``memory_f32_sequential`` / ``memory_f32_chunked`` -- float32 models of
     the memory path, per-token writes vs the chunked weighted-sum scan.
   * ``dense`` -- closed forms in numpy used to pin the oracle.
@@ -54,6 +56,7 @@ def _load():
         lib.tco_forward.argtypes = [_i] * 5 + [ctypes.c_double] + [_D] * 9
         lib.tco_decode_step.argtypes = [_i] * 4 + [ctypes.c_double] + [_D] * 6 + [_I64] + [_D] * 4
         lib.tco_backward.argtypes = [_i] * 5 + [ctypes.c_double] + [_D] * 13
+        lib.tco_forward_chunk_mean.argtypes = [_i] * 6 + [ctypes.c_double] + [_D] * 9
         lib.tco_memory_f32_sequential.argtypes = [_i] * 3 + [ctypes.c_float] * 2 + [_F] * 5
         lib.tco_memory_f32_chunked.argtypes = [_i] * 4 + [ctypes.c_float] * 2 + [_F] * 5
         lib.tco_num_threads.restype = ctypes.c_int
@@ -100,6 +103,25 @@ def forward(q, k, v, lam, eta, gate, W: int, scale: float | None = None, with_st
     lse = np.empty((B, H, T))
     _load().tco_forward(B, H, T, D, int(W), tau, _p(q), _p(k), _p(v), _p(lam), _p(eta),
                         _p(gate), _p(y), _p(A), _p(lse))
+    return y, A, lse
+
+
+def forward_chunk_mean(q, k, v, lam, eta, gate, W: int, C: int, scale: float | None = None):
+    """The chunk-mean shortcut's forward (what the exact scan replaces): one
+    write A <- lam A + eta kbar vbar^T per chunk of C evicted pairs; a query
+    whose evicted token lies in chunk n reads the memory after chunks
+    0 .. n-1.  q,k,v: [B,H,T,D].  Returns (y, A_final after every complete
+    chunk, lse) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, T, D = q.shape
+    lam, eta, gate = _f64(lam), _f64(eta), _f64(gate)
+    assert lam.shape == eta.shape == gate.shape == (H,) and int(C) >= 1
+    tau = default_scale(D) if scale is None else float(scale)
+    y = np.empty_like(q)
+    A = np.empty((B, H, D, D))
+    lse = np.empty((B, H, T))
+    _load().tco_forward_chunk_mean(B, H, T, D, int(W), int(C), tau, _p(q), _p(k), _p(v), _p(lam), _p(eta),
+                                   _p(gate), _p(y), _p(A), _p(lse))
     return y, A, lse
 
 

@@ -137,6 +137,98 @@ void tco_forward(int B, int H, int T, int D, int W, double tau,
 }
 
 /*
+ * The chunk-mean shortcut that the abstract and Section 1 (contributions) and
+ * Section 2 (training considerations) describe and that the parallel
+ * weighted-sum scan replaces: a chunked scan that summarises each chunk of C
+ * evicted pairs by its mean key and mean value and writes
+ *     A <- lambda A + eta (kbar outer vbar)
+ * once per chunk (lambda applied once per chunk).  The pages fix that write;
+ * they do not say what a query reads between two writes.  Reading taken
+ * (the inter-chunk state of a chunked scan): the evicted tokens form chunks
+ * n = tokens nC .. nC+C-1 in eviction order; a query at step t >= W, whose
+ * evicted token t-W lies in chunk n = (t-W)/C, reads the memory after the
+ * writes of chunks 0 .. n-1; a query at t < W reads nothing.  The write of
+ * chunk n is therefore made at the first step of chunk n+1, before its read,
+ * and the returned A_final is the memory after every complete chunk (the
+ * pairs of an incomplete last chunk are not written).  L1 is exactly as in
+ * forward_one.
+ */
+static void chunk_mean_forward_one(int T, int D, int W, int C, double tau, const double* q, const double* k,
+                                   const double* v, double lam, double eta, double g, double* y, double* A_out,
+                                   double* lse) {
+  const double sg = sigmoid(g);
+  double* A = (double*)calloc((size_t)D * D, sizeof(double));
+  double* ks = (double*)calloc((size_t)D, sizeof(double)); /* sums of the current chunk */
+  double* vs = (double*)calloc((size_t)D, sizeof(double));
+  double* z = (double*)malloc(sizeof(double) * (size_t)(W > 0 ? W : 1));
+  for (int t = 0; t < T; ++t) {
+    const double* qt = q + (size_t)t * D;
+    if (t >= W) {
+      const int e = t - W; /* the token leaving the window at this step */
+      if (e > 0 && e % C == 0) {
+        /* chunk e/C - 1 is complete: one write of its mean pair */
+        for (int a = 0; a < D; ++a)
+          for (int c = 0; c < D; ++c)
+            A[a * D + c] = lam * A[a * D + c] + eta * (ks[a] / C) * (vs[c] / C);
+        memset(ks, 0, sizeof(double) * (size_t)D);
+        memset(vs, 0, sizeof(double) * (size_t)D);
+      }
+      for (int a = 0; a < D; ++a) {
+        ks[a] += k[(size_t)e * D + a];
+        vs[a] += v[(size_t)e * D + a];
+      }
+    }
+    /* L1: exact softmax over the window {max(0,t-W+1) .. t} */
+    int lo = t - W + 1;
+    if (lo < 0) lo = 0;
+    double mu = -INFINITY;
+    for (int i = lo; i <= t; ++i) {
+      z[i - lo] = tau * dot(qt, k + (size_t)i * D, D);
+      if (z[i - lo] > mu) mu = z[i - lo];
+    }
+    double ell = 0.0;
+    for (int i = lo; i <= t; ++i) ell += exp(z[i - lo] - mu);
+    double* yt = y + (size_t)t * D;
+    for (int c = 0; c < D; ++c) yt[c] = 0.0;
+    for (int i = lo; i <= t; ++i) {
+      const double p = exp(z[i - lo] - mu) / ell;
+      const double* vi = v + (size_t)i * D;
+      for (int c = 0; c < D; ++c) yt[c] += p * vi[c];
+    }
+    if (lse) lse[t] = mu + log(ell);
+    /* L2: the read of the chunk writes made so far, fused through sigma(g) */
+    for (int c = 0; c < D; ++c) {
+      double m = 0.0;
+      for (int a = 0; a < D; ++a) m += qt[a] * A[a * D + c];
+      yt[c] += sg * m;
+    }
+  }
+  if (T > W && (T - W) % C == 0) {
+    /* the last chunk completed at the last step */
+    for (int a = 0; a < D; ++a)
+      for (int c = 0; c < D; ++c) A[a * D + c] = lam * A[a * D + c] + eta * (ks[a] / C) * (vs[c] / C);
+  }
+  if (A_out) memcpy(A_out, A, sizeof(double) * (size_t)D * D);
+  free(A);
+  free(ks);
+  free(vs);
+  free(z);
+}
+
+/* tco_forward_chunk_mean: the chunk-mean shortcut's forward, same layout as tco_forward. */
+void tco_forward_chunk_mean(int B, int H, int T, int D, int W, int C, double tau, const double* q, const double* k,
+                            const double* v, const double* lam, const double* eta, const double* gate, double* y,
+                            double* A_final, double* lse) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int bh = 0; bh < B * H; ++bh) {
+    const int h = bh % H;
+    const size_t off = (size_t)bh * T * D;
+    chunk_mean_forward_one(T, D, W, C, tau, q + off, k + off, v + off, lam[h], eta[h], gate[h], y + off,
+                           A_final ? A_final + (size_t)bh * D * D : 0, lse ? lse + (size_t)bh * T : 0);
+  }
+}
+
+/*
  * tco_decode_step: one streaming step (Figure 2, steps 1-5) for S streams x
  * H heads.  Ring slot of token t is t mod W; pos[s] is the index of the
  * incoming token of stream s.  While pos < W the slots pos+1..W-1 hold no

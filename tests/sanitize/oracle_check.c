@@ -20,6 +20,9 @@ void tco_decode_step(int S, int H, int D, int W, double tau, const double* q, co
 void tco_backward(int B, int H, int T, int D, int W, double tau, const double* q, const double* k, const double* v,
                   const double* dy, const double* lam, const double* eta, const double* gate, double* dq, double* dk,
                   double* dv, double* dlam, double* deta, double* dgate);
+void tco_forward_chunk_mean(int B, int H, int T, int D, int W, int C, double tau, const double* q, const double* k,
+                            const double* v, const double* lam, const double* eta, const double* gate, double* y,
+                            double* A_final, double* lse);
 void tco_memory_f32_sequential(int T, int D, int W, float lam, float eta, const float* q, const float* k,
                                const float* v, float* m, float* A_final);
 void tco_memory_f32_chunked(int T, int D, int W, int C, float lam, float eta, const float* q, const float* k,
@@ -56,7 +59,13 @@ static int check_forward_backward(int B, int H, int T, int D, int W) {
   double *dl = dalloc(nh, 0), *de = dalloc(nh, 0), *dg = dalloc(nh, 0);
   tco_forward(B, H, T, D, W, 1.0 / sqrt((double)D), q, k, v, lam, eta, gate, y, A, lse);
   tco_backward(B, H, T, D, W, 1.0 / sqrt((double)D), q, k, v, dy, lam, eta, gate, dq, dk, dv, dl, de, dg);
-  int ok = finite_all(y, n) && finite_all(A, (size_t)B * H * D * D) && finite_all(lse, (size_t)B * H * T) &&
+  int ok = 1;
+  for (int C = 1; C <= 5; C += 2) {  /* the chunk-mean shortcut, incomplete last chunks included */
+    tco_forward_chunk_mean(B, H, T, D, W, C, 0.5, q, k, v, lam, eta, gate, dq, A, lse);
+    ok = ok && finite_all(dq, n) && finite_all(A, (size_t)B * H * D * D);
+  }
+  tco_backward(B, H, T, D, W, 1.0 / sqrt((double)D), q, k, v, dy, lam, eta, gate, dq, dk, dv, dl, de, dg);
+  ok = ok && finite_all(y, n) && finite_all(A, (size_t)B * H * D * D) && finite_all(lse, (size_t)B * H * T) &&
            finite_all(dq, n) && finite_all(dk, n) && finite_all(dv, n) && finite_all(dl, nh) &&
            finite_all(de, nh) && finite_all(dg, nh);
   free(q); free(k); free(v); free(dy); free(lam); free(eta); free(gate); free(y); free(A); free(lse);
