@@ -10,7 +10,7 @@ forward, each with its roofline, plus the CPU oracle timed on the host on
 bounded samples of the same workloads.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
-                    [--legs prefill,decode,backward,train_forward,continue,capacity[,calib]]
+                    [--legs prefill,decode,backward,train_forward,continue,chunk_mean,capacity[,calib]]
 
 The long-context prefill (the headline) always runs; --legs picks the others.
 """
@@ -236,6 +236,46 @@ def continue_leg(steps, warmup, chunk=4096):
                               traffic=measured_traffic().get("continue"),
                               kernel="%d tc_forward_continue calls (gather + initial-state read + forward over "
                                      "ring prefix and chunk + state/ring update)" % n))
+
+
+def chunk_mean_leg(steps, warmup, exact_ms):
+    """The chunk-mean shortcut (one mean write per chunk of C evicted pairs)
+    on the long-context workload, next to the exact scan: its time per call,
+    the cost ratio shortcut / exact, and how far its output lands from the
+    exact one (relative L2 over y) -- the pages claim the exact scan comes at
+    the same computational cost and removes the C^2 - C cross terms per chunk
+    ("Tensor Cache: Eviction-conditioned Associative Memory for
+    Transformers", abstract and Section 1)."""
+    import torch
+
+    import eviction_fed_weight_amd as tc
+    import tc_inputs
+
+    cfg = tc_inputs.CONFIGS[3]
+    d = tc_inputs.prefill_inputs(3)
+    dv = torch.device("cuda")
+    q, k, v = (torch.from_numpy(d[x]).to(dv).to(torch.bfloat16).contiguous() for x in ("q", "k", "v"))
+    lam, eta, g = (torch.from_numpy(d[x]).to(dv) for x in ("lam", "eta", "gate"))
+    y = torch.empty_like(q)
+    A = torch.empty((cfg.B, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dv)
+    lse = torch.empty((cfg.B, cfg.H, cfg.T), dtype=torch.float32, device=dv)
+    shape = tc.make_shape(cfg.B, cfg.H, cfg.T, cfg.D, cfg.W, cfg.C)
+    ws = torch.empty(max(tc.tc_forward_workspace_size(shape), 1), dtype=torch.uint8, device=dv)
+
+    def call():
+        tc.tc_forward_chunk_mean(q, k, v, lam, eta, g, cfg.W, cfg.C, y=y, A_final=A, lse=lse, ws=ws)
+
+    ms = time_calls(call, steps, warmup)
+    ye, Ae, _ = tc.tc_forward(q, k, v, lam, eta, g, cfg.W, cfg.C)
+    torch.cuda.synchronize()
+    gap = float((y.float() - ye.float()).norm() / ye.float().norm())
+    gap_m = float((A - Ae).norm() / Ae.norm())
+    return dict(workload="chunk-mean shortcut, prefill B=%d H=%d D=%d T=%d W=%d C=%d bf16" % (cfg.B, cfg.H, cfg.D, cfg.T,
+                                                                                            cfg.W, cfg.C),
+                ms_per_call=ms, tokens_per_s=cfg.B * cfg.T / (ms * 1e-3), exact_ms_per_call=exact_ms,
+                cost_ratio_shortcut_over_exact=ms / exact_ms, rel_gap_y_vs_exact=gap, rel_gap_A_final_vs_exact=gap_m,
+                kernel="one tc_forward_chunk_mean call (seg_state_kernel [mean writes] + seg_chain_kernel + "
+                       "fwd_kernel_rows, no intra-chunk terms)")
 
 
 def capacity_leg(D=128, H=8, Ns=(64, 128, 256, 512, 1024, 2048, 4096)):
@@ -487,7 +527,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--legs", default="prefill,decode,backward,train_forward,continue,capacity")
+    ap.add_argument("--legs", default="prefill,decode,backward,train_forward,continue,chunk_mean,capacity")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -539,6 +579,11 @@ def main():
         cl = continue_leg(max(3, args.steps // 5), 2)
         log("  continue", json.dumps(cl))
         out["chunked_prefill"] = cl
+    if "chunk_mean" in legs:
+        log("chunk-mean shortcut leg ...")
+        cm = chunk_mean_leg(args.steps, args.warmup, lp["ms_per_call"])
+        log("  chunk_mean", json.dumps(cm))
+        out["chunk_mean_shortcut"] = cm
     if "capacity" in legs:
         log("capacity diagnostic leg ...")
         cp = capacity_leg()

@@ -142,8 +142,10 @@ float scale_of(float scale, int D) { return scale > 0.0f ? scale : 1.0f / sqrtf(
 // One forward launch over shape s (rows >= row0 stored, yadd added to them).
 tc_status_t launch_fwd(const tc_shape_t& s, const Plan& p, const void* q, const void* k, const void* v,
                        const float* lambda, const float* eta, const float* gate, void* y, float* A_final,
-                       float* lse, void* ws, bool ws_ok, int row0, const float* yadd, hipStream_t stream) {
+                       float* lse, void* ws, bool ws_ok, int row0, const float* yadd, hipStream_t stream,
+                       int mean_c = 0) {
   tck::FwdArgs a{};
+  a.mean_c = mean_c;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -307,6 +309,26 @@ tc_status_t tc_forward(const tc_shape_t* s, const void* q, const void* k, const 
   }
   return launch_fwd(*s, p, q, k, v, lambda, eta, gate, y, A_final, lse, ws, ws_bytes >= need, 0, nullptr,
                     (hipStream_t)stream);
+}
+
+tc_status_t tc_forward_chunk_mean(const tc_shape_t* s, const void* q, const void* k, const void* v,
+                                  const float* lambda, const float* eta, const float* gate, void* y,
+                                  float* A_final, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const tc_status_t st = check_fwd_args(s, q, k, v, lambda, eta, gate, y, A_final, lse);
+  if (st != TC_OK) return st;
+  // built for the 128-row bf16 kernel, with chunks that tile its blocks
+  if (s->dtype != TC_BF16 || s->D > 64 || (s->C != 64 && s->C != 128) || s->W % s->C != 0) return TC_ERR_UNSUPPORTED;
+  const Plan p = plan_for(*s);
+  const size_t need = fwd_ws_bytes(*s, p);
+  if (p.nseg > 1 && (!ws || ws_bytes < need)) return TC_ERR_WORKSPACE;
+  if (ws && ws_bytes >= need) {
+    const FwdExtents x = fwd_extents(*s, A_final, lse);
+    const void* bufs[9] = {q, k, v, lambda, eta, gate, y, A_final, lse};
+    for (int i = 0; i < 9; ++i)
+      if (overlap(ws, need, bufs[i], x.sz[i])) return TC_ERR_INVALID_ARGUMENT;
+  }
+  return launch_fwd(*s, p, q, k, v, lambda, eta, gate, y, A_final, lse, ws, ws_bytes >= need, 0, nullptr,
+                    (hipStream_t)stream, s->C);
 }
 
 tc_status_t tc_forward_noalloc(const tc_shape_t* s, const void* q, const void* k, const void* v,

@@ -380,7 +380,10 @@ __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128
 }
 
 template <class E, int D>
-static hipError_t launch_fwd_impl(const FwdArgs& a, hipStream_t s) {
+static hipError_t launch_fwd_impl(const FwdArgs& a0, hipStream_t s) {
+  FwdArgs a = a0;
+  if (a.mean_c != 0) return hipErrorInvalidValue;  // (the chunk-mean shortcut runs on the rows kernel only)
+  a.blk_pow = 64;  // exact scan: one decay per evicted token of a 64-row block
   const int BH = a.B * a.H;
   if (a.nseg > 1) {
     hipLaunchKernelGGL((seg_state_kernel<E, D, 64>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);

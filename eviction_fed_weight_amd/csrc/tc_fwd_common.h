@@ -172,6 +172,34 @@ __device__ __forceinline__ void state_fill(State<E, D>& st, float x) {
     for (int at = 0; at < D / 16; ++at) st.s[o][at] = f32x4{x, x, x, x};
 }
 
+// st <- dec * st + km vm^T (km, vm: D floats each, e.g. in LDS): one write
+// of the chunk-mean shortcut in the accumulator layout of State.
+template <class E, int D>
+__device__ __forceinline__ void state_rank1(State<E, D>& st, float dec, const float* km, const float* vm, int wid,
+                                            int l16, int lg) {
+  constexpr int NT = D / 16;
+#pragma unroll
+  for (int o = 0; o < State<E, D>::NOWN; ++o) {
+    const int ct = wid + 4 * o;
+    if (ct < NT) {
+      const float vc = vm[16 * ct + l16];
+#pragma unroll
+      for (int at = 0; at < NT; ++at)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.s[o][at][i] = dec * st.s[o][at][i] + km[16 * at + 4 * lg + i] * vc;
+    }
+  }
+}
+
+// Sum of rows 0..63 of column c of a row-major LDS tile (row stride ld).
+template <class E>
+__device__ __forceinline__ float tile_col_sum(const E* tile, int ld, int c) {
+  float s = 0.0f;
+#pragma unroll 8
+  for (int r = 0; r < 64; ++r) s += (float)tile[r * ld + c];
+  return s;
+}
+
 // st <- mult * st + (the state whose transpose is at Sl, S[a][c] at Sl[c * LDS + a])
 template <class E, int D, int LDS>
 __device__ __forceinline__ void state_scale_add_lds_t(State<E, D>& st, float mult, const float* Sl, int wid, int l16,
@@ -284,12 +312,20 @@ __device__ __forceinline__ void store4(float* dst, f32x4 x) { *(f32x4*)dst = x; 
 // grid is BH * nseg and workgroup m = nseg - 1 of each head forms instead the
 // local state of the last segment's evictions up to step T-1 (for the final
 // state), at seg_state[BH * nseg + bh].
-template <class E, int D, int BM>
+//
+// MEANC > 0: the chunk-mean shortcut with chunks of MEANC (64 or 128)
+// evictions: L_m = sum over the segment's chunks n of lambda^(later chunks)
+// kbar_n vbar_n^T, one decay per chunk; in the last segment (final_slot)
+// only the chunks complete by step T-1.  Segment starts are multiples of
+// MEANC evictions (the launcher requires W to be one), so chunks never
+// straddle segments.
+template <class E, int D, int BM, int MEANC = 0>
 __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
   constexpr int LDK = D + 16 / (int)sizeof(E);
   constexpr int TILE = 64 * LDK * (int)sizeof(E);
   __shared__ __attribute__((aligned(16))) char smem[2 * TILE];
   __shared__ float pw[72];
+  __shared__ float cm[MEANC > 0 ? 2 * D : 1];  // means of the chunk just completed (keys, then values)
   E* Ks = (E*)smem;
   E* Vs = (E*)(smem + TILE);
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
@@ -314,6 +350,7 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
   while (t0 < ntile && ebase + 64 * t0 + 63 < 0) ++t0;  // tiles wholly before the first token
   kl.load(Kg, ebase + 64 * t0);
   vl.load(Vg, ebase + 64 * t0);
+  float run = 0.0f;  // MEANC: column sum of the running chunk (thread c < D: keys, D <= c < 2D: values)
   for (int t = t0; t < ntile; ++t) {
     const int e0 = ebase + 64 * t;
     __syncthreads();
@@ -324,8 +361,23 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
       kl.load(Kg, e0 + 64);
       vl.load(Vg, e0 + 64);
     }
-    const int len = tile_len(t);
-    if (len > 0) state_update(st, Ks, LDK, Vs, LDK, pw, len, e0, wid, l16, lg);
+    if (MEANC == 0) {
+      const int len = tile_len(t);
+      if (len > 0) state_update(st, Ks, LDK, Vs, LDK, pw, len, e0, wid, l16, lg);
+    } else {
+      // (rows past the end of the sequence were loaded as zeros; an incomplete
+      // chunk is never written)
+      if (tid < 2 * D) run += tid < D ? tile_col_sum(Ks, LDK, tid) : tile_col_sum(Vs, LDK, tid - D);
+      if ((t + 1) % (MEANC / 64 > 0 ? MEANC / 64 : 1) == 0) {
+        if (tid < 2 * D) {
+          cm[tid] = run * (1.0f / (MEANC > 0 ? MEANC : 1));
+          run = 0.0f;
+        }
+        __syncthreads();
+        const bool complete = !fin || tb + 64 * (t + 1) <= a.T;
+        if (complete) state_rank1(st, a.lam[h], cm, cm + D, wid, l16, lg);
+      }
+    }
   }
   float* dst = fin ? a.seg_state + ((size_t)a.B * a.H * a.nseg + bh) * D * D
                    : a.seg_state + ((size_t)bh * a.nseg + m + 1) * D * D;
@@ -333,7 +385,8 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
 }
 
 // Chain over segments, in place: seg_state[0] = 0 and
-// seg_state[m+1] = lambda^(BM blocks(m)) seg_state[m] + L_m.
+// seg_state[m+1] = lambda^(blk_pow blocks(m)) seg_state[m] + L_m (blk_pow:
+// decays per block, BM for the exact scan, BM / C for the chunk-mean shortcut).
 // grid = (D*D/4 + 63)/64 x BH of one wave (kChainThreads) each (the pass moves two D x D
 // states per segment; small workgroups spread it over many compute units);
 // each thread owns four consecutive floats and loads 32 segments ahead of the
@@ -344,8 +397,8 @@ __global__ void __launch_bounds__(kChainThreads) seg_chain_kernel(FwdArgs a) {
   const int bh = blockIdx.y;
   const int x = blockIdx.x * kChainThreads + threadIdx.x;
   if (x * 4 >= D * D) return;
-  // S_m = lambda^(BM blocks(m-1)) S_{m-1} + L_{m-1}
-  const float decay = powi(a.lam[bh % a.H], BM * a.G), decay1 = decay * powi(a.lam[bh % a.H], BM);
+  // S_m = lambda^(blk_pow blocks(m-1)) S_{m-1} + L_{m-1}
+  const float decay = powi(a.lam[bh % a.H], a.blk_pow * a.G), decay1 = decay * powi(a.lam[bh % a.H], a.blk_pow);
   float4* p = (float4*)(a.seg_state + (size_t)bh * a.nseg * D * D) + x;
   const size_t stride = (size_t)D * D / 4;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);

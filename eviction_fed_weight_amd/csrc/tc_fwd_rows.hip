@@ -154,16 +154,29 @@ __device__ __forceinline__ void lds_state_update(float* Sl, const E* Ks, int ldk
 
 // PUB: one block per segment, local states exchanged through flags (see
 // FwdArgs::publish); otherwise the segment states come from the state pass.
-template <class E, int D, int NW, bool PUB>
+//
+// MEANC > 0 (64 or 128, with W a multiple of it; never with PUB): the
+// chunk-mean shortcut instead of the exact scan.  The evictions form chunks
+// of MEANC tokens; one write per chunk, S <- lambda S + kbar vbar^T; a row
+// whose evicted token lies in chunk n reads S after chunks 0 .. n-1.  Block
+// j evicts the chunks of e0 .. e0+127, so its row r reads
+//   lambda^(r / MEANC) q S(e0) + [MEANC = 64, r >= 64] <q, kbar_0> vbar_0
+// (kbar_0, vbar_0: the means of the block's first 64 evictions), and the
+// carry is BM / MEANC such writes.  No intra-chunk triangle.
+template <class E, int D, int NW, bool PUB, int MEANC = 0>
 __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdArgs a) {
   using M = Mfma<E>;
   using frag = typename M::frag;
   using L = FRows<E, D, NW>;
   constexpr int NT = L::NT, NKC = L::NKC, LDK = L::LDK, LDV = L::LDV;
   constexpr int NTH = L::NTH, BM = L::BM, NQ = L::NQ;
+  constexpr bool MEAN = MEANC > 0;
   static_assert(D <= 64 && NW == 4, "128-row blocks: the two chunk tiles fit the two buffers");
+  static_assert(!(MEAN && PUB), "the chunk-mean shortcut runs with the state pass");
+  static_assert(MEANC == 0 || MEANC == 64 || MEANC == 128, "chunk-mean chunks of 64 or 128 evictions");
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
   __shared__ float pw[BM + 4];
+  __shared__ float cm[MEAN ? 4 * D : 1];  // MEAN: chunk means kbar_0, vbar_0, kbar_1, vbar_1
   E* Qs = (E*)(smem + 2 * L::BUF);
   float* Sl = (float*)(smem + 2 * L::BUF + L::QB);
   constexpr int LDS = L::LDS;
@@ -287,7 +300,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
     // S at the segment start from the local states L_m (stored at index m+1):
     // S_{m+1} = lambda^(BM blocks(m)) S_m + L_m, in chain order
     constexpr int PER = (D * D + NTH - 1) / NTH;
-    const float dec = powi(a.lam[h], BM * a.G), dec1 = dec * powi(a.lam[h], BM);
+    const float dec = powi(a.lam[h], a.blk_pow * a.G), dec1 = dec * powi(a.lam[h], a.blk_pow);
     const float* g = a.seg_state + (size_t)bh * a.nseg * D * D;
     float acc[PER];
 #pragma unroll
@@ -516,13 +529,54 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
       Kc = (const E*)(smem + (ub & 1) * L::BUF);
       Vc = (const E*)(smem + (ub & 1) * L::BUF + L::KT);
     };
+    if constexpr (MEAN) {
+      // means of the block's evicted chunks (both tiles are still in the
+      // buffers; rows before token 0 were loaded as zeros)
+      if (has_mem) {
+        const E *K0, *V0, *K1, *V1;
+        chunk_tile(0, K0, V0);
+        chunk_tile(1, K1, V1);
+        if (MEANC == 64 && tid < 4 * D) {
+          const int which = tid / D, c = tid - which * D;
+          const E* tl = which == 0 ? K0 : which == 1 ? V0 : which == 2 ? K1 : V1;
+          cm[tid] = tile_col_sum(tl, (which & 1) ? LDV : LDK, c) * (1.0f / 64);
+        } else if (MEANC == 128 && tid < 2 * D) {
+          const bool isv = tid >= D;
+          const int c = tid - (isv ? D : 0);
+          cm[tid] = (tile_col_sum(isv ? V0 : K0, isv ? LDV : LDK, c) + tile_col_sum(isv ? V1 : K1, isv ? LDV : LDK, c)) *
+                    (1.0f / 128);
+        }
+        __syncthreads();
+      }
+    }
     // PUB: the first read of the earlier segments' flags is issued here and
     // returns while the chunk terms below are computed
     const bool poller = PUB && seg > m_lo && tid < seg - m_lo;
     const unsigned long long* const myflag = a.flags + (size_t)bh * a.nseg + m_lo + tid;
     unsigned long long flag0 = 0;
     if (poller) flag0 = __hip_atomic_load(myflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (has_mem) {
+    if (MEAN && MEANC == 64 && has_mem && rw >= 64) {
+      // rows 64..127 are in the block's second chunk: they also read the
+      // write of the first one, sigma(g) eta <q_r, kbar_0> vbar_0
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        float x[8], dotp = 0.0f;
+#pragma unroll
+        for (int dc = 0; dc < NKC; ++dc) {
+          if (dc * 32 + lg * 8 < D) {
+            M::to_f32(qf[g][dc], x);
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) dotp += x[jj] * cm[dc * 32 + lg * 8 + jj];
+          }
+        }
+        const float f = seta * xsum4(dotp);
+#pragma unroll
+        for (int dt = 0; dt < NT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[g][dt][i] += f * cm[D + dt * 16 + 4 * lg + i];
+      }
+    }
+    if (!MEAN && has_mem) {
       // O += sigma(g) eta sum_{c <= r} lambda^(r-c) <q_r, k_{e0+c}> v_{e0+c}
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -613,18 +667,39 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
           }
         }
 #pragma unroll
-        for (int g = 0; g < 2; ++g) O[g][dt] += (seta * pw[rw + 16 * g + l16 + 1]) * acc[g];
+        for (int g = 0; g < 2; ++g) {
+          // exact: lambda^(r+1); chunk mean: lambda^(r / MEANC) (rows 64.. of a 64-chunk block)
+          const float dk = MEAN ? ((MEANC == 64 && rw >= 64) ? pw[1] : 1.0f) : pw[rw + 16 * g + l16 + 1];
+          O[g][dt] += (seta * dk) * acc[g];
+        }
       }
     }
     if (!PUB && has_mem && (more || (last && a.A_final && !a.final_slot))) {
       __syncthreads();  // every wave has read S(e0)
+      if constexpr (MEAN) {
+        // the block's chunk writes, S <- lambda S + kbar vbar^T each (in the
+        // last block only the chunks complete by step T-1)
+        constexpr int NCH = BM / (MEANC > 0 ? MEANC : 1);
+        int nw = NCH;
+        if (!more)
+          for (nw = 0; nw < NCH && t0 + (MEANC > 0 ? MEANC : 1) * (nw + 1) <= T; ++nw) {
+          }
+        const float lam = pw[1];
+        for (int x = tid; x < D * D; x += NTH) {
+          const int ar = x % D, c = x / D;
+          float sv = Sl[c * LDS + ar];
+          for (int m = 0; m < nw; ++m) sv = lam * sv + cm[2 * m * D + ar] * cm[(2 * m + 1) * D + c];
+          Sl[c * LDS + ar] = sv;
+        }
+      } else {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int len = more ? 64 : min(64, T - t0 - 64 * c);
-        if (c < cb.nlate && len > 0) {
-          const E *Kc, *Vc;
-          chunk_tile(c, Kc, Vc);
-          lds_state_update<E, D, NW>(Sl, Kc, LDK, Vc, LDV, pw, len, e0 + 64 * c, wid, l16, lg);
+        for (int c = 0; c < 2; ++c) {
+          const int len = more ? 64 : min(64, T - t0 - 64 * c);
+          if (c < cb.nlate && len > 0) {
+            const E *Kc, *Vc;
+            chunk_tile(c, Kc, Vc);
+            lds_state_update<E, D, NW>(Sl, Kc, LDK, Vc, LDV, pw, len, e0 + 64 * c, wid, l16, lg);
+          }
         }
       }
     }
@@ -662,7 +737,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
     if (a.prefix_direct) {
-      const float dec = powi(a.lam[h], BM * a.G), dec1 = dec * powi(a.lam[h], BM);
+      const float dec = powi(a.lam[h], a.blk_pow * a.G), dec1 = dec * powi(a.lam[h], a.blk_pow);
       for (int m = 1; m <= last_seg; ++m) {
         const float dm = m - 1 < a.R ? dec1 : dec;
 #pragma unroll
@@ -675,7 +750,10 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
       for (int k = 0; k < PER; ++k)
         if ((D * D) % NTH == 0 || tid + NTH * k < D * D) acc[k] = g[(size_t)last_seg * D * D + tid + NTH * k];
     }
-    const float dn = powi(a.lam[h], T - seg_first_block(a, last_seg) * BM);
+    // decays since the last segment's start: one per eviction (exact), one
+    // per complete chunk (chunk mean)
+    const int nev = T - seg_first_block(a, last_seg) * BM;
+    const float dn = powi(a.lam[h], MEAN ? nev / (MEANC > 0 ? MEANC : 1) : nev);
     const float eta = a.eta[h];
     float* Af = a.A_final + (size_t)bh * D * D;
 #pragma unroll
@@ -715,22 +793,24 @@ static long long rows_resident_capacity() {
   return c;
 }
 
-template <class E, int D>
+template <class E, int D, int MEANC>
 static hipError_t launch_rows_impl(const FwdArgs& a0, hipStream_t s) {
   constexpr int NW = kRowWaves, BM = 32 * NW;
   FwdArgs a = a0;
   const int BH = a.B * a.H;
   a.prefix_direct = a.nseg <= kDirectPrefixMaxSeg ? 1 : 0;
+  a.blk_pow = MEANC > 0 ? BM / MEANC : BM;
   // One block per segment and a grid the device holds at once: the
   // workgroups exchange their local states through flags and no state pass
   // runs.  (The residency test is for speed only: a workgroup waits only for
   // workgroups dispatched before it, so the waits end in any case.)
   // Not under graph capture: a replayed launch repeats this call's flag value,
-  // so flags left by the previous replay would read as current.
+  // so flags left by the previous replay would read as current.  Not for the
+  // chunk-mean shortcut, which always takes the state pass.
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   const bool capturing = hipStreamIsCapturing(s, &capture) != hipSuccess || capture != hipStreamCaptureStatusNone;
-  a.publish = (a.G == 1 && a.R == 0 && a.nseg > 1 && a.prefix_direct && a.flags != nullptr && !capturing &&
-               (long long)BH * a.nseg <= rows_resident_capacity<E, D, NW>())
+  a.publish = (MEANC == 0 && a.G == 1 && a.R == 0 && a.nseg > 1 && a.prefix_direct && a.flags != nullptr &&
+               !capturing && (long long)BH * a.nseg <= rows_resident_capacity<E, D, NW>())
                   ? 1
                   : 0;
   // otherwise the state pass also forms the last block's local state (final
@@ -741,23 +821,34 @@ static hipError_t launch_rows_impl(const FwdArgs& a0, hipStream_t s) {
   const char* polls = getenv("TC_FORWARD_MAX_POLLS");
   a.max_polls = polls ? atoi(polls) : kPublishPolls;
   if (a.nseg > 1 && !a.publish) {
-    hipLaunchKernelGGL((seg_state_kernel<E, D, BM>), dim3(BH * (a.nseg - 1 + a.final_slot)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((seg_state_kernel<E, D, BM, MEANC>), dim3(BH * (a.nseg - 1 + a.final_slot)), dim3(256), 0, s,
+                       a);
     if (!a.prefix_direct)
       hipLaunchKernelGGL((seg_chain_kernel<D, BM>), dim3((D * D / 4 + kChainThreads - 1) / kChainThreads, BH), dim3(kChainThreads), 0, s, a);
   }
   if (a.publish)
     hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, true>), dim3(BH * a.nseg), dim3(64 * NW), 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, false>), dim3(BH * a.nseg), dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, false, MEANC>), dim3(BH * a.nseg), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
+}
+
+template <class E, int D>
+static hipError_t launch_rows_mode(const FwdArgs& a, hipStream_t s) {
+  switch (a.mean_c) {
+    case 0: return launch_rows_impl<E, D, 0>(a, s);
+    case 64: return launch_rows_impl<E, D, 64>(a, s);
+    case 128: return launch_rows_impl<E, D, 128>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_forward_rows(const FwdArgs& a, int D, bool is_bf16, hipStream_t s) {
   if (!is_bf16) return hipErrorInvalidValue;
   switch (D) {
-    case 16: return launch_rows_impl<bf16, 16>(a, s);
-    case 32: return launch_rows_impl<bf16, 32>(a, s);
-    case 64: return launch_rows_impl<bf16, 64>(a, s);
+    case 16: return launch_rows_mode<bf16, 16>(a, s);
+    case 32: return launch_rows_mode<bf16, 32>(a, s);
+    case 64: return launch_rows_mode<bf16, 64>(a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -50,6 +50,12 @@ struct FwdArgs {
   // to each stored row before rounding.  tc_forward: row0 = 0, yadd = null.
   int row0;
   const float* yadd;
+  // Decays of the state per query block: BM (one per evicted token) for the
+  // exact scan, BM / C for the chunk-mean shortcut (one per chunk).
+  int blk_pow;
+  // 0: the exact scan.  64 or 128: the chunk-mean shortcut with chunks of
+  // that many evictions (tc_forward_chunk_mean; bf16 rows kernel only).
+  int mean_c;
 };
 
 // First block of forward segment s (s = nseg gives nblk).

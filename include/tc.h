@@ -67,9 +67,11 @@ typedef enum { TC_F32 = 0, TC_BF16 = 1 } tc_dtype_t;
 
 /* Prefill / training shapes.  scale <= 0 selects 1/sqrt(D) (the standard
  * scaled dot product; the pages do not state the scale).  C is the chunk
- * length of the weighted-sum scan; exact results do not depend on it (only
- * float rounding does), and the GPU path tiles the scan in 64-token chunks
- * for every C. */
+ * length of the scan.  The exact weighted-sum scan (tc_forward, the
+ * backward, the continuation) gives results that do not depend on it (only
+ * float rounding does): its kernels read the state per query block (128 rows
+ * for bf16 with D <= 64, else 64) and advance it in 64-token steps whatever
+ * C is.  C matters to tc_forward_chunk_mean, the chunk-mean shortcut. */
 typedef struct {
   int32_t B, H, T, D, W, C;
   float scale;
@@ -120,6 +122,25 @@ size_t tc_backward_workspace_size(const tc_shape_t* shape);
 tc_status_t tc_forward(const tc_shape_t* shape, const void* q, const void* k, const void* v,
                        const float* lambda, const float* eta, const float* gate, void* y,
                        float* A_final, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tc_forward_chunk_mean -- the chunk-mean shortcut that the exact scan
+ * replaces (abstract; Section 1, contributions; Section 2, training
+ * considerations): the eviction stream in chunks of C pairs, each chunk
+ * written once as its mean pair, A <- lambda A + eta (kbar outer vbar).
+ * It exists to measure what the shortcut costs and how far it lands from
+ * the exact scan.  Read between writes (the pages do not say; the chunked
+ * scan's inter-chunk state): a query at step t >= W whose evicted token t-W
+ * lies in chunk n = (t-W)/C reads the memory after chunks 0 .. n-1; earlier
+ * queries read nothing.  A_final (nullable) is the memory after every
+ * complete chunk; L1, y, lse and the arguments are as for tc_forward, with
+ * the same workspace (tc_forward_workspace_size).
+ * Built for bf16 with D in {16, 32, 64}, C in {64, 128} and W a multiple of
+ * C; other shapes return TC_ERR_UNSUPPORTED.
+ */
+tc_status_t tc_forward_chunk_mean(const tc_shape_t* shape, const void* q, const void* k, const void* v,
+                                  const float* lambda, const float* eta, const float* gate, void* y,
+                                  float* A_final, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * tc_forward_noalloc -- tc_forward for callers that cannot allocate device
