@@ -234,12 +234,12 @@ def tc_forward_chunk_mean(q, k, v, lam, eta, gate, W: int, C: int, scale: float 
     return y, (A_final if want_state else None), (lse if want_lse else None)
 
 
-NOALLOC_SCRATCH_BYTES = 16 << 20  # the static device scratch of tc_forward_noalloc
+NOALLOC_SCRATCH_BYTES = 32 << 20  # the static device scratch of tc_forward_noalloc
 
 
 def tc_forward_noalloc(q, k, v, lam, eta, gate, W: int, C: int = 64, scale: float = 0.0, *, y, A_final=None,
                        lse=None):
-    """tc_forward without a workspace: the library uses its static 16 MiB
+    """tc_forward without a workspace: the library uses its static 32 MiB
     device scratch (no device allocation in the call).  The outputs are
     passed in (y required; A_final and lse optional).  Returns (y, A_final,
     lse)."""

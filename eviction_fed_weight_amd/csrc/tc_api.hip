@@ -16,7 +16,7 @@
 #include "../../include/tc.h"
 #include "tc_launch.h"
 
-constexpr size_t kScratchBytes = (size_t)16 << 20;  // 16 MiB per device
+constexpr size_t kScratchBytes = (size_t)32 << 20;  // 32 MiB per device
 constexpr int kMaxDevices = 64;
 
 // The allocation-free forward's workspace (see scratch_ptr below).
@@ -90,6 +90,14 @@ Plan plan_for(const tc_shape_t& s, int row0 = 0) {
       bestG = G;
     }
   }
+  // The 128-row kernel carries the state from block to block with two decayed
+  // rank-64 updates inside the workgroup, work that the parallel state pass
+  // does off the critical path when segments are short.  When pairs of blocks
+  // fill more than one round of workgroups, segments of two blocks measured
+  // fastest (B=1 H=12 T=32768: 0.234 ms against 0.242 ms for the 42
+  // segments of 6-7 blocks this model picks, and 0.253 ms for single blocks,
+  // whose chain over 256 segments per head costs more than the updates save).
+  if (bm == 128 && bestG > 2 && BH * ((nb + 1) / 2) > slots) bestG = 2;
   p.nseg = (nb + bestG - 1) / bestG;
   if (BH * p.nseg <= slots) {
     const long long fill = slots / BH < nb ? slots / BH : nb;

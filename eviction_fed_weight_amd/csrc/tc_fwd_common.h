@@ -63,6 +63,47 @@ __device__ __forceinline__ void state_update(State<E, D>& st, const E* Ks, int l
   }
 }
 
+// state_update with the masks folded into the weight table: pwz[n] =
+// lambda^n for 0 <= n <= 64 and 0 for -64 <= n < 0, so column c < 64 of the
+// chunk gets weight pwz[len - 1 - c] (0 past len).  Rows of the chunk before
+// token 0 need no mask: their K and V rows were loaded as zeros (buffer loads
+// outside the sequence).
+template <class E, int D>
+__device__ __forceinline__ void state_update_z(State<E, D>& st, const E* Ks, int ldk, const E* Vs, int ldv,
+                                               const float* pwz, int len, int wid, int l16, int lg) {
+  using M = Mfma<E>;
+  using frag = typename M::frag;
+  constexpr int NT = D / 16, NOWN = State<E, D>::NOWN;
+  const float decay = pwz[len];
+#pragma unroll
+  for (int o = 0; o < NOWN; ++o) {
+    const int ct = wid + 4 * o;
+    if (ct < NT) {
+#pragma unroll
+      for (int at = 0; at < NT; ++at) st.s[o][at] *= decay;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        float wv[8];
+        {
+          float vv[8];
+          M::to_f32(ColFrag<E>::read(Vs + (kc * 32 + lg * 8) * ldv + ct * 16, ldv, l16), vv);
+          const float* wp = pwz + (len - 1 - kc * 32 - lg * 8 - 7);  // weight of column c at wp[7 - (c % 8)]
+#pragma unroll
+          for (int j = 0; j < 8; ++j) wv[j] = wp[7 - j] * vv[j];
+        }
+        frag bhi, blo;
+        M::split(wv, bhi, blo);
+#pragma unroll
+        for (int at = 0; at < NT; ++at) {
+          const frag a = ColFrag<E>::read(Ks + (kc * 32 + lg * 8) * ldk + at * 16, ldk, l16);
+          st.s[o][at] = M::mma(a, bhi, st.s[o][at]);
+          if (M::kSplit) st.s[o][at] = M::mma(a, blo, st.s[o][at]);
+        }
+      }
+    }
+  }
+}
+
 template <class E, int D>
 __device__ __forceinline__ void state_zero(State<E, D>& st) {
 #pragma unroll
@@ -324,8 +365,9 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
   constexpr int LDK = D + 16 / (int)sizeof(E);
   constexpr int TILE = 64 * LDK * (int)sizeof(E);
   __shared__ __attribute__((aligned(16))) char smem[2 * TILE];
-  __shared__ float pw[72];
+  __shared__ float pwt[64 + 72];  // pw[n] = lambda^n for 0 <= n <= 64, 0 for -64 <= n < 0
   __shared__ float cm[MEANC > 0 ? 2 * D : 1];  // means of the chunk just completed (keys, then values)
+  float* const pw = pwt + 64;
   E* Ks = (E*)smem;
   E* Vs = (E*)(smem + TILE);
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
@@ -337,7 +379,7 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
   const uint32_t nbytes = (uint32_t)a.T * D * sizeof(E);
   const auto Kg = make_rsrc((const E*)a.k + base, nbytes);
   const auto Vg = make_rsrc((const E*)a.v + base, nbytes);
-  if (tid <= 64) pw[tid] = powi(a.lam[h], tid);
+  if (tid < 64 + 65) pwt[tid] = tid >= 64 ? powi(a.lam[h], tid - 64) : 0.0f;
   State<E, D> st;
   state_zero(st);
   TileRegs<E, D, 64> kl, vl;
@@ -363,7 +405,7 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
     }
     if (MEANC == 0) {
       const int len = tile_len(t);
-      if (len > 0) state_update(st, Ks, LDK, Vs, LDK, pw, len, e0, wid, l16, lg);
+      if (len > 0) state_update_z(st, Ks, LDK, Vs, LDK, pw, len, wid, l16, lg);
     } else {
       // (rows past the end of the sequence were loaded as zeros; an incomplete
       // chunk is never written)

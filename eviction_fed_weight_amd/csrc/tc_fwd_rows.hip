@@ -60,10 +60,15 @@ struct FRows {
   static constexpr int VT = 64 * LDV * (int)sizeof(E);
   static constexpr int BUF = KT + VT;
   static constexpr int QB = BM * LDK * (int)sizeof(E);
-  // The state lives in LDS as float S^T (S[a][c] at c * LDS + a; 17 chunks
-  // per row for D = 64), so it costs no registers between its uses.
+  // L^T of the state-exchange path (float, S[a][c] at c * LDS + a, in the Q
+  // area after the Q block is read).
   static constexpr int LDS = D + 4;
-  static constexpr int SB = D * LDS * 4;
+  // The state S(e0) that every wave reads for q S is kept in LDS as a bf16
+  // hi/lo pair of S^T copies (S[a][c] at c * LDH + a; rows of an odd number
+  // of 16-byte chunks), written once per block by the waves that own it; the
+  // float32 state itself stays in those waves' registers (OwnS).
+  static constexpr int LDH = D + 8;
+  static constexpr int SB = 2 * D * LDH * 2;
   static constexpr int TOTAL = 2 * BUF + QB + SB;
   static constexpr int NT = D / 16;
   static constexpr int NKC = (D + 31) / 32;
@@ -106,38 +111,68 @@ struct VFrag<float> {
   }
 };
 
-// S <- lambda^len S + sum_{c<len, e0+c>=0} lambda^(len-1-c) K[c,:]^T V[c,:]
-// on the LDS copy of S (float S^T), for a 64-row chunk whose K and V are
-// row-major in LDS.  The D/16 x D/16 accumulator tiles are split over the
-// waves: wave w takes column tile w % NT and a contiguous range of row tiles.
+// The float32 state S (D x D) of the 128-row kernel, split over the waves in
+// MFMA accumulator tiles: wave w owns column tile ct = w % NT and the AT row
+// tiles ar * AT .. ar * AT + AT - 1 (ar = w / NT; waves with ar >= RG own
+// nothing).  s[k][i] holds S[a = 16 (ar AT + k) + 4 lg + i][c = 16 ct + l16].
+template <int D, int NW>
+struct OwnS {
+  static constexpr int NT = D / 16;
+  static constexpr int RG = (NW / NT < NT) ? NW / NT : NT;  // row-tile groups per column tile
+  static constexpr int AT = NT / RG;                        // row tiles per wave
+  f32x4 s[AT];
+};
+
+// Four consecutive elements S[a0 .. a0+3][c] into the bf16 hi/lo copies of
+// S^T (hi = rne(x), lo = rne(x - hi): about 2^-17 relative).
+__device__ __forceinline__ void put_hilo(bf16* Sh, bf16* Sm, int ldh, int c, int a0, f32x4 v) {
+  bf16x4 hi, lo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = (bf16)v[i];
+    lo[i] = (bf16)(v[i] - (float)hi[i]);
+  }
+  *(bf16x4*)(Sh + c * ldh + a0) = hi;
+  *(bf16x4*)(Sm + c * ldh + a0) = lo;
+}
+
+// The owner waves publish their part of S as the bf16 hi/lo copies.
+template <int D, int NW>
+__device__ __forceinline__ void own_publish(const OwnS<D, NW>& so, bf16* Sh, bf16* Sm, int ldh, int wid, int l16,
+                                            int lg) {
+  using O = OwnS<D, NW>;
+  const int ct = wid % O::NT, ar = wid / O::NT;
+  if (ar >= O::RG) return;
+#pragma unroll
+  for (int k = 0; k < O::AT; ++k) put_hilo(Sh, Sm, ldh, 16 * ct + l16, 16 * (ar * O::AT + k) + 4 * lg, so.s[k]);
+}
+
+// S <- lambda^len S + sum_{c<len} lambda^(len-1-c) K[c,:]^T V[c,:] in the
+// owners' registers, for a 64-row chunk whose K and V are row-major in LDS.
+// pw[n] = lambda^n for 0 <= n <= 128 and 0 for -128 <= n < 0 (so the
+// columns past len get weight 0); chunk rows before token 0 were loaded as
+// zeros and need no mask.
 template <class E, int D, int NW>
-__device__ __forceinline__ void lds_state_update(float* Sl, const E* Ks, int ldk, const E* Vs, int ldv,
-                                                 const float* pw, int len, int e0, int wid, int l16, int lg) {
+__device__ __forceinline__ void own_state_update(OwnS<D, NW>& so, const E* Ks, int ldk, const E* Vs, int ldv,
+                                                 const float* pw, int len, int wid, int l16, int lg) {
   using M = Mfma<E>;
   using frag = typename M::frag;
-  constexpr int NT = D / 16, LDS = FRows<E, D, NW>::LDS;
-  constexpr int RG = (NW / NT < NT) ? NW / NT : NT;  // row-tile groups per column tile
-  constexpr int AT = NT / RG;                        // row tiles per wave
-  const int ct = wid % NT, ar = wid / NT;
-  if (ar >= RG) return;
+  constexpr int AT = OwnS<D, NW>::AT;
+  const int ct = wid % OwnS<D, NW>::NT, ar = wid / OwnS<D, NW>::NT;
+  if (ar >= OwnS<D, NW>::RG) return;
   f32x4 st[AT];
-  float* col = Sl + (16 * ct + l16) * LDS + 4 * lg;
   const float decay = pw[len];
 #pragma unroll
-  for (int k = 0; k < AT; ++k) st[k] = decay * *(const f32x4*)(col + 16 * (ar * AT + k));
+  for (int k = 0; k < AT; ++k) st[k] = decay * so.s[k];
 #pragma unroll
   for (int kc = 0; kc < 2; ++kc) {
     float wv[8];
     {
       float vv[8];
       M::to_f32(ColFrag<E>::read(Vs + (kc * 32 + lg * 8) * ldv + ct * 16, ldv, l16), vv);
+      const float* wp = pw + (len - 1 - kc * 32 - lg * 8 - 7);  // weight of column c at wp[7 - (c % 8)]
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = kc * 32 + lg * 8 + j;
-        // (branch-free: the LDS read is unconditional, at a clamped index)
-        const float w = ((c < len && e0 + c >= 0) ? 1.0f : 0.0f) * pw[max(len - 1 - c, 0)];
-        wv[j] = w * vv[j];
-      }
+      for (int j = 0; j < 8; ++j) wv[j] = wp[7 - j] * vv[j];
     }
     frag bhi, blo;
     M::split(wv, bhi, blo);
@@ -149,7 +184,7 @@ __device__ __forceinline__ void lds_state_update(float* Sl, const E* Ks, int ldk
     }
   }
 #pragma unroll
-  for (int k = 0; k < AT; ++k) *(f32x4*)(col + 16 * (ar * AT + k)) = st[k];
+  for (int k = 0; k < AT; ++k) so.s[k] = st[k];
 }
 
 // PUB: one block per segment, local states exchanged through flags (see
@@ -175,11 +210,18 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   static_assert(!(MEAN && PUB), "the chunk-mean shortcut runs with the state pass");
   static_assert(MEANC == 0 || MEANC == 64 || MEANC == 128, "chunk-mean chunks of 64 or 128 evictions");
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
-  __shared__ float pw[BM + 4];
+  // ptab: lambda^n at ptab[128 + n] for 0 <= n <= 128 and 0 for n < 0 (pw = ptab + 128); wtab[128 + d]
+  // = sigma(g) eta lambda^d for 0 <= d < 128 and 0 for d < 0, the weights of the intra-chunk terms
+  __shared__ float ptab[BM + 132];
+  __shared__ float wtab[2 * BM];
   __shared__ float cm[MEAN ? 4 * D : 1];  // MEAN: chunk means kbar_0, vbar_0, kbar_1, vbar_1
+  float* const pw = ptab + BM;
   E* Qs = (E*)(smem + 2 * L::BUF);
-  float* Sl = (float*)(smem + 2 * L::BUF + L::QB);
-  constexpr int LDS = L::LDS;
+  bf16* Sh = (bf16*)(smem + 2 * L::BUF + L::QB);  // S^T hi and lo (bf16), row stride LDH
+  bf16* Sm = Sh + D * L::LDH;
+  constexpr int LDS = L::LDS, LDH = L::LDH;
+  using O = OwnS<D, NW>;
+  O so;  // (not PUB) the float32 state, in the owner waves' registers
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   // PUB: segment-major order (workgroup b takes segment b / BH of head b % BH),
@@ -287,39 +329,43 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
 
   TileRegs<E, D, BM, NTH> qr;
   if (PUB) qr.load(Qg, jb * BM);
-  load_next();  // the first item's loads overlap the state set-up below
+  load_next();
 
-  if (tid <= BM) pw[tid] = powi(a.lam[h], tid);
+  for (int x = tid; x < 2 * BM + 1; x += NTH) {
+    const float lp = x >= BM ? powi(a.lam[h], x - BM) : 0.0f;
+    ptab[x] = lp;
+    if (x < 2 * BM) wtab[x] = seta * lp;
+  }
 
-  // S(e0) of the segment's first block -> LDS (transposed); with publish it
-  // is gathered after the window, from the earlier segments' published states
-  if (PUB) {
-  } else if (seg == 0) {
-    for (int x = tid; x < D * D; x += NTH) Sl[(x % D) * LDS + x / D] = 0.0f;
-  } else if (a.prefix_direct) {
-    // S at the segment start from the local states L_m (stored at index m+1):
-    // S_{m+1} = lambda^(BM blocks(m)) S_m + L_m, in chain order
-    constexpr int PER = (D * D + NTH - 1) / NTH;
-    const float dec = powi(a.lam[h], a.blk_pow * a.G), dec1 = dec * powi(a.lam[h], a.blk_pow);
-    const float* g = a.seg_state + (size_t)bh * a.nseg * D * D;
-    float acc[PER];
+  // S(e0) of the segment's first block -> the owners' registers and the
+  // hi/lo copies in LDS; with publish it is gathered after the window, from
+  // the earlier segments' published states
+  if (!PUB && wid / O::NT < O::RG) {
+    const int ct = wid % O::NT, ar = wid / O::NT, c = 16 * ct + l16;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
-#pragma unroll 4
-    for (int m = 1; m <= seg; ++m) {
-      const float dm = m - 1 < a.R ? dec1 : dec;
+    for (int k = 0; k < O::AT; ++k) so.s[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (seg > 0 && a.prefix_direct) {
+      // S at the segment start from the local states L_m (stored at index m+1):
+      // S_{m+1} = lambda^(blk_pow blocks(m)) S_m + L_m, in chain order
+      const float dec = powi(a.lam[h], a.blk_pow * a.G), dec1 = dec * powi(a.lam[h], a.blk_pow);
+      const float* g = a.seg_state + (size_t)bh * a.nseg * D * D;
+#pragma unroll 2
+      for (int m = 1; m <= seg; ++m) {
+        const float dm = m - 1 < a.R ? dec1 : dec;
 #pragma unroll
-      for (int k = 0; k < PER; ++k)
-        if ((D * D) % NTH == 0 || tid + NTH * k < D * D) acc[k] = dm * acc[k] + g[(size_t)m * D * D + tid + NTH * k];
+        for (int k = 0; k < O::AT; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            so.s[k][i] = dm * so.s[k][i] + g[(size_t)m * D * D + (16 * (ar * O::AT + k) + 4 * lg + i) * D + c];
+      }
+    } else if (seg > 0) {
+      const float* g = a.seg_state + ((size_t)bh * a.nseg + seg) * D * D;
+#pragma unroll
+      for (int k = 0; k < O::AT; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) so.s[k][i] = g[(16 * (ar * O::AT + k) + 4 * lg + i) * D + c];
     }
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int x = tid + NTH * k;
-      if ((D * D) % NTH == 0 || x < D * D) Sl[(x % D) * LDS + x / D] = acc[k];
-    }
-  } else {
-    const float* g = a.seg_state + ((size_t)bh * a.nseg + seg) * D * D;
-    for (int x = tid; x < D * D; x += NTH) Sl[(x % D) * LDS + x / D] = g[x];
+    own_publish(so, Sh, Sm, LDH, wid, l16, lg);
   }
 
   if (PUB) {
@@ -494,8 +540,8 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
           const int len = pub ? 64 : min(64, T - t0 - 64 * c);
           if (c <= it && len > 0) {
             const int ub = kv_used - it + c;
-            state_update(st, (const E*)(smem + (ub & 1) * L::BUF), LDK, (const E*)(smem + (ub & 1) * L::BUF + L::KT),
-                         LDV, pw, len, e0 + 64 * c, wid, l16, lg);
+            state_update_z(st, (const E*)(smem + (ub & 1) * L::BUF), LDK,
+                           (const E*)(smem + (ub & 1) * L::BUF + L::KT), LDV, pw, len, wid, l16, lg);
           }
         }
         if (pub)
@@ -585,23 +631,18 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
           chunk_tile(c, Kc, Vc);
           f32x4 Z[2][4];
           scores(Z, Kc);
+          // weight of row r and chunk key ci: wtab[128 + r - ci] (0 for ci > r); keys
+          // before token 0 were loaded as zeros (Z = 0).  One base per lane, the
+          // 32 weights at immediate offsets 51 + 16 (g - n) - i from it.
+          const float* wb = wtab + (BM + rw + l16 - 4 * lg - 64 * c - 51);
           float P[2][16];
 #pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            int r = rw + 16 * g + l16;  // row within the block
-            // (opaque here, so the 16 weights' masks and LDS offsets are formed at
-            // their use instead of being kept, or spilled, across the block loop)
-            asm volatile("" : "+v"(r));
+          for (int g = 0; g < 2; ++g)
 #pragma unroll
             for (int n = 0; n < 4; ++n)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int ci = 64 * c + 16 * n + 4 * lg + i;  // index within the chunk
-                // (branch-free: the LDS read is unconditional, at a clamped index)
-                const float on = (ci <= r && e0 + ci >= 0) ? seta : 0.0f;
-                P[g][8 * (n >> 1) + 4 * (n & 1) + i] = on * pw[max(r - ci, 0)] * Z[g][n][i];
-              }
-          }
+              for (int i = 0; i < 4; ++i)
+                P[g][8 * (n >> 1) + 4 * (n & 1) + i] = wb[51 + 16 * (g - n) - i] * Z[g][n][i];
           accum_pv(P, std::false_type{}, Vc);
         }
       }
@@ -621,9 +662,13 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
         }
         const bool ran_out = __syncthreads_or(!seen);
         state_gather_all(acc, pw[BM], slots, m_lo + 1, seg + 1, wid, lane);
-        if (ran_out) state_fill(acc, __builtin_nanf(""));
+        if (ran_out) state_fill(acc, __uint_as_float(0x7fc00000u));  // quiet NaN (bit pattern: no NaN literal here)
         timed_out = ran_out;
-        state_to_lds_t<E, D, LDS>(acc, Sl, wid, l16, lg);
+#pragma unroll
+        for (int o = 0; o < State<E, D>::NOWN; ++o)
+          if (wid + 4 * o < NT)
+#pragma unroll
+            for (int at = 0; at < NT; ++at) put_hilo(Sh, Sm, LDH, 16 * (wid + 4 * o) + l16, 16 * at + 4 * lg, acc.s[o][at]);
       }
       if (last && a.A_final) {
         // A after step T-1 = eta (lambda^n S(e0) + L), n = T - t0 evictions in
@@ -646,19 +691,9 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
 #pragma unroll
         for (int dc = 0; dc < NKC; ++dc) {
           const bool in = dc * 32 + lg * 8 < D;  // D = 16: upper half of the contraction is empty
-          float sv[8];
-          {
-            const float* p = Sl + (dt * 16 + l16) * LDS + dc * 32 + lg * 8;
-            const f32x4 x0 = in ? *(const f32x4*)p : f32x4{0.f, 0.f, 0.f, 0.f};
-            const f32x4 x1 = in ? *(const f32x4*)(p + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              sv[i] = x0[i];
-              sv[4 + i] = x1[i];
-            }
-          }
-          frag shi, slo;
-          M::split(sv, shi, slo);
+          const int off = (dt * 16 + l16) * LDH + dc * 32 + lg * 8;
+          const frag shi = in ? M::lds8(Sh + off) : M::zero();
+          const frag slo = in ? M::lds8(Sm + off) : M::zero();
           acc[0] = M::mma(shi, qf[0][dc], acc[0]);
           acc[1] = M::mma(shi, qf[1][dc], acc[1]);
           if (M::kSplit) {
@@ -685,12 +720,18 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
           for (nw = 0; nw < NCH && t0 + (MEANC > 0 ? MEANC : 1) * (nw + 1) <= T; ++nw) {
           }
         const float lam = pw[1];
-        for (int x = tid; x < D * D; x += NTH) {
-          const int ar = x % D, c = x / D;
-          float sv = Sl[c * LDS + ar];
-          for (int m = 0; m < nw; ++m) sv = lam * sv + cm[2 * m * D + ar] * cm[(2 * m + 1) * D + c];
-          Sl[c * LDS + ar] = sv;
+        if (wid / O::NT < O::RG) {
+          const int ct = wid % O::NT, arow = wid / O::NT, c = 16 * ct + l16;
+          for (int m = 0; m < nw; ++m) {
+            const float vc = cm[(2 * m + 1) * D + c];
+#pragma unroll
+            for (int k = 0; k < O::AT; ++k)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                so.s[k][i] = lam * so.s[k][i] + cm[2 * m * D + 16 * (arow * O::AT + k) + 4 * lg + i] * vc;
+          }
         }
+        own_publish(so, Sh, Sm, LDH, wid, l16, lg);
       } else {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -698,9 +739,10 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
           if (c < cb.nlate && len > 0) {
             const E *Kc, *Vc;
             chunk_tile(c, Kc, Vc);
-            lds_state_update<E, D, NW>(Sl, Kc, LDK, Vc, LDV, pw, len, e0 + 64 * c, wid, l16, lg);
+            own_state_update<E, D, NW>(so, Kc, LDK, Vc, LDV, pw, len, wid, l16, lg);
           }
         }
+        own_publish(so, Sh, Sm, LDH, wid, l16, lg);
       }
     }
 
@@ -720,9 +762,15 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
     }
     if (!PUB && last && a.A_final && !a.final_slot) {
       float* Af = a.A_final + (size_t)bh * D * D;
-      __syncthreads();  // the state updates above are done
+      // (from the owners' registers, after this block's updates)
       const float eta = a.eta[h];
-      for (int x = tid; x < D * D; x += NTH) Af[x] = has_mem ? eta * Sl[(x % D) * LDS + x / D] : 0.0f;
+      if (wid / O::NT < O::RG) {
+        const int ct = wid % O::NT, ar = wid / O::NT, c = 16 * ct + l16;
+#pragma unroll
+        for (int k = 0; k < O::AT; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Af[(16 * (ar * O::AT + k) + 4 * lg + i) * D + c] = has_mem ? eta * so.s[k][i] : 0.0f;
+      }
     }
   }
   if (a.status && tid == 0) a.status[wg] = timed_out ? ~a.gen : a.gen;

@@ -147,14 +147,14 @@ tc_status_t tc_forward_chunk_mean(const tc_shape_t* shape, const void* q, const 
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): the same arguments without the workspace, the same
  * kernels and results.  Instead of a caller's workspace it uses a static
- * device array of 16 MiB that the library holds on each GPU it runs on until
+ * device array of 32 MiB that the library holds on each GPU it runs on until
  * the process ends; it calls no hipMalloc, hipFree or other allocating
  * routine.  The array belongs to the current device (the stream must be one
  * of its streams); its address is looked up once per device on the first
  * call there.
  *   Limit: the shape's forward workspace (tc_forward_workspace_size) must be
- *   at most 16 MiB (16777216 bytes), else TC_ERR_WORKSPACE and nothing runs;
- *   e.g. B=8 H=8 T=1024 D=64 needs 9.4 MB and B=1 H=12 T=32768 D=64 8.5 MB.
+ *   at most 32 MiB (33554432 bytes), else TC_ERR_WORKSPACE and nothing runs;
+ *   e.g. B=8 H=8 T=1024 D=64 needs 9.4 MB and B=1 H=12 T=32768 D=64 25.4 MB.
  *   Every call on one GPU shares its array and leaves its contents there (no
  *   part of it needs clearing: stale flags never match a later call's flag
  *   value).  Calls that overlap in time on one GPU (other streams, other

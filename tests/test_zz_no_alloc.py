@@ -2,7 +2,7 @@
 the C ABI, against tc_forward on the same inputs: two calls in a row, the
 second with a smaller shape, each bit-identical to tc_forward's outputs (the
 same kernels and plan, only the workspace differs) and within the parity
-bars of the oracle; a shape whose workspace exceeds the 16 MiB scratch is
+bars of the oracle; a shape whose workspace exceeds the 32 MiB scratch is
 refused before anything runs."""
 import numpy as np
 import pytest
