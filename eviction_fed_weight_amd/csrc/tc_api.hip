@@ -151,7 +151,8 @@ float scale_of(float scale, int D) { return scale > 0.0f ? scale : 1.0f / sqrtf(
 tc_status_t launch_fwd(const tc_shape_t& s, const Plan& p, const void* q, const void* k, const void* v,
                        const float* lambda, const float* eta, const float* gate, void* y, float* A_final,
                        float* lse, void* ws, bool ws_ok, int row0, const float* yadd, hipStream_t stream,
-                       int mean_c = 0) {
+                       int mean_c = 0, const void* k_ring = nullptr, const void* v_ring = nullptr,
+                       int ring_s0 = 0, const float* A_in = nullptr) {
   tck::FwdArgs a{};
   a.mean_c = mean_c;
   a.q = q;
@@ -178,7 +179,11 @@ tc_status_t launch_fwd(const tc_shape_t& s, const Plan& p, const void* q, const 
   a.nseg = p.nseg;
   a.scale = scale_of(s.scale, s.D);
   a.row0 = row0;
+  a.k_ring = k_ring;
+  a.v_ring = v_ring;
+  a.ring_s0 = ring_s0;
   a.yadd = yadd;
+  a.A_in = A_in;
   const bool is_bf16 = s.dtype == TC_BF16;
   const hipError_t e = fwd_block(s.D, s.dtype) == 128 ? tck::launch_forward_rows(a, s.D, is_bf16, stream)
                                                        : tck::launch_forward(a, s.D, is_bf16, stream);
@@ -239,12 +244,12 @@ void* scratch_ptr() {
 }
 
 // Continuation workspace: the forward's workspace for the extended shape,
-// the extended q/k/v, the initial-state read and the new evictions' state.
+// the initial-state read and the new evictions' state.
 struct ContPlan {
   tc_shape_t x;  // extended shape (T = p + new tokens)
   Plan fp;
   int p;
-  size_t off_fwd, off_q, off_k, off_v, off_yinit, off_anew, total;
+  size_t off_fwd, off_yinit, off_anew, total;
 };
 
 tc_status_t cont_plan_for(const tc_shape_t* s, int64_t pos0, ContPlan& c) {
@@ -258,16 +263,11 @@ tc_status_t cont_plan_for(const tc_shape_t* s, int64_t pos0, ContPlan& c) {
   const tc_status_t sx = check_shape(&c.x);
   if (sx != TC_OK) return sx;
   const long long BH = (long long)s->B * s->H;
-  // grid of the preparation kernel: one workgroup per (b,h) and 128 new rows, plus up to 8192 copy workgroups
-  if (BH * ((s->T + 127) / 128) > (1LL << 31) - 1 - 8192) return TC_ERR_UNSUPPORTED;
+  // grid of the preparation kernel: one workgroup per (b,h) and 128 new rows
+  if (BH * ((s->T + 127) / 128) > (1LL << 31) - 1) return TC_ERR_UNSUPPORTED;
   c.fp = plan_for(c.x, c.p);
-  const size_t es = elem_size(s->dtype);
-  const size_t nx = align256((size_t)BH * c.x.T * s->D * es);
   c.off_fwd = 0;
-  c.off_q = fwd_ws_bytes(c.x, c.fp);
-  c.off_k = c.off_q + nx;
-  c.off_v = c.off_k + nx;
-  c.off_yinit = c.off_v + nx;
+  c.off_yinit = fwd_ws_bytes(c.x, c.fp);
   c.off_anew = c.off_yinit + align256((size_t)BH * s->T * s->D * 4);
   c.total = c.off_anew + align256((size_t)BH * s->D * s->D * 4);
   return TC_OK;
@@ -417,9 +417,6 @@ tc_status_t tc_forward_continue(const tc_shape_t* s, int64_t pos0, const void* q
   a.pos = pos;
   a.lam = lambda;
   a.gate = gate;
-  a.qx = w + c.off_q;
-  a.kx = w + c.off_k;
-  a.vx = w + c.off_v;
   a.yinit = (float*)(w + c.off_yinit);
   a.A_new = (const float*)(w + c.off_anew);
   a.pos0 = pos0;
@@ -431,10 +428,17 @@ tc_status_t tc_forward_continue(const tc_shape_t* s, int64_t pos0, const void* q
   a.p = c.p;
   a.Tx = c.x.T;
   a.esize = (int)es;
+  // Once the window is full (pos0 >= W) and W is a multiple of the forward's
+  // block rows, every processed block starts at or after eviction 0 of the
+  // extended sequence and the forward starts its scan from A (S(0) = A/eta);
+  // otherwise the read of A is formed here (yinit) and A is combined at the end.
+  a.fold = (pos0 >= s->W && s->W % fwd_block(s->D, s->dtype) == 0) ? 1 : 0;
   hipError_t e = tck::launch_continue_prep(a, (hipStream_t)stream);
   if (e != hipSuccess) return TC_ERR_HIP;
-  if (launch_fwd(c.x, c.fp, a.qx, a.kx, a.vx, lambda, eta, gate, y, (float*)(w + c.off_anew), lse,
-                 w + c.off_fwd, true, c.p, a.yinit, (hipStream_t)stream) != TC_OK)
+  // rows below p: ring slots (pos0 - p + r) mod W
+  const int s0 = (int)((pos0 - c.p) % s->W);
+  if (launch_fwd(c.x, c.fp, q, k, v, lambda, eta, gate, y, (float*)(w + c.off_anew), lse, w + c.off_fwd, true, c.p,
+                 a.fold ? nullptr : a.yinit, (hipStream_t)stream, 0, k_ring, v_ring, s0, a.fold ? A : nullptr) != TC_OK)
     return TC_ERR_HIP;
   e = tck::launch_continue_finish(a, (hipStream_t)stream);
   return e == hipSuccess ? TC_OK : TC_ERR_HIP;

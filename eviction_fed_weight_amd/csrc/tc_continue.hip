@@ -9,52 +9,30 @@
 // result of T such steps; here they run through the parallel forward:
 //
 //   * the forward kernels run over an extended sequence -- the ring's
-//     p = min(pos0, W) tokens in time order, then the new tokens -- with a
-//     zero start state and store only rows p .. p+T-1.  Its window rows are
-//     the true windows (the ring holds every key an output row can see) and
-//     its state holds exactly the pairs evicted during this call;
-//   * the memory carried in, A_in, is linear in the read: after n_t of this
-//     call's evictions it has decayed to lambda^n_t A_in, so each row adds
-//     sigmoid(g) lambda^n_t q_t A_in (formed here in float32 and added by the
-//     forward kernels before the output is rounded), and the final memory is
-//     the forward's state plus lambda^N A_in;
-//   * the last min(pos0 + T, W) tokens go back into their ring slots.
+//     p = min(pos0, W) tokens in time order, then the new tokens -- and store
+//     only rows p .. p+T-1.  They read it in place: keys and values of rows
+//     below p from their ring slots, the others from the caller's new tokens
+//     (no copy).  Its window rows are the true windows (the ring holds every
+//     key an output row can see) and its scan runs over exactly the pairs
+//     evicted during this call;
+//   * the memory carried in, A_in, decays by lambda per eviction of this call
+//     (n_t of them by step t).  Once the window is full (pos0 >= W) the
+//     extended sequence's evictions start at its row W = p, and when W is a
+//     multiple of the forward's block rows every processed block starts at
+//     or after that eviction: then the forward simply starts its scan from
+//     S(0) = A_in / eta ("fold"), and its final state is the new memory.
+//     Otherwise the scan starts from zero, the read of A_in,
+//     sigmoid(g) lambda^n_t q_t A_in, is formed here in float32 and added by
+//     the forward kernels before the output is rounded, and the final memory
+//     is the forward's state plus lambda^N A_in;
+//   * the last min(T, W) new tokens go into their ring slots (after the
+//     forward has read the ring).
 // Steps t < W evict nothing (the memory is left as it is), so
 // n_t = max(0, t + 1 - max(pos0, W)) for the step at position t.
 #include "tc_device.h"
 #include "tc_launch.h"
 
 namespace tck {
-
-// Extended sequence rows, one 16-byte vector per thread: row r < p is ring
-// slot (pos0 - p + r) mod W (its query row is zero: never stored), row
-// r >= p is new token r - p.
-__device__ __forceinline__ void cont_gather(const ContArgs& a, long long blk, long long nblk) {
-  const int nv = a.D * a.esize / 16;  // vectors per row
-  const long long total = (long long)a.B * a.H * a.Tx * nv;
-  for (long long i = blk * 256 + threadIdx.x; i < total; i += nblk * 256) {
-    const long long row = i / nv;
-    const int c = (int)(i - row * nv);
-    const long long bh = row / a.Tx;
-    const int r = (int)(row - bh * a.Tx);
-    uint4 qv, kv, vv;
-    if (r < a.p) {
-      const long long slot = (a.pos0 - a.p + r) % a.W;
-      const long long src = (bh * a.W + slot) * nv + c;
-      kv = ((const uint4*)a.k_ring)[src];
-      vv = ((const uint4*)a.v_ring)[src];
-      qv = make_uint4(0u, 0u, 0u, 0u);
-    } else {
-      const long long src = (bh * a.T + (r - a.p)) * nv + c;
-      qv = ((const uint4*)a.q)[src];
-      kv = ((const uint4*)a.k)[src];
-      vv = ((const uint4*)a.v)[src];
-    }
-    ((uint4*)a.qx)[i] = qv;
-    ((uint4*)a.kx)[i] = kv;
-    ((uint4*)a.vx)[i] = vv;
-  }
-}
 
 // yinit[b,h,t,:] = sigmoid(g_h) lambda_h^n_t q_t A_in[b,h] in float32, on
 // the matrix cores.  One workgroup (four waves) per (b,h) and 128 rows; A_in
@@ -113,20 +91,19 @@ __device__ __forceinline__ void cont_init_read(const ContArgs& a, int blk) {
   }
 }
 
-// One launch for both preparations (they are independent and overlap):
-// workgroups 0 .. nI-1 form the initial-state read, the others copy the
-// extended sequence.
+// The initial-state read: one workgroup per (b,h) and 128 new rows.  (Not
+// launched when the forward folds A_in into its scan.  A read-ahead of the
+// inputs into the last-level cache in this launch was measured: it cost more
+// than the forward gained from it.)
 template <class E, int D>
-__global__ void __launch_bounds__(256) cont_prep_kernel(ContArgs a, int nI) {
-  if ((int)blockIdx.x < nI)
-    cont_init_read<E, D>(a, blockIdx.x);
-  else
-    cont_gather(a, blockIdx.x - nI, gridDim.x - nI);
+__global__ void __launch_bounds__(256) cont_prep_kernel(ContArgs a) {
+  cont_init_read<E, D>(a, blockIdx.x);
 }
 
 // Workgroups 0 .. nA-1: A <- A_new + lambda^N A (N = evictions in this call),
-// elementwise.  The others: the last min(Tx, W) extended rows into their ring
-// slots.  Workgroup 0 also sets pos[b] = pos0 + T.
+// elementwise; A <- A_new when the forward started its scan from A (fold).  The others: the last min(T, W) new tokens' keys and values
+// into their ring slots (position mod W; the ring's other slots keep the
+// earlier tokens they hold).  Workgroup 0 also sets pos[b] = pos0 + T.
 __global__ void __launch_bounds__(256) cont_finish_kernel(ContArgs a, int nA) {
   if (a.pos && blockIdx.x == 0)
     for (int b = threadIdx.x; b < a.B; b += 256) a.pos[b] = a.pos0 + a.T;
@@ -136,23 +113,23 @@ __global__ void __launch_bounds__(256) cont_finish_kernel(ContArgs a, int nA) {
     const long long N = a.pos0 + a.T - first;
     for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)nA * 256) {
       const int h = (int)((i / DD) % a.H);
-      a.A[i] = __builtin_fmaf(powi(a.lam[h], N > 0 ? (int)N : 0), a.A[i], a.A_new[i]);
+      a.A[i] = a.fold ? a.A_new[i] : __builtin_fmaf(powi(a.lam[h], N > 0 ? (int)N : 0), a.A[i], a.A_new[i]);
     }
     return;
   }
   const int nv = a.D * a.esize / 16;
-  const int keep = a.Tx < a.W ? a.Tx : a.W;
+  const int keep = a.T < a.W ? a.T : a.W;
   const long long total = (long long)a.B * a.H * keep * nv;
   const long long nr = gridDim.x - nA;
   for (long long i = (long long)(blockIdx.x - nA) * 256 + threadIdx.x; i < total; i += nr * 256) {
     const long long row = i / nv;
     const int cc = (int)(i - row * nv);
     const long long bh = row / keep;
-    const int r = a.Tx - keep + (int)(row - bh * keep);  // extended row
-    const long long slot = (a.pos0 - a.p + r) % a.W;
-    const long long src = (bh * a.Tx + r) * nv + cc, dst = (bh * a.W + slot) * nv + cc;
-    ((uint4*)a.k_ring)[dst] = ((const uint4*)a.kx)[src];
-    ((uint4*)a.v_ring)[dst] = ((const uint4*)a.vx)[src];
+    const int t = a.T - keep + (int)(row - bh * keep);  // new token
+    const long long slot = (a.pos0 + t) % a.W;
+    const long long src = (bh * a.T + t) * nv + cc, dst = (bh * a.W + slot) * nv + cc;
+    ((uint4*)a.k_ring)[dst] = ((const uint4*)a.k)[src];
+    ((uint4*)a.v_ring)[dst] = ((const uint4*)a.v)[src];
   }
 }
 
@@ -164,14 +141,13 @@ unsigned copy_grid(long long vectors) {
 
 template <class E>
 hipError_t launch_prep(const ContArgs& a, hipStream_t s) {
-  const int nI = (int)((long long)a.B * a.H * ((a.T + 127) / 128));  // (bounded on the host)
-  const unsigned nG = copy_grid((long long)a.B * a.H * a.Tx * (a.D * a.esize / 16));
-  const dim3 grid(nI + nG);
+  if (a.fold) return hipSuccess;
+  const dim3 grid((unsigned)((long long)a.B * a.H * ((a.T + 127) / 128)));  // (bounded on the host)
   switch (a.D) {
-    case 16: hipLaunchKernelGGL((cont_prep_kernel<E, 16>), grid, dim3(256), 0, s, a, nI); break;
-    case 32: hipLaunchKernelGGL((cont_prep_kernel<E, 32>), grid, dim3(256), 0, s, a, nI); break;
-    case 64: hipLaunchKernelGGL((cont_prep_kernel<E, 64>), grid, dim3(256), 0, s, a, nI); break;
-    case 128: hipLaunchKernelGGL((cont_prep_kernel<E, 128>), grid, dim3(256), 0, s, a, nI); break;
+    case 16: hipLaunchKernelGGL((cont_prep_kernel<E, 16>), grid, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((cont_prep_kernel<E, 32>), grid, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((cont_prep_kernel<E, 64>), grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((cont_prep_kernel<E, 128>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -184,7 +160,7 @@ hipError_t launch_continue_prep(const ContArgs& a, hipStream_t s) {
 
 hipError_t launch_continue_finish(const ContArgs& a, hipStream_t s) {
   const int nv = a.D * a.esize / 16;
-  const long long keep = a.Tx < a.W ? a.Tx : a.W;
+  const long long keep = a.T < a.W ? a.T : a.W;
   const unsigned nA = copy_grid((long long)a.B * a.H * a.D * a.D);
   const unsigned nR = copy_grid((long long)a.B * a.H * keep * nv);
   hipLaunchKernelGGL(cont_finish_kernel, dim3(nA + nR), dim3(256), 0, s, a, (int)nA);

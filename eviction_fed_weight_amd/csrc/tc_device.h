@@ -10,6 +10,8 @@
 //   same 32 contraction indices with the same lane assignment.
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -212,6 +214,16 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t rs, int byte_
   return uint4{(uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]};
 }
 
+// Key or value rows of a sequence that may continue an earlier one: rows
+// r >= p are rows r - p of `cur` (this call's tokens); rows 0 <= r < p are the
+// ring slots (s0 + r) mod W of `ring` (the re-read window of a continuation,
+// in time order); rows r < 0 and rows past the end read as zeros.  p = 0 for a
+// sequence that starts at token 0.
+struct SeqRows {
+  __amdgpu_buffer_rsrc_t cur, ring;
+  int p, s0, W;
+};
+
 // Unrolled copy of NR rows of a row-major [T][D] matrix by NTH threads: load() issues every
 // global load of the tile at once (through a buffer resource covering the
 // sequence, so out-of-range rows read as zero) so they can be in flight while
@@ -246,6 +258,59 @@ struct TileRegs {
   }
 };
 
+
+// Tile load from a sequence: RING = false for a sequence that starts at
+// token 0 (no prefix: the plain single-resource load, nothing else in the
+// kernel's code), RING = true for a continuation that re-reads the ring.
+template <bool RING, class TR>
+__device__ __forceinline__ void load_seq(TR& t, const SeqRows& s, int r0) {
+  if constexpr (RING)
+    t.load(s, r0);
+  else
+    t.load(s.cur, r0);
+}
+
+// TileRegs for rows of a continued sequence (SeqRows): each vector is read
+// from the ring or from the current tokens with a pair of loads, of which the
+// other is out of range and returns zero; the pair is combined only in
+// store(), a pipeline step later, so that no wait follows the loads.
+template <class E, int D, int NR, int NTH = 256>
+struct SeqTileRegs {
+  using Base = TileRegs<E, D, NR, NTH>;
+  static constexpr int VE = Base::VE, VPR = Base::VPR, NV = Base::NV, PER = Base::PER;
+  uint4 v[PER], w[PER];
+  __device__ __forceinline__ void load(const SeqRows& s, int r0) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int x = (int)threadIdx.x + NTH * p;
+      const int row = x / VPR;
+      const int col = (x - row * VPR) * VE;
+      const int rr = r0 + row;
+      const bool in = NV % NTH == 0 || x < NV;
+      int slot = s.s0 + rr;  // (s0 < W and rr < p <= W)
+      if (slot >= s.W) slot -= s.W;
+      const int oc = (in && rr >= s.p) ? ((rr - s.p) * D + col) * (int)sizeof(E) : -16;
+      const int orr = (in && rr >= 0 && rr < s.p) ? (slot * D + col) * (int)sizeof(E) : -16;
+      v[p] = buf_load16(s.cur, oc);
+      w[p] = buf_load16(s.ring, orr);
+    }
+  }
+  __device__ __forceinline__ void store(E* lds, int ld) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int x = (int)threadIdx.x + NTH * p;
+      const int row = x / VPR;
+      const int col = (x - row * VPR) * VE;
+      if (NV % NTH == 0 || x < NV)
+        *(uint4*)(lds + row * ld + col) = uint4{v[p].x | w[p].x, v[p].y | w[p].y, v[p].z | w[p].z, v[p].w | w[p].w};
+    }
+  }
+};
+
+// Staging registers of a key/value tile: plain for a sequence from token 0,
+// SeqTileRegs for a continuation that re-reads the ring.
+template <bool RING, class E, int D, int NR, int NTH = 256>
+using KVRegs = typename std::conditional<RING, SeqTileRegs<E, D, NR, NTH>, TileRegs<E, D, NR, NTH>>::type;
 
 // Workgroup b of a grid of n runs on XCD b % 8 (the eight chiplets take
 // workgroups in turn, each with its own L2).  Renumber so that each XCD gets

@@ -69,7 +69,9 @@ struct FwdLds {
 // one), which keeps every accumulator in VGPRs and uses no AGPR at all.
 //
 // Fused forward: grid = BH * nseg, 256 threads (4 waves x 16 query rows).
-template <class E, int D>
+// RING: a continuation (row0 > 0) whose first row0 keys and values are read
+// from the ring.
+template <class E, int D, bool RING = false>
 __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a) {
   using M = Mfma<E>;
   using frag = typename M::frag;
@@ -90,26 +92,30 @@ __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128
   const int bh = blockIdx.x / a.nseg, seg = blockIdx.x - bh * a.nseg;
   const int h = bh % a.H;
   const int T = a.T, W = a.W;
-  const size_t base = (size_t)bh * T * D;
-  const uint32_t nbytes = (uint32_t)T * D * sizeof(E);
-  const auto Qg = make_rsrc((const E*)a.q + base, nbytes);
-  const auto Kg = make_rsrc((const E*)a.k + base, nbytes);
-  const auto Vg = make_rsrc((const E*)a.v + base, nbytes);
+  const auto Qg = query_rows<E, D>(a, bh);  // (query row t is row t - row0 of q)
+  const SeqRows Kg = seq_rows<E, D>(a, a.k, a.k_ring, bh);
+  const SeqRows Vg = seq_rows<E, D>(a, a.v, a.v_ring, bh);
   const int Tout = T - a.row0;  // stored rows
   E* Yg = (E*)a.y + (size_t)bh * Tout * D;
   const float seta = sigmoidf(a.gate[h]) * a.eta[h];
   const float sl2 = a.scale * kLog2e;
   if (tid <= 64) pw[tid] = powi(a.lam[h], tid);
 
+  // S at the segment start: S(0) (zero, or A_in / eta) for the first segment
   State<E, D> st;
+  const float ie = 1.0f / a.eta[h];
+  const float* g0 = a.A_in ? a.A_in + (size_t)bh * D * D : nullptr;
   if (LS) {
     // S^T at the segment start -> LDS (read by every wave after the band loop's barriers)
     const float* g = a.seg_state + ((size_t)bh * a.nseg + seg) * D * D;
-    for (int x = tid; x < D * D; x += 256) Sl[(x % D) * LDSS + x / D] = seg == 0 ? 0.0f : g[x];
-  } else if (seg == 0) {
-    state_zero(st);
-  } else {
+    for (int x = tid; x < D * D; x += 256) Sl[(x % D) * LDSS + x / D] = seg > 0 ? g[x] : g0 ? ie * g0[x] : 0.0f;
+  } else if (seg > 0) {
     state_load(st, a.seg_state + ((size_t)bh * a.nseg + seg) * D * D, wid, l16, lg);
+  } else if (g0) {
+    state_load(st, g0, wid, l16, lg);
+    state_scale(st, ie);
+  } else {
+    state_zero(st);
   }
   vm_fence_loads();
 
@@ -117,15 +123,16 @@ __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128
   const int je = seg_first_block(a, seg + 1);
   const int r = wid * 16 + l16;  // this lane's row within the block
   if (a.status && tid == 0) a.status[blockIdx.x] = a.gen;  // (no flag waits in this kernel)
-  TileRegs<E, D, 64> ql, kl, vl;
-  if (!QA) ql.load(Qg, jb * 64);
+  TileRegs<E, D, 64> ql;
+  KVRegs<RING, E, D, 64> kl, vl;
+  if (!QA) ql.load(Qg, jb * 64 - a.row0);
   // Tiles are loaded one item ahead (in flight while the current one is
   // computed), except for float32 with D = 128 (QA), where the staging
   // registers of a prefetch would push the kernel past 256 registers: there
   // each tile is loaded right before it is stored.
   if (!QA) {
-    kl.load(Kg, (max(0, jb * 64 - W + 1) >> 6) * 64);
-    vl.load(Vg, (max(0, jb * 64 - W + 1) >> 6) * 64);
+    load_seq<RING>(kl, Kg, (max(0, jb * 64 - W + 1) >> 6) * 64);
+    load_seq<RING>(vl, Vg, (max(0, jb * 64 - W + 1) >> 6) * 64);
   }
   for (int j = jb; j < je; ++j) {
     const int t0 = j * 64;
@@ -135,9 +142,9 @@ __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128
     const bool more = j + 1 < je;
     const int next_k0 = (max(0, t0 + 64 - W + 1) >> 6) * 64;
     __syncthreads();
-    if (QA) ql.load(Qg, t0);  // (float32 D = 128: no registers to spare for a prefetch)
+    if (QA) ql.load(Qg, t0 - a.row0);  // (float32 D = 128: no registers to spare for a prefetch)
     ql.store(Qs, LDK);
-    if (!QA) ql.load(Qg, t0 + 64);  // next block's queries, in flight during this block
+    if (!QA) ql.load(Qg, t0 + 64 - a.row0);  // next block's queries, in flight during this block
     __syncthreads();
     frag qf[NKC];
 #pragma unroll
@@ -156,8 +163,8 @@ __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128
       const int k0 = kt * 64;
       if (kt > kt_lo || QA) __syncthreads();  // (QA: every wave has read its Q rows from the K buffer)
       if (QA) {
-        kl.load(Kg, k0);
-        vl.load(Vg, k0);
+        load_seq<RING>(kl, Kg, k0);
+        load_seq<RING>(vl, Vg, k0);
       }
       kl.store(Ks, LDK);
       vl.store(Vs, LDK);
@@ -165,8 +172,8 @@ __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128
       if (!QA) {
         // next tile of this block, else the evicted chunk, else the next block's first tile
         const int nr = (kt < kt_hi) ? k0 + 64 : (has_mem ? e0 : next_k0);
-        kl.load(Kg, nr);
-        vl.load(Vg, nr);
+        load_seq<RING>(kl, Kg, nr);
+        load_seq<RING>(vl, Vg, nr);
       }
       // scores, online softmax and P V for one 64-key tile; FULL: every key of
       // the tile is inside every row's window (no mask)
@@ -240,7 +247,7 @@ __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128
     const bool last = (j == a.nblk - 1);
     if (has_mem) {
       __syncthreads();  // every wave is done with the last band tile
-      if (LS && e0 > 0) {
+      if (LS && (e0 > 0 || g0)) {
         // O += sigma(g) eta lambda^(r+1) q S(e0), S^T read from LDS as hi/lo bf16
         const float f = seta * pw[r + 1];
 #pragma unroll
@@ -264,7 +271,7 @@ __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128
           }
           O[dt] += f * acc;
         }
-      } else if (e0 > 0) {
+      } else if (e0 > 0 || g0) {
         // (QS)^T for this wave's state columns and all 64 rows -> X[row][c]
 #pragma unroll
         for (int o = 0; o < NOWN; ++o) {
@@ -308,15 +315,15 @@ __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128
       }
       // evicted chunk e0 .. e0+63 (prefetched during the last band tile)
       if (QA) {
-        kl.load(Kg, e0);
-        vl.load(Vg, e0);
+        load_seq<RING>(kl, Kg, e0);
+        load_seq<RING>(vl, Vg, e0);
       }
       kl.store(Ks, LDK);
       vl.store(Vs, LDK);
       __syncthreads();
       if (!QA) {
-        kl.load(Kg, next_k0);
-        vl.load(Vg, next_k0);
+        load_seq<RING>(kl, Kg, next_k0);
+        load_seq<RING>(vl, Vg, next_k0);
       }
       f32x4 Z[4];
 #pragma unroll
@@ -385,11 +392,19 @@ static hipError_t launch_fwd_impl(const FwdArgs& a0, hipStream_t s) {
   if (a.mean_c != 0) return hipErrorInvalidValue;  // (the chunk-mean shortcut runs on the rows kernel only)
   a.blk_pow = 64;  // exact scan: one decay per evicted token of a 64-row block
   const int BH = a.B * a.H;
+  const bool ring = a.row0 > 0;
   if (a.nseg > 1) {
-    hipLaunchKernelGGL((seg_state_kernel<E, D, 64>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((seg_chain_kernel<D, 64>), dim3((D * D / 4 + kChainThreads - 1) / kChainThreads, BH), dim3(kChainThreads), 0, s, a);
+    if (ring)
+      hipLaunchKernelGGL((seg_state_kernel<E, D, 64, 0, true>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((seg_state_kernel<E, D, 64>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((seg_chain_kernel<D, 64>), dim3((D * D + kChainThreads - 1) / kChainThreads, BH),
+                       dim3(kChainThreads), 0, s, a);
   }
-  hipLaunchKernelGGL((fwd_kernel<E, D>), dim3(BH * a.nseg), dim3(256), 0, s, a);
+  if (ring)
+    hipLaunchKernelGGL((fwd_kernel<E, D, true>), dim3(BH * a.nseg), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<E, D>), dim3(BH * a.nseg), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -12,6 +12,27 @@
 
 namespace tck {
 
+// Keys (or values) of head bh: this call's rows from `cur` ([B,H,T-row0,D]),
+// the re-read window of a continuation from the ring ([B,H,W,D]).
+template <class E, int D>
+__device__ __forceinline__ SeqRows seq_rows(const FwdArgs& a, const void* cur, const void* ring, int bh) {
+  const int tn = a.T - a.row0;
+  SeqRows r;
+  r.cur = make_rsrc((const E*)cur + (size_t)bh * tn * D, (uint32_t)tn * D * sizeof(E));
+  r.ring = a.row0 > 0 ? make_rsrc((const E*)ring + (size_t)bh * a.W * D, (uint32_t)a.W * D * sizeof(E)) : r.cur;
+  r.p = a.row0;
+  r.s0 = a.ring_s0;
+  r.W = a.W;
+  return r;
+}
+// Queries of head bh: row t of the sequence is row t - row0 of q (rows
+// below row0 read as zeros).
+template <class E, int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t query_rows(const FwdArgs& a, int bh) {
+  const int tn = a.T - a.row0;
+  return make_rsrc((const E*)a.q + (size_t)bh * tn * D, (uint32_t)tn * D * sizeof(E));
+}
+
 // S[o][at] holds rows a = 16*at + 4*lg + i, column c = 16*(wid + 4*o) + l16.
 template <class E, int D>
 struct State {
@@ -110,6 +131,14 @@ __device__ __forceinline__ void state_zero(State<E, D>& st) {
   for (int o = 0; o < State<E, D>::NOWN; ++o)
 #pragma unroll
     for (int at = 0; at < D / 16; ++at) st.s[o][at] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+template <class E, int D>
+__device__ __forceinline__ void state_scale(State<E, D>& st, float x) {
+#pragma unroll
+  for (int o = 0; o < State<E, D>::NOWN; ++o)
+#pragma unroll
+    for (int at = 0; at < D / 16; ++at) st.s[o][at] *= x;
 }
 
 template <class E, int D>
@@ -360,7 +389,10 @@ __device__ __forceinline__ void store4(float* dst, f32x4 x) { *(f32x4*)dst = x; 
 // only the chunks complete by step T-1.  Segment starts are multiples of
 // MEANC evictions (the launcher requires W to be one), so chunks never
 // straddle segments.
-template <class E, int D, int BM, int MEANC = 0>
+//
+// RING: a continuation (row0 > 0) whose first row0 keys and values are read
+// from the ring.
+template <class E, int D, int BM, int MEANC = 0, bool RING = false>
 __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
   constexpr int LDK = D + 16 / (int)sizeof(E);
   constexpr int TILE = 64 * LDK * (int)sizeof(E);
@@ -375,14 +407,12 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
   const int bh = blockIdx.x / nm, m = blockIdx.x - bh * nm;
   const bool fin = m == a.nseg - 1;  // the last segment's evictions (final_slot only)
   const int h = bh % a.H;
-  const size_t base = (size_t)bh * a.T * D;
-  const uint32_t nbytes = (uint32_t)a.T * D * sizeof(E);
-  const auto Kg = make_rsrc((const E*)a.k + base, nbytes);
-  const auto Vg = make_rsrc((const E*)a.v + base, nbytes);
+  const SeqRows Kg = seq_rows<E, D>(a, a.k, a.k_ring, bh);
+  const SeqRows Vg = seq_rows<E, D>(a, a.v, a.v_ring, bh);
   if (tid < 64 + 65) pwt[tid] = tid >= 64 ? powi(a.lam[h], tid - 64) : 0.0f;
   State<E, D> st;
   state_zero(st);
-  TileRegs<E, D, 64> kl, vl;
+  KVRegs<RING, E, D, 64> kl, vl;
   const int tb = seg_first_block(a, m) * BM;  // first row of segment m
   const int ntile = seg_blocks(a, m) * (BM / 64);
   const int ebase = tb - a.W;
@@ -390,8 +420,8 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
   auto tile_len = [&](int t) { return fin ? min(64, a.T - tb - 64 * t) : 64; };
   int t0 = 0;
   while (t0 < ntile && ebase + 64 * t0 + 63 < 0) ++t0;  // tiles wholly before the first token
-  kl.load(Kg, ebase + 64 * t0);
-  vl.load(Vg, ebase + 64 * t0);
+  load_seq<RING>(kl, Kg, ebase + 64 * t0);
+  load_seq<RING>(vl, Vg, ebase + 64 * t0);
   float run = 0.0f;  // MEANC: column sum of the running chunk (thread c < D: keys, D <= c < 2D: values)
   for (int t = t0; t < ntile; ++t) {
     const int e0 = ebase + 64 * t;
@@ -400,8 +430,8 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
     vl.store(Vs, LDK);
     __syncthreads();
     if (t + 1 < ntile) {
-      kl.load(Kg, e0 + 64);
-      vl.load(Vg, e0 + 64);
+      load_seq<RING>(kl, Kg, e0 + 64);
+      load_seq<RING>(vl, Vg, e0 + 64);
     }
     if (MEANC == 0) {
       const int len = tile_len(t);
@@ -426,39 +456,36 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
   state_store(st, dst, 1.0f, wid, l16, lg);
 }
 
-// Chain over segments, in place: seg_state[0] = 0 and
+// Chain over segments, in place: seg_state[0] = S(0) (zero, or A_in / eta) and
 // seg_state[m+1] = lambda^(blk_pow blocks(m)) seg_state[m] + L_m (blk_pow:
 // decays per block, BM for the exact scan, BM / C for the chunk-mean shortcut).
-// grid = (D*D/4 + 63)/64 x BH of one wave (kChainThreads) each (the pass moves two D x D
-// states per segment; small workgroups spread it over many compute units);
-// each thread owns four consecutive floats and loads 32 segments ahead of the
-// dependent chain.
+// grid = (D*D / kChainThreads) x BH of one wave each: one thread per state
+// element, so that a head's D*D chains run on D*D/64 waves spread over the
+// compute units, and each thread issues the loads of 64 segments at once
+// before walking its dependent chain through them (the walk is bound by how
+// many loads are in flight, not by arithmetic).
 constexpr int kChainThreads = 64;  // workgroup size of seg_chain_kernel (its launches use it too)
 template <int D, int BM>
 __global__ void __launch_bounds__(kChainThreads) seg_chain_kernel(FwdArgs a) {
   const int bh = blockIdx.y;
   const int x = blockIdx.x * kChainThreads + threadIdx.x;
-  if (x * 4 >= D * D) return;
+  if (x >= D * D) return;
   // S_m = lambda^(blk_pow blocks(m-1)) S_{m-1} + L_{m-1}
   const float decay = powi(a.lam[bh % a.H], a.blk_pow * a.G), decay1 = decay * powi(a.lam[bh % a.H], a.blk_pow);
-  float4* p = (float4*)(a.seg_state + (size_t)bh * a.nseg * D * D) + x;
-  const size_t stride = (size_t)D * D / 4;
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  float* p = a.seg_state + (size_t)bh * a.nseg * D * D + x;
+  const size_t stride = (size_t)D * D;
+  float s = a.A_in ? a.A_in[(size_t)bh * D * D + x] / a.eta[bh % a.H] : 0.0f;  // S(0)
   p[0] = s;
-  constexpr int AHEAD = 32;
+  constexpr int AHEAD = 64;
   for (int m0 = 1; m0 < a.nseg; m0 += AHEAD) {
-    float4 l[AHEAD];
+    float l[AHEAD];
 #pragma unroll
     for (int u = 0; u < AHEAD; ++u)
       if (m0 + u < a.nseg) l[u] = p[(m0 + u) * stride];
 #pragma unroll
     for (int u = 0; u < AHEAD; ++u)
       if (m0 + u < a.nseg) {
-        const float dm = m0 + u - 1 < a.R ? decay1 : decay;
-        s.x = dm * s.x + l[u].x;
-        s.y = dm * s.y + l[u].y;
-        s.z = dm * s.z + l[u].z;
-        s.w = dm * s.w + l[u].w;
+        s = (m0 + u - 1 < a.R ? decay1 : decay) * s + l[u];
         p[(m0 + u) * stride] = s;
       }
   }

@@ -198,7 +198,10 @@ __device__ __forceinline__ void own_state_update(OwnS<D, NW>& so, const E* Ks, i
 //   lambda^(r / MEANC) q S(e0) + [MEANC = 64, r >= 64] <q, kbar_0> vbar_0
 // (kbar_0, vbar_0: the means of the block's first 64 evictions), and the
 // carry is BM / MEANC such writes.  No intra-chunk triangle.
-template <class E, int D, int NW, bool PUB, int MEANC = 0>
+//
+// RING: a continuation (row0 > 0) whose first row0 keys and values are read
+// from the ring.
+template <class E, int D, int NW, bool PUB, int MEANC = 0, bool RING = false>
 __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdArgs a) {
   using M = Mfma<E>;
   using frag = typename M::frag;
@@ -233,11 +236,12 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   const int bh = wg / a.nseg, seg = wg - bh * a.nseg;
   const int h = bh % a.H;
   const int T = a.T, W = a.W;
-  const size_t base = (size_t)bh * T * D;
-  const uint32_t nbytes = (uint32_t)T * D * sizeof(E);
-  const auto Qg = make_rsrc((const E*)a.q + base, nbytes);
-  const auto Kg = make_rsrc((const E*)a.k + base, nbytes);
-  const auto Vg = make_rsrc((const E*)a.v + base, nbytes);
+  const auto Qg = query_rows<E, D>(a, bh);
+  const SeqRows Kg = seq_rows<E, D>(a, a.k, a.k_ring, bh);
+  const SeqRows Vg = seq_rows<E, D>(a, a.v, a.v_ring, bh);
+  SeqRows Qr = Kg;  // the queries as a sequence whose rows below row0 read as zeros
+  Qr.cur = Qg;
+  Qr.ring = make_rsrc(a.q, 0);
   const int Tout = T - a.row0;  // stored rows
   E* Yg = (E*)a.y + (size_t)bh * Tout * D;
   const float seta = sigmoidf(a.gate[h]) * a.eta[h];
@@ -292,14 +296,19 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   int pj = jb, pidx = PUB ? NQ : 0;
   Blk pb = blk(jb);
   int kv_stored = 0;  // key/value items written to LDS so far (buffer parity)
-  TileRegs<E, D, 64, NTH> kr, vr;
+  KVRegs<RING, E, D, 64, NTH> kr, vr;
   auto load_next = [&]() {
     const bool q = pidx < NQ;
     const int ki = pidx - NQ;
     int r0 = q ? pb.t0 + 128 * pidx : pb.kb + 64 * tile_of(pb, ki);
     if (pj >= je) r0 = T + 64;  // past the end: reads zeros
-    kr.load(q ? Qg : Kg, r0);
-    vr.load(q ? Qg : Vg, q ? r0 + 64 : r0);
+    if constexpr (RING) {  // (a select of the sources, no branch: see TileRegs)
+      kr.load(q ? Qr : Kg, r0);
+      vr.load(q ? Qr : Vg, q ? r0 + 64 : r0);
+    } else {  // (row0 = 0)
+      kr.load(q ? Qg : Kg.cur, r0);
+      vr.load(q ? Qg : Vg.cur, q ? r0 + 64 : r0);
+    }
   };
   auto store_next = [&]() {
     if (pidx < NQ) {
@@ -328,7 +337,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   };
 
   TileRegs<E, D, BM, NTH> qr;
-  if (PUB) qr.load(Qg, jb * BM);
+  if (PUB) qr.load(Qg, jb * BM - a.row0);
   load_next();
 
   for (int x = tid; x < 2 * BM + 1; x += NTH) {
@@ -344,9 +353,18 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
     const int ct = wid % O::NT, ar = wid / O::NT, c = 16 * ct + l16;
 #pragma unroll
     for (int k = 0; k < O::AT; ++k) so.s[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (seg > 0 && a.prefix_direct) {
-      // S at the segment start from the local states L_m (stored at index m+1):
+    if (a.prefix_direct && (seg > 0 || a.A_in)) {
+      // S at the segment start from S(0) (zero, or A_in / eta) and the local
+      // states L_m (stored at index m+1):
       // S_{m+1} = lambda^(blk_pow blocks(m)) S_m + L_m, in chain order
+      if (a.A_in) {
+        const float* g0 = a.A_in + (size_t)bh * D * D;
+        const float ie = 1.0f / a.eta[h];
+#pragma unroll
+        for (int k = 0; k < O::AT; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) so.s[k][i] = ie * g0[(16 * (ar * O::AT + k) + 4 * lg + i) * D + c];
+      }
       const float dec = powi(a.lam[h], a.blk_pow * a.G), dec1 = dec * powi(a.lam[h], a.blk_pow);
       const float* g = a.seg_state + (size_t)bh * a.nseg * D * D;
 #pragma unroll 2
@@ -358,7 +376,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
           for (int i = 0; i < 4; ++i)
             so.s[k][i] = dm * so.s[k][i] + g[(size_t)m * D * D + (16 * (ar * O::AT + k) + 4 * lg + i) * D + c];
       }
-    } else if (seg > 0) {
+    } else if (!a.prefix_direct && (seg > 0 || a.A_in)) {  // (the chain ran: seg_state[0] = S(0))
       const float* g = a.seg_state + ((size_t)bh * a.nseg + seg) * D * D;
 #pragma unroll
       for (int k = 0; k < O::AT; ++k)
@@ -683,7 +701,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
       }
       __syncthreads();  // S(e0) in LDS for every wave
     }
-    if (has_mem && e0 > 0) {
+    if (has_mem && (e0 > 0 || a.A_in)) {
       // O += sigma(g) eta lambda^(r+1) q S(e0), S^T read from LDS as hi/lo bf16
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt) {
@@ -785,6 +803,12 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
     if (a.prefix_direct) {
+      if (a.A_in) {  // S(0) = A_in / eta
+        const float ie = 1.0f / a.eta[h];
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+          if ((D * D) % NTH == 0 || tid + NTH * k < D * D) acc[k] = ie * a.A_in[(size_t)bh * D * D + tid + NTH * k];
+      }
       const float dec = powi(a.lam[h], a.blk_pow * a.G), dec1 = dec * powi(a.lam[h], a.blk_pow);
       for (int m = 1; m <= last_seg; ++m) {
         const float dm = m - 1 < a.R ? dec1 : dec;
@@ -854,11 +878,12 @@ static hipError_t launch_rows_impl(const FwdArgs& a0, hipStream_t s) {
   // workgroups dispatched before it, so the waits end in any case.)
   // Not under graph capture: a replayed launch repeats this call's flag value,
   // so flags left by the previous replay would read as current.  Not for the
-  // chunk-mean shortcut, which always takes the state pass.
+  // chunk-mean shortcut, which always takes the state pass, nor for a scan
+  // that starts from a carried memory (A_in: the state pass adds it).
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   const bool capturing = hipStreamIsCapturing(s, &capture) != hipSuccess || capture != hipStreamCaptureStatusNone;
   a.publish = (MEANC == 0 && a.G == 1 && a.R == 0 && a.nseg > 1 && a.prefix_direct && a.flags != nullptr &&
-               !capturing && (long long)BH * a.nseg <= rows_resident_capacity<E, D, NW>())
+               !a.A_in && !capturing && (long long)BH * a.nseg <= rows_resident_capacity<E, D, NW>())
                   ? 1
                   : 0;
   // otherwise the state pass also forms the last block's local state (final
@@ -868,16 +893,29 @@ static hipError_t launch_rows_impl(const FwdArgs& a0, hipStream_t s) {
   // once, which is how the path of a wait that runs out is tested)
   const char* polls = getenv("TC_FORWARD_MAX_POLLS");
   a.max_polls = polls ? atoi(polls) : kPublishPolls;
+  const bool ring = a.row0 > 0;
   if (a.nseg > 1 && !a.publish) {
-    hipLaunchKernelGGL((seg_state_kernel<E, D, BM, MEANC>), dim3(BH * (a.nseg - 1 + a.final_slot)), dim3(256), 0, s,
-                       a);
+    if (ring)
+      hipLaunchKernelGGL((seg_state_kernel<E, D, BM, MEANC, true>), dim3(BH * (a.nseg - 1 + a.final_slot)),
+                         dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((seg_state_kernel<E, D, BM, MEANC>), dim3(BH * (a.nseg - 1 + a.final_slot)), dim3(256), 0,
+                         s, a);
     if (!a.prefix_direct)
-      hipLaunchKernelGGL((seg_chain_kernel<D, BM>), dim3((D * D / 4 + kChainThreads - 1) / kChainThreads, BH), dim3(kChainThreads), 0, s, a);
+      hipLaunchKernelGGL((seg_chain_kernel<D, BM>), dim3((D * D + kChainThreads - 1) / kChainThreads, BH),
+                         dim3(kChainThreads), 0, s, a);
   }
-  if (a.publish)
-    hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, true>), dim3(BH * a.nseg), dim3(64 * NW), 0, s, a);
-  else
-    hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, false, MEANC>), dim3(BH * a.nseg), dim3(64 * NW), 0, s, a);
+  const dim3 grid(BH * a.nseg), block(64 * NW);
+  if (MEANC == 0 && ring) {  // (continuations run the exact scan)
+    if (a.publish)
+      hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, true, 0, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, false, 0, true>), grid, block, 0, s, a);
+  } else if (a.publish) {
+    hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, true>), grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, false, MEANC>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -44,12 +44,22 @@ struct FwdArgs {
   // flag waits ran out (its rows and the final state are then NaN).  The
   // host reads them with tc_forward_status.
   unsigned long long* status;
-  // Output rows: query rows t >= row0 are stored at row t - row0 of y and lse
-  // ([B,H,T-row0,...]); rows below row0 (a continuation's re-read prefix) are
-  // computed but not stored.  yadd (nullable, float [B,H,T-row0,D]) is added
-  // to each stored row before rounding.  tc_forward: row0 = 0, yadd = null.
+  // Rows of the sequence: q, k and v hold rows row0 .. T-1 ([B,H,T-row0,D]);
+  // keys and values of rows 0 .. row0-1 (a continuation's re-read window) are
+  // the ring slots (ring_s0 + r) mod W of k_ring and v_ring ([B,H,W,D]).
+  // Query rows t >= row0 are stored at row t - row0 of y and lse
+  // ([B,H,T-row0,...]); rows below row0 have no queries and are not stored.
+  // yadd (nullable, float [B,H,T-row0,D]) is added to each stored row before
+  // rounding.  tc_forward: row0 = 0, no ring, yadd = null.
   int row0;
+  const void* k_ring;
+  const void* v_ring;
+  int ring_s0;
   const float* yadd;
+  // (nullable) memory carried in by a continuation whose first processed
+  // block starts at eviction 0 (row0 = W, a multiple of the block rows): the
+  // scan starts from S(0) = A_in / eta instead of zero.  [B,H,D,D] float.
+  const float* A_in;
   // Decays of the state per query block: BM (one per evicted token) for the
   // exact scan, BM / C for the chunk-mean shortcut (one per chunk).
   int blk_pow;
@@ -107,9 +117,9 @@ struct BwdArgs {
   float scale;
 };
 
-// Continuation of a sequence (T new tokens after pos0 seen ones) through an
-// extended sequence in the workspace: the ring's p = min(pos0, W) tokens in
-// time order, then the new tokens (Tx = p + T rows).
+// Continuation of a sequence (T new tokens after pos0 seen ones) as an
+// extended sequence: the ring's p = min(pos0, W) tokens in time order, then
+// the new tokens (Tx = p + T rows), read in place by the forward kernels.
 struct ContArgs {
   const void* q;  // [B,H,T,D] new tokens
   const void* k;
@@ -120,17 +130,17 @@ struct ContArgs {
   int64_t* pos;   // [B] nullable: set to pos0 + T
   const float* lam;
   const float* gate;
-  void* qx;       // [B,H,Tx,D] extended sequence (workspace)
-  void* kx;
-  void* vx;
   float* yinit;   // [B,H,T,D] sigmoid(g) lambda^n_t q_t A_in (workspace)
   const float* A_new;  // [B,H,D,D] memory of this call's evictions alone (workspace)
   long long pos0;
   int B, H, T, W, D, p, Tx;
   int esize;      // bytes per element of q/k/v and the rings
+  // 1: the forward starts its scan from A_in (pos0 >= W and W a multiple of
+  // its block rows), so there is no initial-state read and A <- A_new
+  int fold;
 };
 
-hipError_t launch_continue_prep(const ContArgs& a, hipStream_t s);    // extended sequence + initial-state read
+hipError_t launch_continue_prep(const ContArgs& a, hipStream_t s);    // initial-state read
 hipError_t launch_continue_finish(const ContArgs& a, hipStream_t s);  // A, ring and pos updates
 
 hipError_t launch_forward_bf16(const FwdArgs& a, int D, hipStream_t s);  // 64-row blocks: bf16 with D = 128

@@ -211,8 +211,12 @@ tc_status_t tc_decode_step(const tc_decode_shape_t* shape, const void* q, const 
  *   pos      [B] int64, out, nullable: set to pos0 + T (the decode position).
  *   y        [B,H,T,D] dtype, out.   lse [B,H,T] float32, out, nullable.
  *   ws       device workspace of at least tc_continue_workspace_size(shape,
- *            pos0) bytes (it holds the ring prefix and the new tokens as one
- *            extended sequence of min(pos0, W) + T rows).
+ *            pos0) bytes: the forward's segment states and flags for the
+ *            extended sequence of min(pos0, W) + T rows (the ring prefix, then
+ *            the new tokens, both read in place: nothing is copied), and
+ *            float32 room for the read of A when the forward cannot start its
+ *            scan from A (pos0 < W, or W not a multiple of the forward's
+ *            block rows: 128 for bf16 with D <= 64, else 64).
  * Every pointer must be 16-byte aligned.  Outputs (rings, A, pos, y, lse,
  * ws) must not overlap the inputs or each other.  The extended sequence is
  * subject to the tc_forward size limits (TC_ERR_UNSUPPORTED otherwise).

@@ -113,14 +113,15 @@ def test_continue_workspace_layout():
     """The continuation workspace is a forward workspace for the extended
     shape (p = min(pos0, W) ring rows + T new rows; whole blocks inside the
     prefix are not planned, so it is at most tc_forward's for that shape),
-    then the extended q, k and v, the float32 initial-state read [B,H,T,D] and
-    the float32 state of this call's evictions [B,H,D,D], each part rounded up
-    to 256 bytes."""
+    then the float32 initial-state read [B,H,T,D] and the float32 state of
+    this call's evictions [B,H,D,D], each part rounded up to 256 bytes (the
+    forward reads the ring and the new tokens in place: no copy of the
+    extended sequence)."""
     up = lambda n: -(-n // 256) * 256  # noqa: E731
     for (B, H, T, D, W, pos0, es, dt) in [(2, 4, 512, 64, 256, 1000, 2, tc.TC_BF16), (1, 3, 100, 16, 8, 5, 4, tc.TC_F32),
                                           (1, 2, 300, 128, 128, 0, 2, tc.TC_BF16)]:
         p = min(pos0, W)
-        tail = 3 * up(B * H * (T + p) * D * es) + up(B * H * T * D * 4) + up(B * H * D * D * 4)
+        tail = up(B * H * T * D * 4) + up(B * H * D * D * 4)
         fwd = tc.tc_continue_workspace_size(tc.make_shape(B, H, T, D, W, 64, 0.0, dt), pos0) - tail
         assert fwd > 0 and fwd % 256 == 0
         assert fwd <= tc.tc_forward_workspace_size(tc.make_shape(B, H, T + p, D, W, 64, 0.0, dt))
@@ -163,9 +164,9 @@ def test_continue_validation():
     s = tc.make_shape(2, 4, 512, 64, 256, 64)
     assert tc.tc_continue_workspace_size(s, -1) == 0
     assert tc.tc_continue_workspace_size(tc.make_shape(1, 1, 64, 48, 8, 8), 0) == 0
-    # the workspace grows with the ring prefix min(pos0, W) that joins the new tokens
-    assert tc.tc_continue_workspace_size(s, 0) < tc.tc_continue_workspace_size(s, 100) \
-        < tc.tc_continue_workspace_size(s, 256) == tc.tc_continue_workspace_size(s, 10 ** 12)
+    # the workspace depends on pos0 only through the ring prefix min(pos0, W) that joins the new tokens
+    assert all(tc.tc_continue_workspace_size(s, p0) > 0 for p0 in (0, 100, 256))
+    assert tc.tc_continue_workspace_size(s, 256) == tc.tc_continue_workspace_size(s, 10 ** 12)
     assert call(s, pos0=-1) == tc.TC_ERR_INVALID_ARGUMENT
     assert call(tc.make_shape(2, 4, 512, 48, 256, 64)) == tc.TC_ERR_UNSUPPORTED
     for name in ("q", "kr", "vr", "A", "y", "gate"):
