@@ -30,7 +30,11 @@ constexpr int kBlock = 64;  // backward: query rows per block = tokens per scan 
 // for bf16 with D <= 64, else 64 (four waves of 16 rows).  float32 inputs
 // run on the 64-row kernel, whose float32 build keeps every matrix-core
 // result in VGPRs (see the 16x16x4 float32 note in tc_forward.hip).
-int fwd_block(int D, int32_t dtype) { return (D <= 64 && dtype == TC_BF16) ? 128 : 64; }
+// Query rows per block of the forward: 128 for bf16 (the rows kernel for
+// D <= 64, eight waves of the fused kernel for D = 128), 64 for float32.
+int fwd_block(int D, int32_t dtype) { return dtype == TC_BF16 ? 128 : 64; }
+// bf16 with D <= 64 runs the rows kernel, everything else the fused kernel.
+bool rows_kernel(int D, int32_t dtype) { return D <= 64 && dtype == TC_BF16; }
 
 bool supported_d(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
 
@@ -97,7 +101,7 @@ Plan plan_for(const tc_shape_t& s, int row0 = 0) {
   // fastest (B=1 H=12 T=32768: 0.234 ms against 0.242 ms for the 42
   // segments of 6-7 blocks this model picks, and 0.253 ms for single blocks,
   // whose chain over 256 segments per head costs more than the updates save).
-  if (bm == 128 && bestG > 2 && BH * ((nb + 1) / 2) > slots) bestG = 2;
+  if (rows_kernel(s.D, s.dtype) && bestG > 2 && BH * ((nb + 1) / 2) > slots) bestG = 2;
   p.nseg = (nb + bestG - 1) / bestG;
   if (BH * p.nseg <= slots) {
     const long long fill = slots / BH < nb ? slots / BH : nb;
@@ -185,7 +189,7 @@ tc_status_t launch_fwd(const tc_shape_t& s, const Plan& p, const void* q, const 
   a.yadd = yadd;
   a.A_in = A_in;
   const bool is_bf16 = s.dtype == TC_BF16;
-  const hipError_t e = fwd_block(s.D, s.dtype) == 128 ? tck::launch_forward_rows(a, s.D, is_bf16, stream)
+  const hipError_t e = rows_kernel(s.D, s.dtype) ? tck::launch_forward_rows(a, s.D, is_bf16, stream)
                                                        : tck::launch_forward(a, s.D, is_bf16, stream);
   return e == hipSuccess ? TC_OK : TC_ERR_HIP;
 }

@@ -43,19 +43,32 @@ namespace tck {
 // staged in the K tile's buffer (QA: it is read into registers once per block,
 // before the first key tile is stored), so that the tiles and the float32
 // state fit in the 160 KB of LDS.
+//
+// Blocks of BMR query rows, 16 per wave.  bf16 with D = 128 runs 128-row
+// blocks on eight waves at one workgroup per compute unit (two waves per
+// SIMD, and every key/value tile staged in LDS serves 128 rows); its evicted
+// chunk is two 64-row tiles.  The other instances run 64-row blocks on four
+// waves.
 template <class E, int D>
 struct FwdLds {
   static constexpr bool LS = D == 128;                                  // state in LDS
   static constexpr bool QA = LS && !std::is_same<E, bf16>::value;       // Q staged in the K buffer
+  static constexpr int BMR = (std::is_same<E, bf16>::value && D == 128) ? 128 : 64;  // rows per block
+  static constexpr int NWV = BMR / 16;                                  // waves
+  static constexpr int NTH = 64 * NWV;                                  // threads
+  static constexpr int MINB = NWV == 8 ? 1 : 2;                         // workgroups per unit (launch bound)
+  static constexpr int NCH = BMR / 64;                                  // tiles of the evicted chunk
   static constexpr int VE = 16 / sizeof(E);
   static constexpr int LDK = D + VE;  // row stride of K, V, Q tiles
   static constexpr int LDX = D + 4;
   static constexpr int LDSS = D + 4;
   static constexpr int TILE = 64 * LDK * (int)sizeof(E);
+  static constexpr int QB = BMR * LDK * (int)sizeof(E);
   static constexpr int XB = 64 * LDX * 4;
   static constexpr int U = (LS || (2 * TILE) > XB) ? (2 * TILE) : XB;
   static constexpr int SB = LS ? D * LDSS * 4 : 0;
-  static constexpr int TOTAL = U + (QA ? 0 : TILE) + SB;  // + Q block (+ S^T)
+  static constexpr int TOTAL = U + (QA ? 0 : QB) + SB;  // + Q block (+ S^T)
+  static_assert(BMR == 64 || LS, "128-row blocks keep the state in LDS");
 };
 
 // ---------------------------------------------------------------------------
@@ -68,24 +81,25 @@ struct FwdLds {
 // bound of two workgroups per unit; with D = 128 the LDS still holds only
 // one), which keeps every accumulator in VGPRs and uses no AGPR at all.
 //
-// Fused forward: grid = BH * nseg, 256 threads (4 waves x 16 query rows).
+// Fused forward: grid = BH * nseg, NWV waves of 16 query rows each.
 // RING: a continuation (row0 > 0) whose first row0 keys and values are read
 // from the ring.
 template <class E, int D, bool RING = false>
-__global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128 ? 1 : 2)) fwd_kernel(FwdArgs a) {
+__global__ void __launch_bounds__((FwdLds<E, D>::NTH), (FwdLds<E, D>::MINB)) fwd_kernel(FwdArgs a) {
   using M = Mfma<E>;
   using frag = typename M::frag;
   using L = FwdLds<E, D>;
   constexpr int NT = D / 16, NKC = (D + 31) / 32, NOWN = State<E, D>::NOWN;
   constexpr int LDK = L::LDK, LDX = L::LDX;
+  constexpr int BMR = L::BMR, NTH = L::NTH, NCH = L::NCH;
   __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
-  __shared__ float pw[72];
+  __shared__ float pw[BMR + 8];  // pw[n] = lambda^n, 0 <= n <= BMR
   E* Ks = (E*)smem;
   E* Vs = (E*)(smem + L::TILE);
   float* X = (float*)smem;
   constexpr bool LS = L::LS, QA = L::QA;
   E* Qs = QA ? Ks : (E*)(smem + L::U);
-  float* Sl = (float*)(smem + L::U + (QA ? 0 : L::TILE));  // (LS only)
+  float* Sl = (float*)(smem + L::U + (QA ? 0 : L::QB));  // (LS only)
   constexpr int LDSS = L::LDSS;
 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
@@ -99,7 +113,7 @@ __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128
   E* Yg = (E*)a.y + (size_t)bh * Tout * D;
   const float seta = sigmoidf(a.gate[h]) * a.eta[h];
   const float sl2 = a.scale * kLog2e;
-  if (tid <= 64) pw[tid] = powi(a.lam[h], tid);
+  for (int x = tid; x <= BMR; x += NTH) pw[x] = powi(a.lam[h], x);
 
   // S at the segment start: S(0) (zero, or A_in / eta) for the first segment
   State<E, D> st;
@@ -108,7 +122,7 @@ __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128
   if (LS) {
     // S^T at the segment start -> LDS (read by every wave after the band loop's barriers)
     const float* g = a.seg_state + ((size_t)bh * a.nseg + seg) * D * D;
-    for (int x = tid; x < D * D; x += 256) Sl[(x % D) * LDSS + x / D] = seg > 0 ? g[x] : g0 ? ie * g0[x] : 0.0f;
+    for (int x = tid; x < D * D; x += NTH) Sl[(x % D) * LDSS + x / D] = seg > 0 ? g[x] : g0 ? ie * g0[x] : 0.0f;
   } else if (seg > 0) {
     state_load(st, a.seg_state + ((size_t)bh * a.nseg + seg) * D * D, wid, l16, lg);
   } else if (g0) {
@@ -123,28 +137,29 @@ __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128
   const int je = seg_first_block(a, seg + 1);
   const int r = wid * 16 + l16;  // this lane's row within the block
   if (a.status && tid == 0) a.status[blockIdx.x] = a.gen;  // (no flag waits in this kernel)
-  TileRegs<E, D, 64> ql;
-  KVRegs<RING, E, D, 64> kl, vl;
-  if (!QA) ql.load(Qg, jb * 64 - a.row0);
+  TileRegs<E, D, BMR, NTH> ql;
+  KVRegs<RING, E, D, 64, NTH> kl, vl;
+  if (!QA) ql.load(Qg, jb * BMR - a.row0);
   // Tiles are loaded one item ahead (in flight while the current one is
   // computed), except for float32 with D = 128 (QA), where the staging
   // registers of a prefetch would push the kernel past 256 registers: there
   // each tile is loaded right before it is stored.
   if (!QA) {
-    load_seq<RING>(kl, Kg, (max(0, jb * 64 - W + 1) >> 6) * 64);
-    load_seq<RING>(vl, Vg, (max(0, jb * 64 - W + 1) >> 6) * 64);
+    load_seq<RING>(kl, Kg, (max(0, jb * BMR - W + 1) >> 6) * 64);
+    load_seq<RING>(vl, Vg, (max(0, jb * BMR - W + 1) >> 6) * 64);
   }
   for (int j = jb; j < je; ++j) {
-    const int t0 = j * 64;
+    const int t0 = j * BMR;
     const int trow = t0 + r;
     const int e0 = t0 - W;
-    const bool has_mem = t0 + 63 >= W;
+    const bool has_mem = t0 + BMR - 1 >= W;
     const bool more = j + 1 < je;
-    const int next_k0 = (max(0, t0 + 64 - W + 1) >> 6) * 64;
+    const int next_k0 = (max(0, t0 + BMR - W + 1) >> 6) * 64;
+    const int R0 = t0 + 16 * wid;  // first row of this wave
     __syncthreads();
     if (QA) ql.load(Qg, t0 - a.row0);  // (float32 D = 128: no registers to spare for a prefetch)
     ql.store(Qs, LDK);
-    if (!QA) ql.load(Qg, t0 + 64 - a.row0);  // next block's queries, in flight during this block
+    if (!QA) ql.load(Qg, t0 + BMR - a.row0);  // next block's queries, in flight during this block
     __syncthreads();
     frag qf[NKC];
 #pragma unroll
@@ -158,7 +173,7 @@ __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128
 
     // ---- L1: band tiles ----
     const int kt_lo = max(0, t0 - W + 1) >> 6;
-    const int kt_hi = min(T - 1, t0 + 63) >> 6;
+    const int kt_hi = min(T - 1, t0 + BMR - 1) >> 6;
     for (int kt = kt_lo; kt <= kt_hi; ++kt) {
       const int k0 = kt * 64;
       if (kt > kt_lo || QA) __syncthreads();  // (QA: every wave has read its Q rows from the K buffer)
@@ -229,10 +244,14 @@ __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128
             O[dt] = M::mma(ColFrag<E>::read(Vs + (p * 32 + lg * 8) * LDK + dt * 16, LDK, l16), pf, O[dt]);
         }
       };
-      if ((k0 + 63 <= t0) && (k0 >= t0 + 64 - W))
-        tile(std::true_type{});
-      else
-        tile(std::false_type{});
+      // (per wave: no key of the tile in any of its rows' windows -> nothing
+      // to add; every key in every window -> no mask)
+      if (!(k0 > R0 + 15 || k0 + 63 <= R0 - W)) {
+        if ((k0 + 63 <= R0) && (k0 >= R0 + 16 - W))
+          tile(std::true_type{});
+        else
+          tile(std::false_type{});
+      }
     }
     {
       lrow = xsum4(lrow);
@@ -313,52 +332,62 @@ __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128
         }
         __syncthreads();
       }
-      // evicted chunk e0 .. e0+63 (prefetched during the last band tile)
-      if (QA) {
-        load_seq<RING>(kl, Kg, e0);
-        load_seq<RING>(vl, Vg, e0);
-      }
-      kl.store(Ks, LDK);
-      vl.store(Vs, LDK);
-      __syncthreads();
-      if (!QA) {
-        load_seq<RING>(kl, Kg, next_k0);
-        load_seq<RING>(vl, Vg, next_k0);
-      }
-      f32x4 Z[4];
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        Z[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int kr = 32 * (n >> 1) + (l16 >> 2) * 8 + (n & 1) * 4 + (l16 & 3);
-#pragma unroll
-        for (int dc = 0; dc < NKC; ++dc) {
-          const frag ka = (dc * 32 + lg * 8 < D) ? M::lds8(Ks + kr * LDK + dc * 32 + lg * 8) : M::zero();
-          Z[n] = M::mma(ka, qf[dc], Z[n]);
+      // evicted chunk e0 .. e0+BMR-1, as NCH tiles of 64 (each prefetched
+      // during the item before it): the intra-chunk terms of the read, then
+      // the carry of the state (every wave has read S(e0) above, before the
+      // barrier after the first chunk tile is stored)
+      for (int c = 0; c < NCH; ++c) {
+        const int ec = e0 + 64 * c;  // first eviction of chunk tile c
+        if (c > 0) __syncthreads();  // tile c-1 and its state update are done
+        if (QA) {
+          load_seq<RING>(kl, Kg, ec);
+          load_seq<RING>(vl, Vg, ec);
         }
-      }
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        float pv[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int c = 32 * p + lg * 8 + jj;  // chunk index of the key
-          const float z = Z[2 * p + (jj >> 2)][jj & 3];
-          pv[jj] = (c <= r && e0 + c >= 0) ? seta * pw[r - c] * z : 0.0f;
+        kl.store(Ks, LDK);
+        vl.store(Vs, LDK);
+        __syncthreads();
+        if (!QA) {
+          const int nr = c + 1 < NCH ? ec + 64 : next_k0;
+          load_seq<RING>(kl, Kg, nr);
+          load_seq<RING>(vl, Vg, nr);
         }
-        const frag pf = M::pack(pv);
+        if (16 * wid + 15 >= 64 * c) {  // (rows before the tile read none of its keys)
+          f32x4 Z[4];
 #pragma unroll
-        for (int dt = 0; dt < NT; ++dt)
-          O[dt] = M::mma(ColFrag<E>::read(Vs + (p * 32 + lg * 8) * LDK + dt * 16, LDK, l16), pf, O[dt]);
-      }
-      // carry the state to the next block (or to step T-1 for A_final); with
-      // the state in LDS every wave has read it (the barrier after the chunk
-      // tiles were stored) before the owners of its column tiles update it
-      if (more || (last && a.A_final)) {
-        const int len = more ? 64 : T - t0;
-        if (LS)
-          lds_state_update_cols<E, D, LDSS>(Sl, Ks, LDK, Vs, LDK, pw, len, e0, wid, l16, lg);
-        else
-          state_update(st, Ks, LDK, Vs, LDK, pw, len, e0, wid, l16, lg);
+          for (int n = 0; n < 4; ++n) {
+            Z[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int kr = 32 * (n >> 1) + (l16 >> 2) * 8 + (n & 1) * 4 + (l16 & 3);
+#pragma unroll
+            for (int dc = 0; dc < NKC; ++dc) {
+              const frag ka = (dc * 32 + lg * 8 < D) ? M::lds8(Ks + kr * LDK + dc * 32 + lg * 8) : M::zero();
+              Z[n] = M::mma(ka, qf[dc], Z[n]);
+            }
+          }
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            float pv[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+              const int cc = 64 * c + 32 * p + lg * 8 + jj;  // chunk index of the key
+              const float z = Z[2 * p + (jj >> 2)][jj & 3];
+              pv[jj] = (cc <= r && e0 + cc >= 0) ? seta * pw[r - cc] * z : 0.0f;
+            }
+            const frag pf = M::pack(pv);
+#pragma unroll
+            for (int dt = 0; dt < NT; ++dt)
+              O[dt] = M::mma(ColFrag<E>::read(Vs + (p * 32 + lg * 8) * LDK + dt * 16, LDK, l16), pf, O[dt]);
+          }
+        }
+        // carry the state to the next block (or to step T-1 for A_final)
+        if (more || (last && a.A_final)) {
+          const int len = more ? 64 : min(64, T - t0 - 64 * c);
+          if (len > 0) {
+            if (LS)
+              lds_state_update_cols<E, D, LDSS, L::NWV>(Sl, Ks, LDK, Vs, LDK, pw, len, ec, wid, l16, lg);
+            else
+              state_update(st, Ks, LDK, Vs, LDK, pw, len, ec, wid, l16, lg);
+          }
+        }
       }
     }
     // ---- store y ----
@@ -376,11 +405,11 @@ __global__ void __launch_bounds__(256, (std::is_same<E, bf16>::value && D >= 128
       if (LS) {
         __syncthreads();  // the state update above is done
         const float eta = a.eta[h];
-        for (int x = tid; x < D * D; x += 256) Af[x] = has_mem ? eta * Sl[(x % D) * LDSS + x / D] : 0.0f;
+        for (int x = tid; x < D * D; x += NTH) Af[x] = has_mem ? eta * Sl[(x % D) * LDSS + x / D] : 0.0f;
       } else if (has_mem) {
         state_store(st, Af, a.eta[h], wid, l16, lg);
       } else {
-        for (int x = tid; x < D * D; x += 256) Af[x] = 0.0f;
+        for (int x = tid; x < D * D; x += NTH) Af[x] = 0.0f;
       }
     }
   }
@@ -390,21 +419,22 @@ template <class E, int D>
 static hipError_t launch_fwd_impl(const FwdArgs& a0, hipStream_t s) {
   FwdArgs a = a0;
   if (a.mean_c != 0) return hipErrorInvalidValue;  // (the chunk-mean shortcut runs on the rows kernel only)
-  a.blk_pow = 64;  // exact scan: one decay per evicted token of a 64-row block
+  constexpr int BMR = FwdLds<E, D>::BMR, NTH = FwdLds<E, D>::NTH;
+  a.blk_pow = BMR;  // exact scan: one decay per evicted token of a block
   const int BH = a.B * a.H;
   const bool ring = a.row0 > 0;
   if (a.nseg > 1) {
     if (ring)
-      hipLaunchKernelGGL((seg_state_kernel<E, D, 64, 0, true>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((seg_state_kernel<E, D, BMR, 0, true>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((seg_state_kernel<E, D, 64>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((seg_chain_kernel<D, 64>), dim3((D * D + kChainThreads - 1) / kChainThreads, BH),
+      hipLaunchKernelGGL((seg_state_kernel<E, D, BMR>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((seg_chain_kernel<D, BMR>), dim3((D * D + kChainThreads - 1) / kChainThreads, BH),
                        dim3(kChainThreads), 0, s, a);
   }
   if (ring)
-    hipLaunchKernelGGL((fwd_kernel<E, D, true>), dim3(BH * a.nseg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_kernel<E, D, true>), dim3(BH * a.nseg), dim3(NTH), 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<E, D>), dim3(BH * a.nseg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((fwd_kernel<E, D>), dim3(BH * a.nseg), dim3(NTH), 0, s, a);
   return hipGetLastError();
 }
 

@@ -288,16 +288,16 @@ __device__ __forceinline__ void state_scale_add_lds_t(State<E, D>& st, float mul
 
 // S <- lambda^len S + sum_{c<len, e0+c>=0} lambda^(len-1-c) K[c,:]^T V[c,:] on
 // an LDS copy of S (float S^T: S[a][c] at Sl[c * LDSS + a]) for a 64-row
-// chunk whose K and V are row-major in LDS; four waves, wave w updating the
-// column tiles w, w + 4, ... (no state registers outside the update).
-template <class E, int D, int LDSS>
+// chunk whose K and V are row-major in LDS; NWAVES waves, wave w updating the
+// column tiles w, w + NWAVES, ... (no state registers outside the update).
+template <class E, int D, int LDSS, int NWAVES = 4>
 __device__ __forceinline__ void lds_state_update_cols(float* Sl, const E* Ks, int ldk, const E* Vs, int ldv,
                                                       const float* pw, int len, int e0, int wid, int l16, int lg) {
   using M = Mfma<E>;
   using frag = typename M::frag;
   constexpr int NT = D / 16;
   const float decay = pw[len];
-  for (int ct = wid; ct < NT; ct += 4) {
+  for (int ct = wid; ct < NT; ct += NWAVES) {
     f32x4 sc[NT];
     float* col = Sl + (16 * ct + l16) * LDSS + 4 * lg;
 #pragma unroll
