@@ -52,6 +52,8 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 struct Plan {
   int nblk, j0, G, R, nseg;  // segments of blocks j0..nblk-1: the first R of G + 1 blocks, the others of G
   size_t state_bytes;  // one [BH][nseg][D*D] float block
+  int nparts;          // workgroups per segment of the state pass (fused kernel)
+  size_t parts_bytes;  // their local states, [BH][nseg][nparts][D*D] float (nparts > 1)
 };
 
 // Workgroups of the fused forward kernel resident at once on an MI355X
@@ -111,17 +113,34 @@ Plan plan_for(const tc_shape_t& s, int row0 = 0) {
   p.R = nb - p.G * p.nseg;
   // segment states, then one last-block local state per (b,h)
   p.state_bytes = (size_t)BH * (p.nseg + 1) * s.D * s.D * sizeof(float);
+  // The fused kernel's segments are long (one workgroup per unit walks many
+  // blocks), so its state pass has few workgroups, each a long dependent walk
+  // over the segment's tiles: split each segment into up to four parts so
+  // that about three workgroups per compute unit share the walk.
+  p.nparts = 1;
+  p.parts_bytes = 0;
+  if (!rows_kernel(s.D, s.dtype) && p.nseg > 1) {
+    const long long want = (768 + BH * (p.nseg - 1) - 1) / (BH * (p.nseg - 1));
+    const int tiles = p.G * (bm / 64);
+    p.nparts = (int)(want < 4 ? want : 4);
+    if (p.nparts > tiles) p.nparts = tiles;
+    if (p.nparts < 1) p.nparts = 1;
+    if (p.nparts > 1) p.parts_bytes = (size_t)BH * p.nseg * p.nparts * s.D * s.D * sizeof(float);
+  }
   return p;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Forward workspace: the segment states, then one 64-bit flag per segment,
-// then one 64-bit status word per workgroup (one workgroup per segment).
+// then one 64-bit status word per workgroup (one workgroup per segment),
+// then the state pass's parts (fused kernel, when split).
 size_t fwd_flags_bytes(const tc_shape_t& s, const Plan& p) {
   return align256((size_t)s.B * s.H * p.nseg * sizeof(unsigned long long));
 }
-size_t fwd_ws_bytes(const tc_shape_t& s, const Plan& p) { return align256(p.state_bytes) + 2 * fwd_flags_bytes(s, p); }
+size_t fwd_ws_bytes(const tc_shape_t& s, const Plan& p) {
+  return align256(p.state_bytes) + 2 * fwd_flags_bytes(s, p) + align256(p.parts_bytes);
+}
 
 // Flag value of one forward call: a per-process random salt combined with a
 // call counter, so that flags left in a reused workspace by earlier calls,
@@ -171,6 +190,9 @@ tc_status_t launch_fwd(const tc_shape_t& s, const Plan& p, const void* q, const 
   a.seg_state = (float*)ws;
   a.flags = ws && ws_ok ? (unsigned long long*)((char*)ws + align256(p.state_bytes)) : nullptr;
   a.status = a.flags ? (unsigned long long*)((char*)a.flags + fwd_flags_bytes(s, p)) : nullptr;
+  // (the parts follow the status words; the workspace is required whenever nseg > 1)
+  a.nparts = (ws && ws_ok && p.nparts > 1) ? p.nparts : 1;
+  a.parts = a.nparts > 1 ? (float*)((char*)a.status + fwd_flags_bytes(s, p)) : nullptr;
   a.gen = next_generation();
   a.B = s.B;
   a.H = s.H;

@@ -201,6 +201,43 @@ struct ColFrag<float> {
   }
 };
 
+// Rows rb..rb+3 and rb+16..rb+19 at column c0 + l16 of a row-major LDS tile:
+// the 8 contraction values of the V operand for keys in the order the
+// score layout produces them (key 16 n + 4 lg + i sits at contraction index
+// 8 lg + 4 (n & 1) + i of the 32-key chunk n >> 1).
+template <class E>
+struct VFrag;
+template <>
+struct VFrag<bf16> {
+  static __device__ __forceinline__ bf16x8 read(const bf16* tile, int ld, int rb, int c0, int l16) {
+    const bf16* p0 = tile + (rb + (l16 >> 2)) * ld + c0 + 4 * (l16 & 3);
+    const bf16* p1 = p0 + 16 * ld;
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p1));
+    bf16x8 r;
+    const bf16* ea = (const bf16*)&a;
+    const bf16* eb = (const bf16*)&b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r[j] = ea[j];
+      r[j + 4] = eb[j];
+    }
+    return r;
+  }
+};
+template <>
+struct VFrag<float> {
+  static __device__ __forceinline__ f32x8 read(const float* tile, int ld, int rb, int c0, int l16) {
+    f32x8 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r[j] = tile[(rb + j) * ld + c0 + l16];
+      r[j + 4] = tile[(rb + 16 + j) * ld + c0 + l16];
+    }
+    return r;
+  }
+};
+
 // Buffer resource over `bytes` bytes at p: buffer loads at byte offsets
 // outside [0, bytes) return zero, so tile loads need no per-lane branches
 // (rows before the sequence start or past its end read as zeros).

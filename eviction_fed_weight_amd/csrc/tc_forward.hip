@@ -219,20 +219,26 @@ __global__ void __launch_bounds__((FwdLds<E, D>::NTH), (FwdLds<E, D>::MINB)) fwd
             zv[(n >> 1) * 8 + (n & 1) * 4 + i] = z;
             mz = fmaxf(mz, z);
           }
-        mz = xmax4(mz);
-        const float mnew = fmaxf(mrow, mz * sl2);
-        const float msafe = (mnew == kNegInf) ? 0.0f : mnew;
-        const float alpha = fast_exp2(mrow - msafe);
+        mz = xmax4(mz) * sl2;
+        // move the reference max only when some row's maximum grew by more
+        // than 2^8 (the probabilities stay below 256), so that most tiles
+        // leave the accumulators unscaled
+        if (__builtin_amdgcn_ballot_w64(mz > mrow + 8.0f)) {
+          const float mnew = fmaxf(mrow, mz);
+          const float alpha = fast_exp2(mrow - (mnew == kNegInf ? 0.0f : mnew));
+          lrow *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NT; ++dt) O[dt] *= alpha;
+          mrow = mnew;
+        }
+        const float msafe = (mrow == kNegInf) ? 0.0f : mrow;
         float ps = 0.0f;
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           zv[x] = fast_exp2(__builtin_fmaf(zv[x], sl2, -msafe));
           ps += zv[x];
         }
-        lrow = lrow * alpha + ps;  // this lane's share of the row sum
-        mrow = mnew;
-#pragma unroll
-        for (int dt = 0; dt < NT; ++dt) O[dt] *= alpha;
+        lrow += ps;  // this lane's share of the row sum
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           float pv[8];
@@ -418,16 +424,18 @@ __global__ void __launch_bounds__((FwdLds<E, D>::NTH), (FwdLds<E, D>::MINB)) fwd
 template <class E, int D>
 static hipError_t launch_fwd_impl(const FwdArgs& a0, hipStream_t s) {
   FwdArgs a = a0;
-  if (a.mean_c != 0) return hipErrorInvalidValue;  // (the chunk-mean shortcut runs on the rows kernel only)
+  if (a.mean_c != 0 || a.final_slot || a.nparts > kMaxStateParts)
+    return hipErrorInvalidValue;  // (the chunk-mean shortcut and the final slot belong to the rows kernel)
   constexpr int BMR = FwdLds<E, D>::BMR, NTH = FwdLds<E, D>::NTH;
   a.blk_pow = BMR;  // exact scan: one decay per evicted token of a block
   const int BH = a.B * a.H;
   const bool ring = a.row0 > 0;
   if (a.nseg > 1) {
+    const dim3 sg(BH * (a.nseg - 1) * (a.nparts > 1 ? a.nparts : 1));
     if (ring)
-      hipLaunchKernelGGL((seg_state_kernel<E, D, BMR, 0, true>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((seg_state_kernel<E, D, BMR, 0, true>), sg, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((seg_state_kernel<E, D, BMR>), dim3(BH * (a.nseg - 1)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((seg_state_kernel<E, D, BMR>), sg, dim3(256), 0, s, a);
     hipLaunchKernelGGL((seg_chain_kernel<D, BMR>), dim3((D * D + kChainThreads - 1) / kChainThreads, BH),
                        dim3(kChainThreads), 0, s, a);
   }

@@ -381,7 +381,10 @@ __device__ __forceinline__ void store4(float* dst, f32x4 x) { *(f32x4*)dst = x; 
 // grid = BH * (nseg - 1); writes seg_state[bh][m + 1].  With final_slot the
 // grid is BH * nseg and workgroup m = nseg - 1 of each head forms instead the
 // local state of the last segment's evictions up to step T-1 (for the final
-// state), at seg_state[BH * nseg + bh].
+// state), at seg_state[BH * nseg + bh].  With nparts = P > 1 the grid is
+// BH * (nseg - 1) * P: workgroup (m, p) forms the local state of tiles
+// [p nt / P, (p + 1) nt / P) of the segment's nt tiles, decayed to the end
+// of its own range, at parts[bh][m + 1][p] (the chain combines the parts).
 //
 // MEANC > 0: the chunk-mean shortcut with chunks of MEANC (64 or 128)
 // evictions: L_m = sum over the segment's chunks n of lambda^(later chunks)
@@ -404,7 +407,9 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
   E* Vs = (E*)(smem + TILE);
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int nm = a.nseg - 1 + a.final_slot;
-  const int bh = blockIdx.x / nm, m = blockIdx.x - bh * nm;
+  const int P = a.nparts > 1 ? a.nparts : 1;  // (parts: never with MEANC or a final slot)
+  const int bh = blockIdx.x / (nm * P), rem = blockIdx.x - bh * nm * P;
+  const int m = rem / P, part = rem - m * P;
   const bool fin = m == a.nseg - 1;  // the last segment's evictions (final_slot only)
   const int h = bh % a.H;
   const SeqRows Kg = seq_rows<E, D>(a, a.k, a.k_ring, bh);
@@ -414,11 +419,12 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
   state_zero(st);
   KVRegs<RING, E, D, 64> kl, vl;
   const int tb = seg_first_block(a, m) * BM;  // first row of segment m
-  const int ntile = seg_blocks(a, m) * (BM / 64);
+  const int nts = seg_blocks(a, m) * (BM / 64);  // tiles of the segment; this part: [part nts / P, ntile)
+  const int ntile = (part + 1) * nts / P;
   const int ebase = tb - a.W;
   // evictions in tile t: 64, or in the last segment those of rows up to T-1
   auto tile_len = [&](int t) { return fin ? min(64, a.T - tb - 64 * t) : 64; };
-  int t0 = 0;
+  int t0 = part * nts / P;
   while (t0 < ntile && ebase + 64 * t0 + 63 < 0) ++t0;  // tiles wholly before the first token
   load_seq<RING>(kl, Kg, ebase + 64 * t0);
   load_seq<RING>(vl, Vg, ebase + 64 * t0);
@@ -452,7 +458,8 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
     }
   }
   float* dst = fin ? a.seg_state + ((size_t)a.B * a.H * a.nseg + bh) * D * D
-                   : a.seg_state + ((size_t)bh * a.nseg + m + 1) * D * D;
+            : P > 1 ? a.parts + (((size_t)bh * a.nseg + m + 1) * P + part) * D * D
+                    : a.seg_state + ((size_t)bh * a.nseg + m + 1) * D * D;
   state_store(st, dst, 1.0f, wid, l16, lg);
 }
 
@@ -465,6 +472,7 @@ __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
 // before walking its dependent chain through them (the walk is bound by how
 // many loads are in flight, not by arithmetic).
 constexpr int kChainThreads = 64;  // workgroup size of seg_chain_kernel (its launches use it too)
+constexpr int kMaxStateParts = 4;  // most parts of one segment's state pass
 template <int D, int BM>
 __global__ void __launch_bounds__(kChainThreads) seg_chain_kernel(FwdArgs a) {
   const int bh = blockIdx.y;
@@ -476,6 +484,41 @@ __global__ void __launch_bounds__(kChainThreads) seg_chain_kernel(FwdArgs a) {
   const size_t stride = (size_t)D * D;
   float s = a.A_in ? a.A_in[(size_t)bh * D * D + x] / a.eta[bh % a.H] : 0.0f;  // S(0)
   p[0] = s;
+  if (a.nparts > 1) {
+    // L_m = sum_p lambda^(64 (nt - end_p)) L_{m,p}: part p of segment m ends
+    // at tile end_p = (p + 1) nt / P of the segment's nt tiles (nt1 for the
+    // first R segments, nt0 for the others)
+    constexpr int MAXP = kMaxStateParts, AH = 16;
+    const int P = a.nparts, nt0 = a.G * (BM / 64), nt1 = nt0 + BM / 64;
+    const float lam = a.lam[bh % a.H];
+    float w0[MAXP], w1[MAXP];
+#pragma unroll
+    for (int q = 0; q < MAXP; ++q) {
+      w0[q] = q < P ? powi(lam, 64 * (nt0 - (q + 1) * nt0 / P)) : 0.0f;
+      w1[q] = q < P ? powi(lam, 64 * (nt1 - (q + 1) * nt1 / P)) : 0.0f;
+    }
+    const float* lp = a.parts + (size_t)bh * a.nseg * P * D * D + x;
+    for (int m0 = 1; m0 < a.nseg; m0 += AH) {
+      float l[AH];
+#pragma unroll
+      for (int u = 0; u < AH; ++u) {
+        l[u] = 0.0f;
+        if (m0 + u < a.nseg) {
+          const bool r1 = m0 + u - 1 < a.R;
+#pragma unroll
+          for (int q = 0; q < MAXP; ++q)
+            if (q < P) l[u] += (r1 ? w1[q] : w0[q]) * lp[((size_t)(m0 + u) * P + q) * D * D];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < AH; ++u)
+        if (m0 + u < a.nseg) {
+          s = (m0 + u - 1 < a.R ? decay1 : decay) * s + l[u];
+          p[(m0 + u) * stride] = s;
+        }
+    }
+    return;
+  }
   constexpr int AHEAD = 64;
   for (int m0 = 1; m0 < a.nseg; m0 += AHEAD) {
     float l[AHEAD];

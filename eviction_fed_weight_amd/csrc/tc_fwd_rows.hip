@@ -74,43 +74,6 @@ struct FRows {
   static constexpr int NKC = (D + 31) / 32;
 };
 
-// Rows rb..rb+3 and rb+16..rb+19 at column c0 + l16 of a row-major LDS tile:
-// the 8 contraction values of the V operand for keys in the order the
-// score layout produces them (key 16 n + 4 lg + i sits at contraction index
-// 8 lg + 4 (n & 1) + i of the 32-key chunk n >> 1).
-template <class E>
-struct VFrag;
-template <>
-struct VFrag<bf16> {
-  static __device__ __forceinline__ bf16x8 read(const bf16* tile, int ld, int rb, int c0, int l16) {
-    const bf16* p0 = tile + (rb + (l16 >> 2)) * ld + c0 + 4 * (l16 & 3);
-    const bf16* p1 = p0 + 16 * ld;
-    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
-    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p1));
-    bf16x8 r;
-    const bf16* ea = (const bf16*)&a;
-    const bf16* eb = (const bf16*)&b;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      r[j] = ea[j];
-      r[j + 4] = eb[j];
-    }
-    return r;
-  }
-};
-template <>
-struct VFrag<float> {
-  static __device__ __forceinline__ f32x8 read(const float* tile, int ld, int rb, int c0, int l16) {
-    f32x8 r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      r[j] = tile[(rb + j) * ld + c0 + l16];
-      r[j + 4] = tile[(rb + 16 + j) * ld + c0 + l16];
-    }
-    return r;
-  }
-};
-
 // The float32 state S (D x D) of the 128-row kernel, split over the waves in
 // MFMA accumulator tiles: wave w owns column tile ct = w % NT and the AT row
 // tiles ar * AT .. ar * AT + AT - 1 (ar = w / NT; waves with ar >= RG own
@@ -870,6 +833,8 @@ static hipError_t launch_rows_impl(const FwdArgs& a0, hipStream_t s) {
   constexpr int NW = kRowWaves, BM = 32 * NW;
   FwdArgs a = a0;
   const int BH = a.B * a.H;
+  a.nparts = 1;  // (the state pass of the rows kernel has one workgroup per segment)
+  a.parts = nullptr;
   a.prefix_direct = a.nseg <= kDirectPrefixMaxSeg ? 1 : 0;
   a.blk_pow = MEANC > 0 ? BM / MEANC : BM;
   // One block per segment and a grid the device holds at once: the

@@ -66,6 +66,13 @@ struct FwdArgs {
   // 0: the exact scan.  64 or 128: the chunk-mean shortcut with chunks of
   // that many evictions (tc_forward_chunk_mean; bf16 rows kernel only).
   int mean_c;
+  // State pass in parts (fused kernel only, exact scan, no final slot): each
+  // segment's evictions are split into nparts tile ranges, one workgroup
+  // each, whose local states go to parts ([B*H][nseg][nparts][D*D], slot
+  // m + 1 for segment m); the chain combines them.  nparts = 1: one
+  // workgroup per segment writing L_m to seg_state[m+1].
+  int nparts;
+  float* parts;
 };
 
 // First block of forward segment s (s = nseg gives nblk).
