@@ -11,6 +11,8 @@ Contents
     IEEE double (``tc_oracle.c``), OpenMP over independent (b,h) pairs.
   * ``forward_chunk_mean`` -- the chunk-mean shortcut the exact scan
     replaces (one mean write per chunk of C evicted pairs), for the ablation.
+  * ``forward_delta`` -- the optional delta-rule write (the evicted key's
+    prediction error is written instead of its value), per token.
   * ``memory_f32_sequential`` / ``memory_f32_chunked`` -- float32 models of
     the memory path, per-token writes vs the chunked weighted-sum scan.
   * ``dense`` -- closed forms in numpy used to pin the oracle.
@@ -57,6 +59,7 @@ def _load():
         lib.tco_decode_step.argtypes = [_i] * 4 + [ctypes.c_double] + [_D] * 6 + [_I64] + [_D] * 4
         lib.tco_backward.argtypes = [_i] * 5 + [ctypes.c_double] + [_D] * 13
         lib.tco_forward_chunk_mean.argtypes = [_i] * 6 + [ctypes.c_double] + [_D] * 9
+        lib.tco_forward_delta.argtypes = [_i] * 5 + [ctypes.c_double] + [_D] * 9
         lib.tco_memory_f32_sequential.argtypes = [_i] * 3 + [ctypes.c_float] * 2 + [_F] * 5
         lib.tco_memory_f32_chunked.argtypes = [_i] * 4 + [ctypes.c_float] * 2 + [_F] * 5
         lib.tco_num_threads.restype = ctypes.c_int
@@ -122,6 +125,24 @@ def forward_chunk_mean(q, k, v, lam, eta, gate, W: int, C: int, scale: float | N
     lse = np.empty((B, H, T))
     _load().tco_forward_chunk_mean(B, H, T, D, int(W), int(C), tau, _p(q), _p(k), _p(v), _p(lam), _p(eta),
                                    _p(gate), _p(y), _p(A), _p(lse))
+    return y, A, lse
+
+
+def forward_delta(q, k, v, lam, eta, gate, W: int, scale: float | None = None):
+    """The delta-rule variant's forward (Figure 2, step 3, the optional
+    write; reading: u = v_old - k_old A with A before the write, then
+    A <- lam A + eta k_old u^T).  q,k,v: [B,H,T,D].  Returns (y, A_final,
+    lse) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, T, D = q.shape
+    lam, eta, gate = _f64(lam), _f64(eta), _f64(gate)
+    assert lam.shape == eta.shape == gate.shape == (H,)
+    tau = default_scale(D) if scale is None else float(scale)
+    y = np.empty_like(q)
+    A = np.empty((B, H, D, D))
+    lse = np.empty((B, H, T))
+    _load().tco_forward_delta(B, H, T, D, int(W), tau, _p(q), _p(k), _p(v), _p(lam), _p(eta), _p(gate), _p(y),
+                              _p(A), _p(lse))
     return y, A, lse
 
 

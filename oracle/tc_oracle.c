@@ -229,6 +229,79 @@ void tco_forward_chunk_mean(int B, int H, int T, int D, int W, int C, double tau
 }
 
 /*
+ * The delta-rule write that Figure 2 (step 3) names as the optional
+ * alternative to the outer-product write.  The pages give no formula for it;
+ * the related-work section traces the delta rule to the Widrow-Hoff
+ * error-correcting update.  Reading taken: the evicted key first reads the
+ * memory as it stands before this write, and only the error of that
+ * prediction is written, with the same decay and write rate,
+ *     u     = v_old - k_old A            (row vector: u[c] = v[c] - sum_a k[a] A[a][c])
+ *     A    <- lambda A + eta (k_old outer u).
+ * Everything else (the eviction schedule, the window, the read m_t = q_t A
+ * and the gated fusion) is exactly as in forward_one.
+ */
+static void delta_forward_one(int T, int D, int W, double tau, const double* q, const double* k, const double* v,
+                              double lam, double eta, double g, double* y, double* A_out, double* lse) {
+  const double sg = sigmoid(g);
+  double* A = (double*)calloc((size_t)D * D, sizeof(double));
+  double* u = (double*)malloc(sizeof(double) * (size_t)D);
+  double* z = (double*)malloc(sizeof(double) * (size_t)(W > 0 ? W : 1));
+  for (int t = 0; t < T; ++t) {
+    const double* qt = q + (size_t)t * D;
+    if (t >= W) {
+      const double* ke = k + (size_t)(t - W) * D;
+      const double* ve = v + (size_t)(t - W) * D;
+      for (int c = 0; c < D; ++c) {
+        double pred = 0.0; /* what the memory returns for the evicted key */
+        for (int a = 0; a < D; ++a) pred += ke[a] * A[a * D + c];
+        u[c] = ve[c] - pred;
+      }
+      for (int a = 0; a < D; ++a)
+        for (int c = 0; c < D; ++c) A[a * D + c] = lam * A[a * D + c] + eta * ke[a] * u[c];
+    }
+    int lo = t - W + 1;
+    if (lo < 0) lo = 0;
+    double mu = -INFINITY;
+    for (int i = lo; i <= t; ++i) {
+      z[i - lo] = tau * dot(qt, k + (size_t)i * D, D);
+      if (z[i - lo] > mu) mu = z[i - lo];
+    }
+    double ell = 0.0;
+    for (int i = lo; i <= t; ++i) ell += exp(z[i - lo] - mu);
+    double* yt = y + (size_t)t * D;
+    for (int c = 0; c < D; ++c) yt[c] = 0.0;
+    for (int i = lo; i <= t; ++i) {
+      const double p = exp(z[i - lo] - mu) / ell;
+      const double* vi = v + (size_t)i * D;
+      for (int c = 0; c < D; ++c) yt[c] += p * vi[c];
+    }
+    if (lse) lse[t] = mu + log(ell);
+    for (int c = 0; c < D; ++c) {
+      double m = 0.0;
+      for (int a = 0; a < D; ++a) m += qt[a] * A[a * D + c];
+      yt[c] += sg * m;
+    }
+  }
+  if (A_out) memcpy(A_out, A, sizeof(double) * (size_t)D * D);
+  free(A);
+  free(u);
+  free(z);
+}
+
+/* tco_forward_delta: the delta-rule variant's forward, same layout as tco_forward. */
+void tco_forward_delta(int B, int H, int T, int D, int W, double tau, const double* q, const double* k,
+                       const double* v, const double* lam, const double* eta, const double* gate, double* y,
+                       double* A_final, double* lse) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int bh = 0; bh < B * H; ++bh) {
+    const int h = bh % H;
+    const size_t off = (size_t)bh * T * D;
+    delta_forward_one(T, D, W, tau, q + off, k + off, v + off, lam[h], eta[h], gate[h], y + off,
+                      A_final ? A_final + (size_t)bh * D * D : 0, lse ? lse + (size_t)bh * T : 0);
+  }
+}
+
+/*
  * tco_decode_step: one streaming step (Figure 2, steps 1-5) for S streams x
  * H heads.  Ring slot of token t is t mod W; pos[s] is the index of the
  * incoming token of stream s.  While pos < W the slots pos+1..W-1 hold no
