@@ -278,6 +278,48 @@ def chunk_mean_leg(steps, warmup, exact_ms):
                        "fwd_kernel_rows, no intra-chunk terms)")
 
 
+def delta_leg(steps, warmup, exact_ms):
+    """The delta-rule write variant (the optional write of Figure 2, step 3,
+    of "Tensor Cache: Eviction-conditioned Associative Memory for
+    Transformers"; reading: the evicted key's prediction error is written) on
+    the long-context and the training-shape prefill: time per call, cost
+    ratio over the outer-product layer (exact scan) and the relative distance
+    of its output from it.  exact_ms: {cfg_id: ms per tc_forward call}."""
+    import torch
+
+    import eviction_fed_weight_amd as tc
+    import tc_inputs
+
+    out = []
+    for cfg_id in (3, 2):
+        cfg = tc_inputs.CONFIGS[cfg_id]
+        d = tc_inputs.prefill_inputs(cfg_id)
+        dv = torch.device("cuda")
+        q, k, v = (torch.from_numpy(d[x]).to(dv).to(torch.bfloat16).contiguous() for x in ("q", "k", "v"))
+        lam, eta, g = (torch.from_numpy(d[x]).to(dv) for x in ("lam", "eta", "gate"))
+        y = torch.empty_like(q)
+        A = torch.empty((cfg.B, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dv)
+        lse = torch.empty((cfg.B, cfg.H, cfg.T), dtype=torch.float32, device=dv)
+        shape = tc.make_shape(cfg.B, cfg.H, cfg.T, cfg.D, cfg.W, cfg.C)
+        ws = torch.empty(tc.tc_forward_delta_workspace_size(shape), dtype=torch.uint8, device=dv)
+
+        def call():
+            tc.tc_forward_delta(q, k, v, lam, eta, g, cfg.W, cfg.C, y=y, A_final=A, lse=lse, ws=ws)
+
+        ms = time_calls(call, max(3, steps // 10), max(1, warmup // 10))
+        ye, Ae, _ = tc.tc_forward(q, k, v, lam, eta, g, cfg.W, cfg.C)
+        torch.cuda.synchronize()
+        out.append(dict(
+            workload="delta-rule write, prefill B=%d H=%d D=%d T=%d W=%d bf16" % (cfg.B, cfg.H, cfg.D, cfg.T, cfg.W),
+            ms_per_call=ms, tokens_per_s=cfg.B * cfg.T / (ms * 1e-3), exact_ms_per_call=exact_ms.get(cfg_id),
+            cost_ratio_delta_over_exact=(ms / exact_ms[cfg_id]) if cfg_id in exact_ms else None,
+            rel_gap_y_vs_exact=float((y.float() - ye.float()).norm() / ye.float().norm()),
+            rel_gap_A_final_vs_exact=float((A - Ae).norm() / Ae.norm()),
+            kernel="one tc_forward_delta call (delta_chunk_kernel + delta_chain_kernel [one workgroup per head, "
+                   "a walk over the chunks of 64 evictions] + delta_read_kernel + the window-only forward)"))
+    return out
+
+
 def capacity_leg(D=128, H=8, Ns=(64, 128, 256, 512, 1024, 2048, 4096)):
     """Raw memory-capacity diagnostic (the "memory-capacity diagnostics" of the
     abstract of "Tensor Cache: Eviction-conditioned Associative Memory for
@@ -527,7 +569,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--legs", default="prefill,decode,backward,train_forward,continue,chunk_mean,capacity")
+    ap.add_argument("--legs", default="prefill,decode,backward,train_forward,continue,chunk_mean,delta,capacity")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -584,6 +626,12 @@ def main():
         cm = chunk_mean_leg(args.steps, args.warmup, lp["ms_per_call"])
         log("  chunk_mean", json.dumps(cm))
         out["chunk_mean_shortcut"] = cm
+    if "delta" in legs:
+        log("delta-rule write leg ...")
+        dl = delta_leg(args.steps, args.warmup, {3: lp["ms_per_call"], 2: out["prefill"]["ms_per_call"]}
+                       if "prefill" in out else {3: lp["ms_per_call"]})
+        log("  delta", json.dumps(dl))
+        out["delta_rule"] = dl
     if "capacity" in legs:
         log("capacity diagnostic leg ...")
         cp = capacity_leg()

@@ -10,7 +10,7 @@ If the library has not been built it raises; there is no fallback.
 Entry points mirror the C names: ``tc_forward``, ``tc_decode_step``,
 ``tc_forward_continue``, ``tc_backward``, ``tc_forward_workspace_size``,
 ``tc_continue_workspace_size``, ``tc_backward_workspace_size``,
-``tc_forward_status``, ``tc_forward_noalloc``, ``tc_forward_chunk_mean``,
+``tc_forward_status``, ``tc_forward_noalloc``, ``tc_forward_chunk_mean``, ``tc_forward_delta``,
 ``tc_status_string``.
 """
 from __future__ import annotations
@@ -68,6 +68,10 @@ def lib() -> ctypes.CDLL:
         L.tc_forward_continue.restype = ctypes.c_int
         L.tc_forward_chunk_mean.argtypes = [ctypes.POINTER(Shape)] + [_vp] * 10 + [_sz, _vp]
         L.tc_forward_chunk_mean.restype = ctypes.c_int
+        L.tc_forward_delta_workspace_size.argtypes = [ctypes.POINTER(Shape)]
+        L.tc_forward_delta_workspace_size.restype = _sz
+        L.tc_forward_delta.argtypes = [ctypes.POINTER(Shape)] + [_vp] * 10 + [_sz, _vp]
+        L.tc_forward_delta.restype = ctypes.c_int
         L.tc_forward_noalloc.argtypes = [ctypes.POINTER(Shape)] + [_vp] * 10
         L.tc_forward_noalloc.restype = ctypes.c_int
         L.tc_forward_status.argtypes = [ctypes.POINTER(Shape), ctypes.c_int64, _vp, _sz, _vp]
@@ -199,6 +203,41 @@ def tc_forward(q, k, v, lam, eta, gate, W: int, C: int = 64, scale: float = 0.0,
                           wsb, _stream(dev))
     if st != TC_OK:
         raise TCError(st, "tc_forward")
+    return y, (A_final if want_state else None), (lse if want_lse else None)
+
+
+def tc_forward_delta_workspace_size(shape) -> int:
+    return int(lib().tc_forward_delta_workspace_size(ctypes.byref(shape)))
+
+
+def tc_forward_delta(q, k, v, lam, eta, gate, W: int, C: int = 64, scale: float = 0.0, *,
+                     want_state: bool = True, want_lse: bool = True, y=None, A_final=None, lse=None, ws=None):
+    """The layer with the delta-rule write (the evicted key's prediction
+    error is written).  Arguments and returns as tc_forward; its own workspace
+    (tc_forward_delta_workspace_size)."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q: expected [B,H,T,D], got shape %s" % (tuple(q.shape),))
+    B, H, T, D = q.shape
+    shape = make_shape(B, H, T, D, W, C, scale, _dtype_code(q))
+    dev = q.device
+    for name, t in (("k", k), ("v", v), ("y", y)):
+        _want(t, name, q.shape, q.dtype, dev)
+    _want_params(H, dev, lam=lam, eta=eta, gate=gate)
+    _want(A_final, "A_final", (B, H, D, D), torch.float32, dev)
+    _want(lse, "lse", (B, H, T), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(q)
+    if want_state and A_final is None:
+        A_final = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(tc_forward_delta_workspace_size(shape), dev, ws)
+    st = lib().tc_forward_delta(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(eta), _ptr(gate),
+                                _ptr(y), _ptr(A_final) if want_state else None, _ptr(lse) if want_lse else None,
+                                _ptr(ws) if ws is not None else None, wsb, _stream(dev))
+    if st != TC_OK:
+        raise TCError(st, "tc_forward_delta")
     return y, (A_final if want_state else None), (lse if want_lse else None)
 
 

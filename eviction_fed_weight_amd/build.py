@@ -28,6 +28,8 @@ UNITS = [
     ("tc_fwd_rows.hip", "tc_fwd_rows", []),
     ("tc_decode.hip", "tc_decode", []),
     ("tc_continue.hip", "tc_continue", []),
+    # delta-rule memory path (float32 matrix-core products): results kept in VGPRs
+    ("tc_delta.hip", "tc_delta", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
     # bf16 backward: matrix-core results kept in VGPRs (fewer scratch spills)
     ("tc_backward.hip", "tc_backward_bf16", ["-DTC_BWD_BF16=1", "-mllvm", "-amdgpu-mfma-vgpr-form"]),
     ("tc_backward.hip", "tc_backward_f32", ["-DTC_BWD_BF16=0"]),

@@ -175,7 +175,7 @@ tc_status_t launch_fwd(const tc_shape_t& s, const Plan& p, const void* q, const 
                        const float* lambda, const float* eta, const float* gate, void* y, float* A_final,
                        float* lse, void* ws, bool ws_ok, int row0, const float* yadd, hipStream_t stream,
                        int mean_c = 0, const void* k_ring = nullptr, const void* v_ring = nullptr,
-                       int ring_s0 = 0, const float* A_in = nullptr) {
+                       int ring_s0 = 0, const float* A_in = nullptr, int window_only = 0) {
   tck::FwdArgs a{};
   a.mean_c = mean_c;
   a.q = q;
@@ -210,6 +210,7 @@ tc_status_t launch_fwd(const tc_shape_t& s, const Plan& p, const void* q, const 
   a.ring_s0 = ring_s0;
   a.yadd = yadd;
   a.A_in = A_in;
+  a.window_only = window_only;
   const bool is_bf16 = s.dtype == TC_BF16;
   const hipError_t e = rows_kernel(s.D, s.dtype) ? tck::launch_forward_rows(a, s.D, is_bf16, stream)
                                                        : tck::launch_forward(a, s.D, is_bf16, stream);
@@ -375,6 +376,71 @@ tc_status_t tc_forward_noalloc(const tc_shape_t* s, const void* q, const void* k
   void* w = scratch_ptr();
   if (!w) return TC_ERR_HIP;
   return launch_fwd(*s, p, q, k, v, lambda, eta, gate, y, A_final, lse, w, true, 0, nullptr, (hipStream_t)stream);
+}
+
+// Delta-rule workspace: the window-only forward's, then (float32) the
+// chunks' U' and Wm [BH][nch*64][D] each, U^T [BH][nch][D][64], the chunk
+// states A^T [BH][nch+1][D][D] and the memory read [BH][T][D].
+struct DeltaPlan {
+  Plan fp;
+  int E, nch;
+  size_t off_up, off_wm, off_ut, off_at, off_yadd, total;
+};
+DeltaPlan delta_plan_for(const tc_shape_t& s) {
+  DeltaPlan d;
+  d.fp = plan_for(s);
+  d.E = s.T > s.W ? s.T - s.W : 0;
+  d.nch = (d.E + 63) / 64;
+  const size_t BH = (size_t)s.B * s.H, D = (size_t)s.D;
+  d.off_up = align256(fwd_ws_bytes(s, d.fp));
+  d.off_wm = d.off_up + align256(BH * d.nch * 64 * D * 4);
+  d.off_ut = d.off_wm + align256(BH * d.nch * 64 * D * 4);
+  d.off_at = d.off_ut + align256(BH * d.nch * 64 * D * 4);
+  d.off_yadd = d.off_at + align256(BH * (d.nch + 1) * D * D * 4);
+  d.total = d.off_yadd + align256(BH * s.T * D * 4);
+  return d;
+}
+
+size_t tc_forward_delta_workspace_size(const tc_shape_t* s) {
+  if (check_shape(s) != TC_OK) return 0;
+  return delta_plan_for(*s).total;
+}
+
+tc_status_t tc_forward_delta(const tc_shape_t* s, const void* q, const void* k, const void* v, const float* lambda,
+                             const float* eta, const float* gate, void* y, float* A_final, float* lse, void* ws,
+                             size_t ws_bytes, void* stream) {
+  const tc_status_t st = check_fwd_args(s, q, k, v, lambda, eta, gate, y, A_final, lse);
+  if (st != TC_OK) return st;
+  const DeltaPlan d = delta_plan_for(*s);
+  if (!ws || ws_bytes < d.total) return TC_ERR_WORKSPACE;
+  const FwdExtents x = fwd_extents(*s, A_final, lse);
+  const void* bufs[9] = {q, k, v, lambda, eta, gate, y, A_final, lse};
+  for (int i = 0; i < 9; ++i)
+    if (overlap(ws, d.total, bufs[i], x.sz[i])) return TC_ERR_INVALID_ARGUMENT;
+  char* w = (char*)ws;
+  tck::DeltaArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.lam = lambda;
+  a.eta = eta;
+  a.gate = gate;
+  a.Up = (float*)(w + d.off_up);
+  a.Wm = (float*)(w + d.off_wm);
+  a.Ut = (float*)(w + d.off_ut);
+  a.AcT = (float*)(w + d.off_at);
+  a.yadd = (float*)(w + d.off_yadd);
+  a.A_final = A_final;
+  a.B = s->B;
+  a.H = s->H;
+  a.T = s->T;
+  a.W = s->W;
+  a.E = d.E;
+  a.nch = d.nch;
+  if (tck::launch_delta_memory(a, s->D, s->dtype == TC_BF16, (hipStream_t)stream) != hipSuccess) return TC_ERR_HIP;
+  // y = y_local + sigma(g) m, rounded once (the window-only forward adds the read)
+  return launch_fwd(*s, d.fp, q, k, v, lambda, eta, gate, y, nullptr, lse, ws, true, 0, a.yadd, (hipStream_t)stream,
+                    0, nullptr, nullptr, 0, nullptr, 1);
 }
 
 size_t tc_continue_workspace_size(const tc_shape_t* s, int64_t pos0) {

@@ -119,7 +119,9 @@ __global__ void __launch_bounds__((FwdLds<E, D>::NTH), (FwdLds<E, D>::MINB)) fwd
   State<E, D> st;
   const float ie = 1.0f / a.eta[h];
   const float* g0 = a.A_in ? a.A_in + (size_t)bh * D * D : nullptr;
-  if (LS) {
+  if (a.window_only) {
+    state_zero(st);  // (no memory path: the state is never read)
+  } else if (LS) {
     // S^T at the segment start -> LDS (read by every wave after the band loop's barriers)
     const float* g = a.seg_state + ((size_t)bh * a.nseg + seg) * D * D;
     for (int x = tid; x < D * D; x += NTH) Sl[(x % D) * LDSS + x / D] = seg > 0 ? g[x] : g0 ? ie * g0[x] : 0.0f;
@@ -152,7 +154,7 @@ __global__ void __launch_bounds__((FwdLds<E, D>::NTH), (FwdLds<E, D>::MINB)) fwd
     const int t0 = j * BMR;
     const int trow = t0 + r;
     const int e0 = t0 - W;
-    const bool has_mem = t0 + BMR - 1 >= W;
+    const bool has_mem = !a.window_only && t0 + BMR - 1 >= W;
     const bool more = j + 1 < je;
     const int next_k0 = (max(0, t0 + BMR - W + 1) >> 6) * 64;
     const int R0 = t0 + 16 * wid;  // first row of this wave
@@ -430,7 +432,7 @@ static hipError_t launch_fwd_impl(const FwdArgs& a0, hipStream_t s) {
   a.blk_pow = BMR;  // exact scan: one decay per evicted token of a block
   const int BH = a.B * a.H;
   const bool ring = a.row0 > 0;
-  if (a.nseg > 1) {
+  if (a.nseg > 1 && !a.window_only) {
     const dim3 sg(BH * (a.nseg - 1) * (a.nparts > 1 ? a.nparts : 1));
     if (ring)
       hipLaunchKernelGGL((seg_state_kernel<E, D, BMR, 0, true>), sg, dim3(256), 0, s, a);

@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
     b.t0 = j * BM;
     b.kb = b.t0 - W;
     const int ihi = (min(T - 1, b.t0 + BM - 1) - b.kb) >> 6;  // last tile with a key in range
-    b.mem = b.t0 + BM - 1 >= W;
+    b.mem = !a.window_only && b.t0 + BM - 1 >= W;
     if (b.mem) {
       b.nlate = min(2, ihi + 1);
       b.ilo = PUB ? 0 : 2;
@@ -312,7 +312,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
   // S(e0) of the segment's first block -> the owners' registers and the
   // hi/lo copies in LDS; with publish it is gathered after the window, from
   // the earlier segments' published states
-  if (!PUB && wid / O::NT < O::RG) {
+  if (!PUB && !a.window_only && wid / O::NT < O::RG) {
     const int ct = wid % O::NT, ar = wid / O::NT, c = 16 * ct + l16;
 #pragma unroll
     for (int k = 0; k < O::AT; ++k) so.s[k] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -848,18 +848,18 @@ static hipError_t launch_rows_impl(const FwdArgs& a0, hipStream_t s) {
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   const bool capturing = hipStreamIsCapturing(s, &capture) != hipSuccess || capture != hipStreamCaptureStatusNone;
   a.publish = (MEANC == 0 && a.G == 1 && a.R == 0 && a.nseg > 1 && a.prefix_direct && a.flags != nullptr &&
-               !a.A_in && !capturing && (long long)BH * a.nseg <= rows_resident_capacity<E, D, NW>())
+               !a.A_in && !a.window_only && !capturing && (long long)BH * a.nseg <= rows_resident_capacity<E, D, NW>())
                   ? 1
                   : 0;
   // otherwise the state pass also forms the last block's local state (final
   // state without a state update at the end of the critical path)
-  a.final_slot = (!a.publish && a.nseg > 1 && a.A_final) ? 1 : 0;
+  a.final_slot = (!a.publish && a.nseg > 1 && a.A_final && !a.window_only) ? 1 : 0;
   // (TC_FORWARD_MAX_POLLS overrides the poll bound: 0 makes every wait end at
   // once, which is how the path of a wait that runs out is tested)
   const char* polls = getenv("TC_FORWARD_MAX_POLLS");
   a.max_polls = polls ? atoi(polls) : kPublishPolls;
   const bool ring = a.row0 > 0;
-  if (a.nseg > 1 && !a.publish) {
+  if (a.nseg > 1 && !a.publish && !a.window_only) {
     if (ring)
       hipLaunchKernelGGL((seg_state_kernel<E, D, BM, MEANC, true>), dim3(BH * (a.nseg - 1 + a.final_slot)),
                          dim3(256), 0, s, a);

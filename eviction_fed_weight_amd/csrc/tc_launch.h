@@ -73,6 +73,10 @@ struct FwdArgs {
   // workgroup per segment writing L_m to seg_state[m+1].
   int nparts;
   float* parts;
+  // 1: the window attention alone (no state pass, no memory read, no
+  // A_final): y = y_local (+ yadd).  The delta-rule forward forms its memory
+  // read separately and adds it through yadd.
+  int window_only;
 };
 
 // First block of forward segment s (s = nseg gives nblk).
@@ -146,6 +150,26 @@ struct ContArgs {
   // its block rows), so there is no initial-state read and A <- A_new
   int fold;
 };
+
+// Memory path of the delta-rule forward (chunks of 64 evictions).
+struct DeltaArgs {
+  const void* q;  // [B,H,T,D]
+  const void* k;
+  const void* v;
+  const float* lam;
+  const float* eta;
+  const float* gate;
+  float* Up;       // [B*H][nch*64][D] (I+N)^-1 V per chunk
+  float* Wm;       // [B*H][nch*64][D] (I+N)^-1 diag(lambda^i) K per chunk
+  float* Ut;       // [B*H][nch][D][64] U^T per chunk
+  float* AcT;      // [B*H][nch+1][D][D] A^T before each chunk (and after the last)
+  float* yadd;     // [B*H][T][D] sigma(g) m_t
+  float* A_final;  // [B*H][D][D] (nullable)
+  int B, H, T, W;
+  int E;    // evictions per sequence, max(0, T - W)
+  int nch;  // chunks, ceil(E / 64)
+};
+hipError_t launch_delta_memory(const DeltaArgs& a, int D, bool is_bf16, hipStream_t s);
 
 hipError_t launch_continue_prep(const ContArgs& a, hipStream_t s);    // initial-state read
 hipError_t launch_continue_finish(const ContArgs& a, hipStream_t s);  // A, ring and pos updates

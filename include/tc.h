@@ -143,6 +143,25 @@ tc_status_t tc_forward_chunk_mean(const tc_shape_t* shape, const void* q, const 
                                   float* A_final, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * tc_forward_delta -- the layer with the delta-rule write that Figure 2
+ * (step 3) names as the optional alternative to the outer product.  The pages
+ * give no formula; reading (Widrow-Hoff error correction, Section 2): the
+ * evicted pair first reads the memory and only the prediction error is
+ * written, u = v_old - k_old A (A before the write), A <- lambda A +
+ * eta (k_old outer u).  L1, the read m_t = q_t A_t, the gate, y and lse are
+ * as for tc_forward; A_final (nullable) is the memory after step T-1.
+ * Computed in chunks of 64 evictions (a triangular solve per chunk, a walk
+ * over the chunks per (b,h)) in float32; C is not used.
+ *   ws   device workspace of at least tc_forward_delta_workspace_size(shape)
+ *        bytes (the chunks' float32 intermediates and the memory read).
+ * Every shape tc_forward accepts; errors as for tc_forward.
+ */
+size_t tc_forward_delta_workspace_size(const tc_shape_t* shape);
+tc_status_t tc_forward_delta(const tc_shape_t* shape, const void* q, const void* k, const void* v,
+                             const float* lambda, const float* eta, const float* gate, void* y, float* A_final,
+                             float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * tc_forward_noalloc -- tc_forward for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): the same arguments without the workspace, the same

@@ -21,6 +21,7 @@ namespace tck {
 }
 hipError_t launch_continue_prep(const ContArgs&, hipStream_t) { reached("launch_continue_prep"); }
 hipError_t launch_continue_finish(const ContArgs&, hipStream_t) { reached("launch_continue_finish"); }
+hipError_t launch_delta_memory(const DeltaArgs&, int, bool, hipStream_t) { reached("launch_delta_memory"); }
 hipError_t launch_forward_bf16(const FwdArgs&, int, hipStream_t) { reached("launch_forward_bf16"); }
 hipError_t launch_forward_f32(const FwdArgs&, int, hipStream_t) { reached("launch_forward_f32"); }
 hipError_t launch_forward_rows(const FwdArgs&, int, bool, hipStream_t) { reached("launch_forward_rows"); }
