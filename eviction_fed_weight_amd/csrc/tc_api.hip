@@ -378,25 +378,33 @@ tc_status_t tc_forward_noalloc(const tc_shape_t* s, const void* q, const void* k
   return launch_fwd(*s, p, q, k, v, lambda, eta, gate, y, A_final, lse, w, true, 0, nullptr, (hipStream_t)stream);
 }
 
-// Delta-rule workspace: the window-only forward's, then (float32) the
-// chunks' U' and Wm [BH][nch*64][D] each, U^T [BH][nch][D][64], the chunk
-// states A^T [BH][nch+1][D][D] and the memory read [BH][T][D].
+// Delta-rule workspace: the window-only forward's, then (float32) per chunk
+// U'^T and Wm^T [D][64], M_c and B_c^T [D][D]; per group M_g and B_g^T; the
+// group-start and chunk-start states; the memory read [BH][T][D].  Groups of
+// G ~ sqrt(nch / 2) chunks minimise the sequential depth 2 G + nch / G.
 struct DeltaPlan {
   Plan fp;
-  int E, nch;
-  size_t off_up, off_wm, off_ut, off_at, off_yadd, total;
+  int E, nch, G, ng;
+  size_t off_up, off_wm, off_mc, off_bc, off_mg, off_bg, off_ag, off_ac, off_yadd, total;
 };
 DeltaPlan delta_plan_for(const tc_shape_t& s) {
   DeltaPlan d;
   d.fp = plan_for(s);
   d.E = s.T > s.W ? s.T - s.W : 0;
   d.nch = (d.E + 63) / 64;
-  const size_t BH = (size_t)s.B * s.H, D = (size_t)s.D;
+  d.G = 1;
+  while ((long long)(d.G + 1) * (d.G + 1) * 2 <= d.nch) ++d.G;
+  d.ng = (d.nch + d.G - 1) / d.G;
+  const size_t BH = (size_t)s.B * s.H, D = (size_t)s.D, DD = D * D * 4;
   d.off_up = align256(fwd_ws_bytes(s, d.fp));
   d.off_wm = d.off_up + align256(BH * d.nch * 64 * D * 4);
-  d.off_ut = d.off_wm + align256(BH * d.nch * 64 * D * 4);
-  d.off_at = d.off_ut + align256(BH * d.nch * 64 * D * 4);
-  d.off_yadd = d.off_at + align256(BH * (d.nch + 1) * D * D * 4);
+  d.off_mc = d.off_wm + align256(BH * d.nch * 64 * D * 4);
+  d.off_bc = d.off_mc + align256(BH * d.nch * DD);
+  d.off_mg = d.off_bc + align256(BH * d.nch * DD);
+  d.off_bg = d.off_mg + align256(BH * d.ng * DD);
+  d.off_ag = d.off_bg + align256(BH * d.ng * DD);
+  d.off_ac = d.off_ag + align256(BH * (d.ng + 1) * DD);
+  d.off_yadd = d.off_ac + align256(BH * d.nch * DD);
   d.total = d.off_yadd + align256(BH * s.T * D * 4);
   return d;
 }
@@ -425,10 +433,14 @@ tc_status_t tc_forward_delta(const tc_shape_t* s, const void* q, const void* k, 
   a.lam = lambda;
   a.eta = eta;
   a.gate = gate;
-  a.Up = (float*)(w + d.off_up);
-  a.Wm = (float*)(w + d.off_wm);
-  a.Ut = (float*)(w + d.off_ut);
-  a.AcT = (float*)(w + d.off_at);
+  a.UpT = (float*)(w + d.off_up);
+  a.WmT = (float*)(w + d.off_wm);
+  a.Mc = (float*)(w + d.off_mc);
+  a.BcT = (float*)(w + d.off_bc);
+  a.Mg = (float*)(w + d.off_mg);
+  a.BgT = (float*)(w + d.off_bg);
+  a.AgT = (float*)(w + d.off_ag);
+  a.AcT = (float*)(w + d.off_ac);
   a.yadd = (float*)(w + d.off_yadd);
   a.A_final = A_final;
   a.B = s->B;
@@ -437,6 +449,8 @@ tc_status_t tc_forward_delta(const tc_shape_t* s, const void* q, const void* k, 
   a.W = s->W;
   a.E = d.E;
   a.nch = d.nch;
+  a.G = d.G;
+  a.ng = d.ng;
   if (tck::launch_delta_memory(a, s->D, s->dtype == TC_BF16, (hipStream_t)stream) != hipSuccess) return TC_ERR_HIP;
   // y = y_local + sigma(g) m, rounded once (the window-only forward adds the read)
   return launch_fwd(*s, d.fp, q, k, v, lambda, eta, gate, y, nullptr, lse, ws, true, 0, a.yadd, (hipStream_t)stream,

@@ -159,15 +159,21 @@ struct DeltaArgs {
   const float* lam;
   const float* eta;
   const float* gate;
-  float* Up;       // [B*H][nch*64][D] (I+N)^-1 V per chunk
-  float* Wm;       // [B*H][nch*64][D] (I+N)^-1 diag(lambda^i) K per chunk
-  float* Ut;       // [B*H][nch][D][64] U^T per chunk
-  float* AcT;      // [B*H][nch+1][D][D] A^T before each chunk (and after the last)
+  float* UpT;      // [B*H][nch][D][64] ((I+N)^-1 V)^T per chunk
+  float* WmT;      // [B*H][nch][D][64] ((I+N)^-1 diag(lambda^i) K)^T per chunk
+  float* Mc;       // [B*H][nch][D][D] M_c (row-major): A_{c+1} = M_c A_c + B_c
+  float* BcT;      // [B*H][nch][D][D] B_c^T
+  float* Mg;       // [B*H][ng][D][D] composed map of each group of G chunks (row-major)
+  float* BgT;      // [B*H][ng][D][D] its offset, transposed
+  float* AgT;      // [B*H][ng+1][D][D] A^T at every group start (and after the last)
+  float* AcT;      // [B*H][nch][D][D] A^T at every chunk start
   float* yadd;     // [B*H][T][D] sigma(g) m_t
   float* A_final;  // [B*H][D][D] (nullable)
   int B, H, T, W;
   int E;    // evictions per sequence, max(0, T - W)
   int nch;  // chunks, ceil(E / 64)
+  int G;    // chunks per group
+  int ng;   // groups, ceil(nch / G)
 };
 hipError_t launch_delta_memory(const DeltaArgs& a, int D, bool is_bf16, hipStream_t s);
 
