@@ -44,6 +44,35 @@ def fwd(shape, **kw):
                                args["ws"], args["wsb"], None)
 
 
+def test_forward_delta_validation():
+    """tc_forward_delta rejects what tc_forward rejects, and always needs
+    its own workspace (which grows with the chunks of 64 evictions)."""
+    L = tc.lib()
+
+    def call(shape, **kw):
+        args = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, lam=FAKE + 0x300000, eta=FAKE + 0x300100,
+                    gate=FAKE + 0x300200, y=FAKE + 0x400000, A=None, lse=None, ws=None, wsb=0)
+        args.update(kw)
+        return L.tc_forward_delta(ctypes.byref(shape), args["q"], args["k"], args["v"], args["lam"], args["eta"],
+                                  args["gate"], args["y"], args["A"], args["lse"], args["ws"], args["wsb"], None)
+
+    ok = tc.make_shape(1, 1, 64, 64, 8, 8)
+    need = tc.tc_forward_delta_workspace_size(ok)
+    assert need > 0 and need % 256 == 0
+    assert tc.tc_forward_delta_workspace_size(tc.make_shape(1, 1, 64, 48, 8, 8)) == 0
+    assert call(tc.make_shape(1, 1, 64, 48, 8, 8)) == tc.TC_ERR_UNSUPPORTED
+    assert call(tc.make_shape(0, 1, 64, 64, 8, 8)) == tc.TC_ERR_INVALID_ARGUMENT
+    assert call(ok, q=None) == tc.TC_ERR_INVALID_ARGUMENT
+    assert call(ok, y=FAKE) == tc.TC_ERR_INVALID_ARGUMENT  # output aliasing an input
+    assert call(ok) == tc.TC_ERR_WORKSPACE
+    assert call(ok, ws=FAKE + 0x1000000, wsb=need - 1) == tc.TC_ERR_WORKSPACE
+    assert call(ok, ws=FAKE + 0x3f0000, wsb=need) == tc.TC_ERR_INVALID_ARGUMENT  # ws overlaps y
+    assert L.tc_forward_delta(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 0,
+                              None) == tc.TC_ERR_INVALID_ARGUMENT
+    # more evictions, more chunks: a larger workspace
+    assert tc.tc_forward_delta_workspace_size(tc.make_shape(1, 1, 64 * 40, 64, 8, 8)) > need
+
+
 def test_forward_validation():
     ok = tc.make_shape(1, 1, 64, 64, 8, 8)
     assert fwd(tc.make_shape(1, 1, 64, 48, 8, 8)) == tc.TC_ERR_UNSUPPORTED
