@@ -74,10 +74,10 @@ def measured_traffic():
 
 def kernel_chunk(D, dtype="bf16"):
     """Evictions per read chunk of the forward kernels: a query block of 128
-    rows (bf16, D <= 64) or 64 rows (otherwise) reads q S(e0) for the state
-    before the block's evicted chunk plus the decayed triangle over that
-    chunk, so the kernel's intra-chunk term is that of C = 128 or 64."""
-    return 128 if (dtype == "bf16" and D <= 64) else 64
+    rows (bf16) or 64 rows (float32) reads q S(e0) for the state before the
+    block's evicted chunk plus the decayed triangle over that chunk, so the
+    kernel's intra-chunk term is that of C = 128 or 64."""
+    return 128 if dtype == "bf16" else 64
 
 
 def roofline_chunk(C, D, dtype="bf16"):
@@ -182,8 +182,8 @@ def prefill_leg(cfg_id, steps, warmup):
                       traffic=measured_traffic().get({2: "prefill", 3: "long", 5: "train_forward"}[cfg_id]),
                       kernel=("one tc_forward call (fwd_kernel_rows; with several blocks per segment also "
                               "seg_state_kernel [+ seg_chain_kernel])" if cfg.D <= 64 else
-                              "one tc_forward call (seg_state_kernel + seg_chain_kernel + fwd_kernel, D=128: 64-row "
-                              "blocks, state in LDS)")),
+                              "one tc_forward call (seg_state_kernel in parts + seg_chain_kernel + fwd_kernel, "
+                              "D=128: 128-row blocks on eight waves, state in LDS)")),
         hbm_gbs=by / (ms * 1e-3) / 1e9,
         cold=None if cold is None else dict(
             ms_per_call=cold, tokens_per_s=cfg.B * cfg.T / (cold * 1e-3), tflops=fl / (cold * 1e-3) / 1e12,

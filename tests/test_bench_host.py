@@ -53,9 +53,10 @@ def test_traffic_only_for_the_measured_sources(monkeypatch):
 
 
 def test_roofline_chunk_never_exceeds_the_kernel_read_chunk():
-    # bf16 D <= 64: 128-row query blocks read one 128-eviction chunk; otherwise 64
+    # bf16: 128-row query blocks read one 128-eviction chunk; float32: 64
     assert bench.roofline_chunk(128, 64) == 128      # long-context prefill: charged as configured
     assert bench.roofline_chunk(64, 64) == 64        # training-shape prefill: the configured, smaller chunk
-    assert bench.roofline_chunk(64, 128) == 64       # D = 128 forward
-    assert bench.roofline_chunk(512, 64) == 128      # a larger C is charged at the kernel's chunk
+    assert bench.roofline_chunk(64, 128) == 64       # D = 128 training forward: its configured C = 64
+    assert bench.roofline_chunk(512, 128) == 128     # a larger C is charged at the kernel's chunk
+    assert bench.roofline_chunk(512, 64) == 128
     assert bench.roofline_chunk(128, 64, "f32") == 64
