@@ -461,7 +461,13 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
         auto tile = [&](auto full_c) {
           constexpr bool FULL = decltype(full_c)::value;
           f32x4 Z[2][4];
+          // (state-pass instances: the wave issues its score MFMAs, and below its P V
+          // MFMAs, at raised priority, so the two waves of a SIMD interleave
+          // matrix-core bursts with the other's softmax more evenly: -3 % on the long
+          // prefill; the flag-exchange instance measured slower with it)
+          if (!PUB) __builtin_amdgcn_s_setprio(1);
           scores(Z, Kb);
+          if (!PUB) __builtin_amdgcn_s_setprio(0);
           float P[2][16];
           float mz[2];
 #pragma unroll
@@ -502,7 +508,9 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
 #pragma unroll
             for (int x = 0; x < 16; ++x) P[g][x] = fast_exp2(__builtin_fmaf(P[g][x], sl2, -ms));
           }
+          if (!PUB) __builtin_amdgcn_s_setprio(1);
           accum_pv(P, std::true_type{}, Vb);
+          if (!PUB) __builtin_amdgcn_s_setprio(0);
         };
         if (!skip) {
           if (full)
