@@ -634,6 +634,9 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dq_kernel(BwdArgs a) {
         Z[n2] = f32x4{0.f, 0.f, 0.f, 0.f};
         P[n2] = Z[n2];
       }
+      // (the matrix-product blocks run at raised wave priority: the waves
+      // sharing a SIMD then spend less time in the same phase; measured)
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int dc = 0; dc < NKC; ++dc) {
         const bool in = dc * 32 + lg * 8 < D;
@@ -649,6 +652,7 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dq_kernel(BwdArgs a) {
           P[n2] = M::mma(va, yf, P[n2]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       if (m == 0) {
         // the evicted chunk: intra-chunk memory terms of <dy, mt> and its lambda derivative
         float mp = 0.0f, dp = 0.0f;
@@ -697,9 +701,11 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dq_kernel(BwdArgs a) {
           gv[jj] = g;
         }
         const frag gf = M::pack(gv);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dt = 0; dt < NT; ++dt)
           dQ[dt] = M::mma(ColFrag<E>::read(Ks + (half * 32 + lg * 8) * LDK + dt * 16, LDK, l16), gf, dQ[dt]);
+        __builtin_amdgcn_s_setprio(0);
       };
       if (m == 0)
         tile_update(Mode<2>{});
@@ -931,6 +937,7 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dkdv_kernel(BwdArgs a) {
         Z[g2] = f32x4{0.f, 0.f, 0.f, 0.f};
         P[g2] = Z[g2];
       }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int dc = 0; dc < NKC; ++dc) {
         const bool in = dc * 32 + lg * 8 < D;
@@ -945,6 +952,7 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dkdv_kernel(BwdArgs a) {
           P[g2] = M::mma(ya, vf, P[g2]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       // P and dS^T for the wave's 32 queries, then dV += P^T dY, dK += dS^T Q.
       // Variants: 0 = tile inside the band, 1 = band edge, 2 = band edge plus
       // the memory weights of the evicting queries.  Masks enter as an added
@@ -981,6 +989,7 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dkdv_kernel(BwdArgs a) {
           gv[jj] = gvv;
         }
         const frag pf = M::pack(pv), gf = M::pack(gv);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dt = 0; dt < NT; ++dt) {
           dV[dt] = M::mma(ColFrag2<E>::read(Ys + (32 * half + lg * 4) * LDK + dt * 16,
@@ -990,6 +999,7 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 1) dkdv_kernel(BwdArgs a) {
                                             Qs + (32 * half + 16 + lg * 4) * LDK + dt * 16, LDK, l16),
                           gf, dK[dt]);
         }
+        __builtin_amdgcn_s_setprio(0);
       };
       if (m == 0)
         tile_update(Mode<2>{});
