@@ -62,8 +62,55 @@ __device__ __forceinline__ f32x8 ld8f(const bf16* p) {
   for (int j = 0; j < 8; ++j) r[j] = (float)x[j];
   return r;
 }
-__device__ __forceinline__ float ldf(const float* p) { return *p; }
-__device__ __forceinline__ float ldf(const bf16* p) { return (float)*p; }
+// 4 consecutive elements at p as floats.
+__device__ __forceinline__ f32x4 ld4f(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ f32x4 ld4f(const bf16* p) {
+  const bf16x4 x = *(const bf16x4*)p;
+  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+
+// Eight (RawFrag8) or four (RawFrag4) consecutive elements loaded as raw
+// bytes (zero when !ok) and converted to float only at their use.
+template <class E>
+struct RawFrag8;
+template <>
+struct RawFrag8<bf16> {
+  uint4 v;
+  __device__ __forceinline__ void load(const bf16* p, bool ok) { v = ok ? *(const uint4*)p : make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ f32x8 f32() const {
+    const bf16x8 x = __builtin_bit_cast(bf16x8, v);
+    f32x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (float)x[j];
+    return r;
+  }
+};
+template <>
+struct RawFrag8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p, bool ok) {
+    a = ok ? *(const f32x4*)p : f32x4{0.f, 0.f, 0.f, 0.f};
+    b = ok ? *(const f32x4*)(p + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ f32x8 f32() const { return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
+};
+template <class E>
+struct RawFrag4;
+template <>
+struct RawFrag4<bf16> {
+  uint2 v;
+  __device__ __forceinline__ void load(const bf16* p, bool ok) { v = ok ? *(const uint2*)p : make_uint2(0, 0); }
+  __device__ __forceinline__ f32x4 f32() const {
+    const bf16x4 x = __builtin_bit_cast(bf16x4, v);
+    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+  }
+};
+template <>
+struct RawFrag4<float> {
+  f32x4 v;
+  __device__ __forceinline__ void load(const float* p, bool ok) { v = ok ? *(const f32x4*)p : f32x4{0.f, 0.f, 0.f, 0.f}; }
+  __device__ __forceinline__ f32x4 f32() const { return v; }
+};
 
 // Two runs of four floats (p0[0..3], p1[0..3]) as one fragment.
 __device__ __forceinline__ f32x8 ld4x2f(const float* p0, const float* p1) {
@@ -76,7 +123,7 @@ __device__ __forceinline__ f32x8 ld4x2f(const float* p0, const float* p1) {
 // Per chunk c of head bh: U'^T and Wm^T ([D][64]), M_c (row-major) and
 // B_c^T.  grid = BH * nch, 256 threads.
 template <class E, int D>
-__global__ void __launch_bounds__(256) delta_chunk_kernel(DeltaArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) delta_chunk_kernel(DeltaArgs a) {
   using M = Mfma<float>;
   constexpr int C = kDeltaC, LDX = 2 * D + 4, LDN = C + 4, LDT = C + 4, NT = D / 16;
   constexpr int XN = C * LDX + C * LDN, XT_ = 2 * D * LDT;
@@ -85,7 +132,7 @@ __global__ void __launch_bounds__(256) delta_chunk_kernel(DeltaArgs a) {
   __shared__ float pw[C + 1];  // lambda^n
   __shared__ float wv[C];      // eta lambda^(n-1-i), zero for i >= n
   float* const X = big;             // [V | lambda^i K] (rows i), solved in place into registers
-  float* const N = big + C * LDX;   // N_ij, zero for j >= i
+  float* const Nt = big + C * LDX;  // N^T: N_ij at j * LDN + i, zero for j >= i
   float* const XT = big;            // after the solve: [U'^T ; Wm^T] (rows = columns of X)
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int bh = blockIdx.x / a.nch, c = blockIdx.x - bh * a.nch, h = bh % a.H;
@@ -97,13 +144,33 @@ __global__ void __launch_bounds__(256) delta_chunk_kernel(DeltaArgs a) {
   // eviction e is token e of the sequence
   const E* kg = (const E*)a.k + ((size_t)bh * a.T + e0) * D;
   const E* vg = (const E*)a.v + ((size_t)bh * a.T + e0) * D;
-  for (int x = tid; x < C * D; x += 256) {
-    const int i = x / D, d = x - i * D;
-    const float kv = i < n ? ldf(kg + (size_t)i * D + d) : 0.0f;
-    const float vv = i < n ? ldf(vg + (size_t)i * D + d) : 0.0f;
-    KT[d * LDT + i] = kv;
-    X[i * LDX + d] = vv;
-    X[i * LDX + D + d] = pw[i] * kv;
+  {
+    // the chunk's K and V rows as 16-byte vectors, every load in flight
+    // before the first store (rows past the last eviction read as zero)
+    constexpr int VE = 16 / (int)sizeof(E), VPR = D / VE, NV = C * VPR, PER = (NV + 255) / 256;
+    uint4 kr[PER], vr[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int x = tid + 256 * p, i = x / VPR, d = (x - i * VPR) * VE;
+      const bool ok = (NV % 256 == 0 || x < NV) && i < n;
+      kr[p] = ok ? *(const uint4*)(kg + (size_t)i * D + d) : make_uint4(0, 0, 0, 0);
+      vr[p] = ok ? *(const uint4*)(vg + (size_t)i * D + d) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int x = tid + 256 * p, i = x / VPR, d = (x - i * VPR) * VE;
+      if (NV % 256 == 0 || x < NV) {
+        const E* ke = (const E*)&kr[p];
+        const E* ve = (const E*)&vr[p];
+#pragma unroll
+        for (int jj = 0; jj < VE; ++jj) {
+          const float kv = (float)ke[jj];
+          KT[(d + jj) * LDT + i] = kv;
+          X[i * LDX + d + jj] = (float)ve[jj];
+          X[i * LDX + D + d + jj] = pw[i] * kv;
+        }
+      }
+    }
   }
   __syncthreads();
   // Gram matrix: wave w forms rows i of tile w; lane element ii of tile jt
@@ -131,28 +198,37 @@ __global__ void __launch_bounds__(256) delta_chunk_kernel(DeltaArgs a) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int j = 16 * jt + 4 * lg + ii;
-        N[i * LDN + j] = j < i ? eta * pw[i - 1 - j] * g[ii] : 0.0f;
+        Nt[j * LDN + i] = j < i ? eta * pw[i - 1 - j] * g[ii] : 0.0f;
       }
     }
   }
   __syncthreads();
-  // (I + N) X = [V | lambda^i K] by forward substitution, one column per thread
+  // (I + N) X = [V | lambda^i K] by forward substitution, one column per
+  // thread, column-oriented: once x_j is final its term leaves every later
+  // row (x_i -= N_ij x_j, i > j; each x_i receives its terms in the order
+  // j = 0, 1, .. as in the row-oriented form).  The reads of column j of N
+  // do not wait on the running sums, so they issue ahead of the arithmetic.
   float x[C];
   const bool solver = tid < 2 * D;
   if (solver) {
 #pragma unroll
     for (int i = 0; i < C; ++i) x[i] = X[i * LDX + tid];
+    // (column j + 1 is loaded while column j is applied)
+    f32x4 col[2][C / 4];
 #pragma unroll
-    for (int i = 1; i < C; ++i) {
-      float s = x[i];
+    for (int i4 = 0; i4 < C; i4 += 4) col[0][i4 / 4] = *(const f32x4*)(Nt + i4);
 #pragma unroll
-      for (int j4 = 0; j4 < i; j4 += 4) {
-        const f32x4 nv = *(const f32x4*)(N + i * LDN + j4);
+    for (int j = 0; j < C - 1; ++j) {
+      const int b = j & 1;
+      if (j + 2 < C) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          if (j4 + jj < i) s -= nv[jj] * x[j4 + jj];
+        for (int i4 = (j + 2) & ~3; i4 < C; i4 += 4) col[b ^ 1][i4 / 4] = *(const f32x4*)(Nt + (j + 1) * LDN + i4);
       }
-      x[i] = s;
+#pragma unroll
+      for (int i4 = (j + 1) & ~3; i4 < C; i4 += 4)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          if (i4 + ii > j) x[i4 + ii] -= col[b][i4 / 4][ii] * x[j];
     }
   }
   __syncthreads();  // X and N are read; XT reuses their space
@@ -231,6 +307,69 @@ struct AffineStep {
       }
     }
   }
+  // The same step from operands fetched ahead into a StepOperands set
+  // (below); only where they fit in registers (D <= 64), larger D uses run().
+  static constexpr bool kFetch = TPW * NKC <= 8;
+  struct Operands {
+    f32x8 mf[kFetch ? TPW : 1][kFetch ? NKC : 1];
+    f32x4 bf[kFetch ? TPW : 1];
+    // M (row-major) and B^T (nullable) of one step
+    __device__ __forceinline__ void fetch(const float* Mrow, const float* BT, int wid, int l16, int lg) {
+      if constexpr (kFetch) {
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+          const int t = wid + NWV * m;
+          const int pt = t / NT, qt = t - pt * NT;
+          const bool ok = t < NT * NT;
+          bf[m] = (ok && BT) ? *(const f32x4*)(BT + (size_t)(16 * qt + l16) * D + 16 * pt + 4 * lg)
+                             : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < NKC; ++kc) {
+            const int d0 = 32 * kc + 8 * lg;
+            mf[m][kc] = (ok && d0 < D) ? ld8f(Mrow + (size_t)(16 * pt + l16) * D + d0) : Mfma<float>::zero();
+          }
+        }
+      }
+    }
+  };
+  __device__ __forceinline__ void run_fetched(const Operands& o, const float* XT, int lda, bool addB, int wid,
+                                              int l16, int lg) {
+    using M = Mfma<float>;
+    if constexpr (kFetch) {
+#pragma unroll
+      for (int m = 0; m < TPW; ++m) {
+        const int t = wid + NWV * m;
+        if (t < NT * NT) {
+          const int qt = t % NT;
+          f32x4 acc = addB ? o.bf[m] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < NKC; ++kc) {
+            const int d0 = 32 * kc + 8 * lg;
+            if (d0 < D) acc = M::mma(o.mf[m][kc], ld8f(XT + (16 * qt + l16) * lda + d0), acc);
+          }
+          out[m] = acc;
+        }
+      }
+    }
+  }
+  // A step's X_out kept back (hold()) and written to global memory one step
+  // later (store_held(), row stride D, transposed): a wait for the next
+  // step's operand loads then never covers stores issued just before it.
+  f32x4 held[TPW];
+  __device__ __forceinline__ void hold() {
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) held[m] = out[m];
+  }
+  __device__ __forceinline__ void store_held(float* g, int wid, int l16, int lg) const {
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+      const int t = wid + NWV * m;
+      if (t < NT * NT) {
+        const int pt = t / NT, qt = t - pt * NT;
+        *(f32x4*)(g + (size_t)(16 * qt + l16) * D + 16 * pt + 4 * lg) = held[m];
+      }
+    }
+  }
   // X_out^T into LDS (and, if g, into global memory, row stride D)
   __device__ __forceinline__ void put(float* XT, int lda, float* g, int wid, int l16, int lg) const {
 #pragma unroll
@@ -246,6 +385,28 @@ struct AffineStep {
 };
 
 constexpr int kDeltaWaves = 8;  // waves of the group, walk and expand kernels
+
+// Steps s = 0 .. n-1 of a walk whose step operands come three steps ahead:
+// fetch(o, s) loads step s into the operand set o, apply(o, s) runs step s
+// from it.  Three sets rotate (the loop is unrolled by three so that each is
+// addressed at compile time); a step's loads are issued when the set is free,
+// two steps before their use, so their latency hides behind those steps.
+template <class Ops, class Fetch, class Apply>
+__device__ __forceinline__ void walk3(Ops (&o)[3], int n, Fetch fetch, Apply apply) {
+#pragma unroll
+  for (int u = 0; u < 3; ++u)
+    if (u < n) fetch(o[u], u);
+  for (int s0 = 0; s0 < n; s0 += 3) {
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int s = s0 + u;
+      if (s < n) {
+        apply(o[u], s);
+        if (s + 3 < n) fetch(o[u], s + 3);
+      }
+    }
+  }
+}
 
 // Per group g of head bh: the composed map of its chunks, M_g (row-major)
 // and B_g^T.  grid = BH * ng, 512 threads.
@@ -264,15 +425,34 @@ __global__ void __launch_bounds__(64 * kDeltaWaves) delta_group_kernel(DeltaArgs
   __syncthreads();
   const int c0 = g * a.G, c1 = min(a.nch, c0 + a.G);
   AffineStep<D, kDeltaWaves> st;  // (the two products one after the other: half the registers)
-  for (int c = c0; c < c1; ++c) {
-    const float* Mc = a.Mc + ((size_t)bh * a.nch + c) * D * D;
-    st.run(Mc, PT, LDA, nullptr, wid, l16, lg);
-    __syncthreads();
-    st.put(PT, LDA, nullptr, wid, l16, lg);
-    st.run(Mc, QT, LDA, a.BcT + ((size_t)bh * a.nch + c) * D * D, wid, l16, lg);
-    __syncthreads();
-    st.put(QT, LDA, nullptr, wid, l16, lg);
-    __syncthreads();
+  auto mc = [&](int c) { return a.Mc + ((size_t)bh * a.nch + c) * D * D; };
+  auto bc = [&](int c) { return a.BcT + ((size_t)bh * a.nch + c) * D * D; };
+  if constexpr (AffineStep<D, kDeltaWaves>::kFetch) {
+    // (one set of operands, the next chunk's loaded during this one's second
+    // product: here, unlike the walk, the registers of more sets would cost
+    // resident workgroups)
+    typename AffineStep<D, kDeltaWaves>::Operands o;
+    if (c0 < c1) o.fetch(mc(c0), bc(c0), wid, l16, lg);
+    for (int c = c0; c < c1; ++c) {
+      st.run_fetched(o, PT, LDA, false, wid, l16, lg);
+      __syncthreads();
+      st.put(PT, LDA, nullptr, wid, l16, lg);
+      st.run_fetched(o, QT, LDA, true, wid, l16, lg);
+      if (c + 1 < c1) o.fetch(mc(c + 1), bc(c + 1), wid, l16, lg);
+      __syncthreads();
+      st.put(QT, LDA, nullptr, wid, l16, lg);
+      __syncthreads();
+    }
+  } else {
+    for (int c = c0; c < c1; ++c) {
+      st.run(mc(c), PT, LDA, nullptr, wid, l16, lg);
+      __syncthreads();
+      st.put(PT, LDA, nullptr, wid, l16, lg);
+      st.run(mc(c), QT, LDA, bc(c), wid, l16, lg);
+      __syncthreads();
+      st.put(QT, LDA, nullptr, wid, l16, lg);
+      __syncthreads();
+    }
   }
   float* Mg = a.Mg + ((size_t)bh * a.ng + g) * D * D;
   float* Bg = a.BgT + ((size_t)bh * a.ng + g) * D * D;
@@ -296,11 +476,31 @@ __global__ void __launch_bounds__(64 * kDeltaWaves) delta_walk_kernel(DeltaArgs 
   for (int x = tid; x < D * D; x += 64 * kDeltaWaves) Ag[x] = 0.0f;
   __syncthreads();
   AffineStep<D, kDeltaWaves> st;
-  for (int g = 0; g < a.ng; ++g) {
-    st.run(a.Mg + ((size_t)bh * a.ng + g) * D * D, AT, LDA, a.BgT + ((size_t)bh * a.ng + g) * D * D, wid, l16, lg);
-    __syncthreads();
-    st.put(AT, LDA, Ag + (size_t)(g + 1) * D * D, wid, l16, lg);
-    __syncthreads();
+  auto mg = [&](int g) { return a.Mg + ((size_t)bh * a.ng + g) * D * D; };
+  auto bg = [&](int g) { return a.BgT + ((size_t)bh * a.ng + g) * D * D; };
+  if constexpr (AffineStep<D, kDeltaWaves>::kFetch) {
+    // (each step's state goes to global memory one step late, after the next
+    // step's products: see hold())
+    using Ops = typename AffineStep<D, kDeltaWaves>::Operands;
+    Ops ops[3];
+    walk3(
+        ops, a.ng, [&](Ops& o, int g) { o.fetch(mg(g), bg(g), wid, l16, lg); },
+        [&](Ops& o, int g) {
+          st.run_fetched(o, AT, LDA, true, wid, l16, lg);
+          if (g > 0) st.store_held(Ag + (size_t)g * D * D, wid, l16, lg);
+          __syncthreads();
+          st.put(AT, LDA, nullptr, wid, l16, lg);
+          st.hold();
+          if (g + 1 == a.ng) st.store_held(Ag + (size_t)a.ng * D * D, wid, l16, lg);
+          __syncthreads();
+        });
+  } else {
+    for (int g = 0; g < a.ng; ++g) {
+      st.run(mg(g), AT, LDA, bg(g), wid, l16, lg);
+      __syncthreads();
+      st.put(AT, LDA, Ag + (size_t)(g + 1) * D * D, wid, l16, lg);
+      __syncthreads();
+    }
   }
   if (a.A_final) {
     float* Af = a.A_final + (size_t)bh * D * D;
@@ -322,19 +522,51 @@ __global__ void __launch_bounds__(64 * kDeltaWaves) delta_expand_kernel(DeltaArg
   const float* Ag = a.AgT + ((size_t)bh * (a.ng + 1) + g) * D * D;
   const int c0 = g * a.G, c1 = min(a.nch, c0 + a.G);
   float* Ac0 = a.AcT + ((size_t)bh * a.nch + c0) * D * D;
-  for (int x = tid; x < D * D; x += 64 * kDeltaWaves) {
-    const int row = x / D, col = x - row * D;
-    AT[row * LDA + col] = Ag[x];
-    Ac0[x] = Ag[x];
+  {
+    // the group's start state: every load in flight before the first store
+    constexpr int NV = D * D / 4, PER = (NV + 64 * kDeltaWaves - 1) / (64 * kDeltaWaves);
+    f32x4 v[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int x4 = tid + 64 * kDeltaWaves * p;
+      if (NV % (64 * kDeltaWaves) == 0 || x4 < NV) v[p] = *(const f32x4*)(Ag + 4 * x4);
+    }
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int x4 = tid + 64 * kDeltaWaves * p;
+      if (NV % (64 * kDeltaWaves) == 0 || x4 < NV) {
+        const int row = (4 * x4) / D, col = 4 * x4 - row * D;
+        *(f32x4*)(AT + row * LDA + col) = v[p];
+        *(f32x4*)(Ac0 + 4 * x4) = v[p];
+      }
+    }
   }
   __syncthreads();
   AffineStep<D, kDeltaWaves> st;
-  for (int c = c0; c + 1 < c1; ++c) {
-    st.run(a.Mc + ((size_t)bh * a.nch + c) * D * D, AT, LDA, a.BcT + ((size_t)bh * a.nch + c) * D * D, wid, l16,
-           lg);
-    __syncthreads();
-    st.put(AT, LDA, a.AcT + ((size_t)bh * a.nch + c + 1) * D * D, wid, l16, lg);
-    __syncthreads();
+  auto mc = [&](int c) { return a.Mc + ((size_t)bh * a.nch + c) * D * D; };
+  auto bc = [&](int c) { return a.BcT + ((size_t)bh * a.nch + c) * D * D; };
+  if constexpr (AffineStep<D, kDeltaWaves>::kFetch) {
+    // (one set of operands, as in the group kernel; each state goes to
+    // global memory one step late, as in the walk)
+    typename AffineStep<D, kDeltaWaves>::Operands o;
+    if (c0 + 1 < c1) o.fetch(mc(c0), bc(c0), wid, l16, lg);
+    for (int c = c0; c + 1 < c1; ++c) {
+      st.run_fetched(o, AT, LDA, true, wid, l16, lg);
+      if (c > c0) st.store_held(a.AcT + ((size_t)bh * a.nch + c) * D * D, wid, l16, lg);
+      __syncthreads();
+      st.put(AT, LDA, nullptr, wid, l16, lg);
+      st.hold();
+      if (c + 2 < c1) o.fetch(mc(c + 1), bc(c + 1), wid, l16, lg);
+      __syncthreads();
+    }
+    if (c0 + 1 < c1) st.store_held(a.AcT + ((size_t)bh * a.nch + c1 - 1) * D * D, wid, l16, lg);
+  } else {
+    for (int c = c0; c + 1 < c1; ++c) {
+      st.run(mc(c), AT, LDA, bc(c), wid, l16, lg);
+      __syncthreads();
+      st.put(AT, LDA, a.AcT + ((size_t)bh * a.nch + c + 1) * D * D, wid, l16, lg);
+      __syncthreads();
+    }
   }
 }
 
@@ -347,9 +579,16 @@ __global__ void __launch_bounds__(64 * kDeltaWaves) delta_expand_kernel(DeltaArg
 // product before (index 32 kc + 4 lg + ii, then 32 kc + 16 + 4 lg + ii), and
 // the other operand is read in the same order.
 template <class E, int D>
-__global__ void __launch_bounds__(256) delta_read_kernel(DeltaArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) delta_read_kernel(DeltaArgs a) {
   using M = Mfma<float>;
   constexpr int C = kDeltaC, NT = D / 16, NKC = (D + 31) / 32;
+  // The operands arrive in three rounds of loads, each issued as a whole
+  // before any of it is used (a scheduling barrier keeps the compiler from
+  // interleaving them with their uses): the query rows and keys; W_m^T and
+  // the query's columns (for D <= 64 already with the first round); then A_c^T
+  // and U'^T, two column tiles at a time.
+  constexpr bool EARLY = D <= 64;
+  constexpr int CTB = NT >= 2 ? 2 : 1;  // column tiles per round of A_c / U' loads
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int nb = a.nch > 0 ? a.nch : 1;
   const int bh = blockIdx.x / nb, c = blockIdx.x - bh * nb, h = bh % a.H;
@@ -367,12 +606,37 @@ __global__ void __launch_bounds__(256) delta_read_kernel(DeltaArgs a) {
   const float* AcT = a.AcT + ((size_t)bh * a.nch + c) * D * D;
   const float* UpT = a.UpT + ((size_t)bh * a.nch + c) * D * C;
   const float* WmT = a.WmT + ((size_t)bh * a.nch + c) * D * C;
-  f32x8 qf[NKC];
+
+  RawFrag8<E> qr[NKC], kr[4][NKC];
+  RawFrag4<E> q4r[NT];
+  f32x4 wm[NT][2][2];
+  auto load_wm = [&]() {
+#pragma unroll
+    for (int at = 0; at < NT; ++at) {
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const float* wr = WmT + (size_t)(16 * at + l16) * C + 32 * kc + 4 * lg;
+        wm[at][kc][0] = *(const f32x4*)wr;
+        wm[at][kc][1] = *(const f32x4*)(wr + 16);
+      }
+      q4r[at].load(qg + (size_t)r * D + 16 * at + 4 * lg, r < n);
+    }
+  };
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc) {
     const int d0 = 32 * kc + 8 * lg;
-    qf[kc] = (r < n && d0 < D) ? ld8f(qg + (size_t)r * D + d0) : M::zero();
+    qr[kc].load(qg + (size_t)r * D + d0, r < n && d0 < D);
   }
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+    for (int dc = 0; dc < NKC; ++dc) {
+      const int d0 = 32 * dc + 8 * lg;
+      // (keys past the chunk's last eviction may lie past the sequence)
+      kr[jt][dc].load(kg + (size_t)(16 * jt + l16) * D + d0, d0 < D && 16 * jt + l16 < n);
+    }
+  if constexpr (EARLY) load_wm();
+  __builtin_amdgcn_sched_barrier(0);
   // P as two fragments (j slots as above)
   f32x8 pf[2];
 #pragma unroll
@@ -382,18 +646,17 @@ __global__ void __launch_bounds__(256) delta_read_kernel(DeltaArgs a) {
       const int jt = 2 * kc + half;
       f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dc = 0; dc < NKC; ++dc) {
-        const int d0 = 32 * dc + 8 * lg;
-        // (keys past the chunk's last eviction may lie past the sequence)
-        const f32x8 kf = (d0 < D && 16 * jt + l16 < n) ? ld8f(kg + (size_t)(16 * jt + l16) * D + d0) : M::zero();
-        s = M::mma(kf, qf[dc], s);
-      }
+      for (int dc = 0; dc < NKC; ++dc) s = M::mma(kr[jt][dc].f32(), qr[dc].f32(), s);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int j = 16 * jt + 4 * lg + ii;
         pf[kc][4 * half + ii] = (j <= r && j < n) ? eta * powi(lam, r - j) * s[ii] : 0.0f;
       }
     }
+  }
+  if constexpr (!EARLY) {
+    load_wm();
+    __builtin_amdgcn_sched_barrier(0);
   }
   // Qt^T tiles: element ii of tile at is Qt[r][16 at + 4 lg + ii]
   const float dr = powi(lam, r + 1);
@@ -403,47 +666,57 @@ __global__ void __launch_bounds__(256) delta_read_kernel(DeltaArgs a) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      const float* wr = WmT + (size_t)(16 * at + l16) * C + 32 * kc + 4 * lg;
-      acc = M::mma(ld4x2f(wr, wr + 16), pf[kc], acc);
+      const f32x4 w0 = wm[at][kc][0], w1 = wm[at][kc][1];
+      acc = M::mma(f32x8{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]}, pf[kc], acc);
     }
-    f32x4 q4;
-    {
-      const E* qp = qg + (size_t)r * D + 16 * at + 4 * lg;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) q4[ii] = r < n ? ldf(qp + ii) : 0.0f;
-    }
+    const f32x4 q4 = q4r[at].f32();
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) qt[at][ii] = dr * q4[ii] - acc[ii];
   }
   float* yrow = yb + (size_t)(a.W + e0 + r) * D;
 #pragma unroll
-  for (int ct = 0; ct < NT; ++ct) {
-    f32x4 m = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int col = 16 * ct + l16;
+  for (int cb = 0; cb < NT; cb += CTB) {
+    f32x4 av[CTB][NKC][2], uv[CTB][2][2];
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      if (32 * kc + 16 < D) {  // tiles 2 kc and 2 kc + 1 of Qt
-        const f32x8 qq = f32x8{qt[2 * kc][0], qt[2 * kc][1], qt[2 * kc][2], qt[2 * kc][3],
-                               qt[2 * kc + 1][0], qt[2 * kc + 1][1], qt[2 * kc + 1][2], qt[2 * kc + 1][3]};
+    for (int u = 0; u < CTB; ++u) {
+      const int col = 16 * (cb + u) + l16;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
         const float* ar = AcT + (size_t)col * D + 32 * kc + 4 * lg;
-        m = M::mma(ld4x2f(ar, ar + 16), qq, m);
-      } else {  // D = 16: one tile of Qt, the other half of the slots empty
-        const f32x8 qq = f32x8{qt[2 * kc][0], qt[2 * kc][1], qt[2 * kc][2], qt[2 * kc][3], 0.f, 0.f, 0.f, 0.f};
-        const float* ar = AcT + (size_t)col * D + 32 * kc + 4 * lg;
-        const f32x4 a0 = *(const f32x4*)ar;
-        m = M::mma(f32x8{a0[0], a0[1], a0[2], a0[3], 0.f, 0.f, 0.f, 0.f}, qq, m);
+        av[u][kc][0] = *(const f32x4*)ar;
+        // (D = 16: one tile of Qt, the other half of the slots empty)
+        av[u][kc][1] = 32 * kc + 16 < D ? *(const f32x4*)(ar + 16) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const float* ur = UpT + (size_t)col * C + 32 * kc + 4 * lg;
+        uv[u][kc][0] = *(const f32x4*)ur;
+        uv[u][kc][1] = *(const f32x4*)(ur + 16);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const float* ur = UpT + (size_t)col * C + 32 * kc + 4 * lg;
-      m = M::mma(ld4x2f(ur, ur + 16), pf[kc], m);
-    }
-    if (r < n) {
-      f32x4 o;
+    for (int u = 0; u < CTB; ++u) {
+      const int ct = cb + u;
+      f32x4 m = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) o[ii] = sg * m[ii];
-      *(f32x4*)(yrow + 16 * ct + 4 * lg) = o;
+      for (int kc = 0; kc < NKC; ++kc) {
+        const f32x4 x0 = qt[2 * kc], x1 = 32 * kc + 16 < D ? qt[2 * kc + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x8 qq = f32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        const f32x4 a0 = av[u][kc][0], a1 = av[u][kc][1];
+        m = M::mma(f32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}, qq, m);
+      }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const f32x4 u0 = uv[u][kc][0], u1 = uv[u][kc][1];
+        m = M::mma(f32x8{u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]}, pf[kc], m);
+      }
+      if (r < n) {
+        f32x4 o;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) o[ii] = sg * m[ii];
+        *(f32x4*)(yrow + 16 * ct + 4 * lg) = o;
+      }
     }
   }
 }
