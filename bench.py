@@ -315,8 +315,9 @@ def delta_leg(steps, warmup, exact_ms):
             cost_ratio_delta_over_exact=(ms / exact_ms[cfg_id]) if cfg_id in exact_ms else None,
             rel_gap_y_vs_exact=float((y.float() - ye.float()).norm() / ye.float().norm()),
             rel_gap_A_final_vs_exact=float((A - Ae).norm() / Ae.norm()),
-            kernel="one tc_forward_delta call (delta_chunk_kernel + delta_chain_kernel [one workgroup per head, "
-                   "a walk over the chunks of 64 evictions] + delta_read_kernel + the window-only forward)"))
+            kernel="one tc_forward_delta call (delta_chunk_kernel [per chunk of 64 evictions] + delta_group_kernel "
+                   "+ delta_walk_kernel [one workgroup per head] + delta_expand_kernel + delta_read_kernel + the "
+                   "window-only forward)"))
     return out
 
 
