@@ -399,9 +399,17 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
 
     // scores Z[g][n][i] = <q_row, k_key>, row = R0 + 16 g + l16,
     // key = tile row 16 n + 4 lg + i of the K tile at Kt
-    auto scores = [&](f32x4 (&Z)[2][4], const E* Kt) {
+    // (LV: bit p set when the tile's keys 32 p .. 32 p + 31 are computed; the
+    // scores of a dead half are -inf without matrix-core work)
+    auto scores = [&](f32x4 (&Z)[2][4], const E* Kt, auto lv_c) {
+      constexpr int LV = decltype(lv_c)::value;
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
+        if (!((LV >> (n >> 1)) & 1)) {
+          Z[0][n] = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+          Z[1][n] = Z[0][n];
+          continue;
+        }
         Z[0][n] = f32x4{0.f, 0.f, 0.f, 0.f};
         Z[1][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -415,10 +423,12 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
     };
     // O[g] += P[g] V with P[g][8 p + 4 (n & 1) + i] the weight of key 16 n + 4 lg + i;
     // with SUM also Lsum[g] += (row sums of P), from the same packed P; V tile at Vt
-    auto accum_pv = [&](const float (&P)[2][16], auto sum_c, const E* Vt) {
+    auto accum_pv = [&](const float (&P)[2][16], auto sum_c, const E* Vt, auto lv_c) {
       constexpr bool SUM = decltype(sum_c)::value;
+      constexpr int LV = decltype(lv_c)::value;  // halves with nonzero P (as in scores)
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
+        if (!((LV >> p) & 1)) continue;
         float x0[8], x1[8];
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
@@ -458,15 +468,16 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
         // (tiles of early blocks may start before token 0: those keys are masked)
         const bool skip = (k0 > R0 + 31) || (k0 + 63 <= R0 - W) || (k0 + 63 < 0);
         const bool full = (k0 + 63 <= R0) && (k0 >= R0 + 32 - W) && (k0 >= 0);
-        auto tile = [&](auto full_c) {
+        auto tile = [&](auto full_c, auto lv_c) {
           constexpr bool FULL = decltype(full_c)::value;
+          constexpr int LV = decltype(lv_c)::value;
           f32x4 Z[2][4];
           // (state-pass instances: the wave issues its score MFMAs, and below its P V
           // MFMAs, at raised priority, so the two waves of a SIMD interleave
           // matrix-core bursts with the other's softmax more evenly: -3 % on the long
           // prefill; the flag-exchange instance measured slower with it)
           if (!PUB) __builtin_amdgcn_s_setprio(1);
-          scores(Z, Kb);
+          scores(Z, Kb, lv_c);
           if (!PUB) __builtin_amdgcn_s_setprio(0);
           float P[2][16];
           float mz[2];
@@ -506,17 +517,34 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
           for (int g = 0; g < 2; ++g) {
             const float ms = (mrow[g] == kNegInf) ? 0.0f : mrow[g];
 #pragma unroll
-            for (int x = 0; x < 16; ++x) P[g][x] = fast_exp2(__builtin_fmaf(P[g][x], sl2, -ms));
+            for (int x = 0; x < 16; ++x)
+              P[g][x] = ((LV >> (x >> 3)) & 1) ? fast_exp2(__builtin_fmaf(P[g][x], sl2, -ms)) : 0.0f;
           }
           if (!PUB) __builtin_amdgcn_s_setprio(1);
-          accum_pv(P, std::true_type{}, Vb);
+          accum_pv(P, std::true_type{}, Vb, lv_c);
           if (!PUB) __builtin_amdgcn_s_setprio(0);
         };
         if (!skip) {
-          if (full)
-            tile(std::true_type{});
-          else
-            tile(std::false_type{});
+          if (full) {
+            tile(std::true_type{}, std::integral_constant<int, 3>{});
+          } else if constexpr (PUB) {
+            // a band-edge tile may have a half that no row of this wave sees: its
+            // keys all lie after the wave's last row, or before the first key of
+            // the earliest window (max(0, R0 - W + 1)); it contributes zeros, so
+            // its products and exponentials are skipped (the results do not
+            // change).  Only in the state-exchange instance, whose workgroups run
+            // one short chain each (-1.7 %); in the state-pass instances the
+            // extra tile variants cost more than they save (+3.6 %, measured).
+            const int lo_key = max(0, R0 - W + 1);
+            if (k0 + 31 < lo_key)
+              tile(std::false_type{}, std::integral_constant<int, 2>{});
+            else if (k0 + 32 > R0 + 31)
+              tile(std::false_type{}, std::integral_constant<int, 1>{});
+            else
+              tile(std::false_type{}, std::integral_constant<int, 3>{});
+          } else {
+            tile(std::false_type{}, std::integral_constant<int, 3>{});
+          }
         }
       }
       if (PUB && has_mem && (pub || fin) && it == min(1, cb.nwin - 1)) {
@@ -619,7 +647,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
           const E *Kc, *Vc;
           chunk_tile(c, Kc, Vc);
           f32x4 Z[2][4];
-          scores(Z, Kc);
+          scores(Z, Kc, std::integral_constant<int, 3>{});
           // weight of row r and chunk key ci: wtab[128 + r - ci] (0 for ci > r); keys
           // before token 0 were loaded as zeros (Z = 0).  One base per lane, the
           // 32 weights at immediate offsets 51 + 16 (g - n) - i from it.
@@ -632,7 +660,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
 #pragma unroll
               for (int i = 0; i < 4; ++i)
                 P[g][8 * (n >> 1) + 4 * (n & 1) + i] = wb[51 + 16 * (g - n) - i] * Z[g][n][i];
-          accum_pv(P, std::false_type{}, Vc);
+          accum_pv(P, std::false_type{}, Vc, std::integral_constant<int, 3>{});
         }
       }
     }
