@@ -62,12 +62,6 @@ __device__ __forceinline__ f32x8 ld8f(const bf16* p) {
   for (int j = 0; j < 8; ++j) r[j] = (float)x[j];
   return r;
 }
-// 4 consecutive elements at p as floats.
-__device__ __forceinline__ f32x4 ld4f(const float* p) { return *(const f32x4*)p; }
-__device__ __forceinline__ f32x4 ld4f(const bf16* p) {
-  const bf16x4 x = *(const bf16x4*)p;
-  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-}
 
 // Eight (RawFrag8) or four (RawFrag4) consecutive elements loaded as raw
 // bytes (zero when !ok) and converted to float only at their use.
@@ -112,11 +106,6 @@ struct RawFrag4<float> {
   __device__ __forceinline__ f32x4 f32() const { return v; }
 };
 
-// Two runs of four floats (p0[0..3], p1[0..3]) as one fragment.
-__device__ __forceinline__ f32x8 ld4x2f(const float* p0, const float* p1) {
-  const f32x4 a = *(const f32x4*)p0, b = *(const f32x4*)p1;
-  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
 
 }  // namespace
 
