@@ -182,7 +182,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
         const int d0 = 32 * kc + 8 * lg;
         const f32x8 ka = d0 < D ? kcol(16 * jt + l16, d0) : M::zero();
         const f32x8 kb = d0 < D ? kcol(i, d0) : M::zero();
-        g = M::mma(ka, kb, g);
+        if constexpr (sizeof(E) == 2) {
+          // the keys are bf16 values: back to bf16 exactly, one bf16 op
+          float xa[8], xb[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            xa[jj] = ka[jj];
+            xb[jj] = kb[jj];
+          }
+          g = Mfma<bf16>::mma(Mfma<bf16>::pack(xa), Mfma<bf16>::pack(xb), g);
+        } else {
+          g = M::mma(ka, kb, g);
+        }
       }
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
@@ -635,7 +646,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))
       const int jt = 2 * kc + half;
       f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dc = 0; dc < NKC; ++dc) s = M::mma(kr[jt][dc].f32(), qr[dc].f32(), s);
+      for (int dc = 0; dc < NKC; ++dc) {
+        // bf16 inputs: one bf16 matrix-core op (exact products, float32 sums)
+        // instead of eight float32 ones on the same values
+        if constexpr (sizeof(E) == 2)
+          s = Mfma<bf16>::mma(__builtin_bit_cast(bf16x8, kr[jt][dc].v), __builtin_bit_cast(bf16x8, qr[dc].v), s);
+        else
+          s = M::mma(kr[jt][dc].f32(), qr[dc].f32(), s);
+      }
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int j = 16 * jt + 4 * lg + ii;
