@@ -250,6 +250,13 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t rs, int byte_
   const v4i x = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)byte_off, 0, 0);
   return uint4{(uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]};
 }
+// The same load marked non-temporal (the nt cache-policy bit): for data read
+// once per launch, so that streaming it does not evict what is reused.
+__device__ __forceinline__ uint4 buf_load16_nt(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const v4i x = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)byte_off, 0, 2);
+  return uint4{(uint32_t)x[0], (uint32_t)x[1], (uint32_t)x[2], (uint32_t)x[3]};
+}
 
 // Key or value rows of a sequence that may continue an earlier one: rows
 // r >= p are rows r - p of `cur` (this call's tokens); rows 0 <= r < p are the
