@@ -380,21 +380,46 @@ tc_status_t tc_forward_noalloc(const tc_shape_t* s, const void* q, const void* k
 
 // Delta-rule workspace: the window-only forward's, then (float32) per chunk
 // U'^T and Wm^T [D][64], M_c and B_c^T [D][D]; per group M_g and B_g^T; the
-// group-start and chunk-start states; the memory read [BH][T][D].  Groups of
-// G ~ sqrt(nch / 2) chunks minimise the sequential depth 2 G + nch / G.
+// group-start and chunk-start states; the memory read [BH][T][D]; with three
+// levels also per supergroup its map, offset and start state.
+//
+// Level sizes.  A scan level of n maps in groups of g costs g steps in its
+// group kernel (two products a step) and g in its expand kernel (one), each
+// stretched by the share of the chip its BH ceil(n/g) workgroups overfill
+// (the time of a step was measured flat up to about two 512-thread
+// workgroups per compute unit, and growing in proportion beyond); the walk
+// over the top level costs one product per map, and a third level two
+// launches more.  The sizes minimise that cost (in product latencies).
+constexpr double kDeltaSlots = 512.0;  // workgroups the chip runs at full per-step speed
 struct DeltaPlan {
   Plan fp;
-  int E, nch, G, ng;
-  size_t off_up, off_wm, off_mc, off_bc, off_mg, off_bg, off_ag, off_ac, off_yadd, total;
+  int E, nch, G, ng, G2, nsg;
+  size_t off_up, off_wm, off_mc, off_bc, off_mg, off_bg, off_ag, off_ac, off_ms, off_bs, off_as, off_yadd, total;
 };
 DeltaPlan delta_plan_for(const tc_shape_t& s) {
   DeltaPlan d;
   d.fp = plan_for(s);
   d.E = s.T > s.W ? s.T - s.W : 0;
   d.nch = (d.E + 63) / 64;
+  const double heads = (double)s.B * s.H;
+  auto level = [&](int n, int g) {  // group + expand steps of one level
+    const int groups = (n + g - 1) / g;
+    return 3.0 * g * std::max(1.0, heads * groups / kDeltaSlots);
+  };
   d.G = 1;
-  while ((long long)(d.G + 1) * (d.G + 1) * 2 <= d.nch) ++d.G;
+  d.G2 = 0;
+  double best = 1e30;
+  for (int g = 1; g <= 64; ++g) {
+    const int ng = (d.nch + g - 1) / g;
+    const double two = level(d.nch, g) + ng;
+    if (two < best) best = two, d.G = g, d.G2 = 0;
+    for (int g2 = 2; g2 <= 32 && ng > 1; ++g2) {
+      const double three = level(d.nch, g) + level(ng, g2) + (ng + g2 - 1) / g2 + 2.0;
+      if (three < best) best = three, d.G = g, d.G2 = g2;
+    }
+  }
   d.ng = (d.nch + d.G - 1) / d.G;
+  d.nsg = d.G2 > 0 ? (d.ng + d.G2 - 1) / d.G2 : 0;
   const size_t BH = (size_t)s.B * s.H, D = (size_t)s.D, DD = D * D * 4;
   d.off_up = align256(fwd_ws_bytes(s, d.fp));
   d.off_wm = d.off_up + align256(BH * d.nch * 64 * D * 4);
@@ -404,7 +429,10 @@ DeltaPlan delta_plan_for(const tc_shape_t& s) {
   d.off_bg = d.off_mg + align256(BH * d.ng * DD);
   d.off_ag = d.off_bg + align256(BH * d.ng * DD);
   d.off_ac = d.off_ag + align256(BH * (d.ng + 1) * DD);
-  d.off_yadd = d.off_ac + align256(BH * d.nch * DD);
+  d.off_ms = d.off_ac + align256(BH * d.nch * DD);
+  d.off_bs = d.off_ms + align256(BH * d.nsg * DD);
+  d.off_as = d.off_bs + align256(BH * d.nsg * DD);
+  d.off_yadd = d.off_as + (d.nsg > 0 ? align256(BH * (d.nsg + 1) * DD) : 0);
   d.total = d.off_yadd + align256(BH * s.T * D * 4);
   return d;
 }
@@ -441,6 +469,9 @@ tc_status_t tc_forward_delta(const tc_shape_t* s, const void* q, const void* k, 
   a.BgT = (float*)(w + d.off_bg);
   a.AgT = (float*)(w + d.off_ag);
   a.AcT = (float*)(w + d.off_ac);
+  a.Ms = (float*)(w + d.off_ms);
+  a.BsT = (float*)(w + d.off_bs);
+  a.AsT = (float*)(w + d.off_as);
   a.yadd = (float*)(w + d.off_yadd);
   a.A_final = A_final;
   a.B = s->B;
@@ -451,6 +482,8 @@ tc_status_t tc_forward_delta(const tc_shape_t* s, const void* q, const void* k, 
   a.nch = d.nch;
   a.G = d.G;
   a.ng = d.ng;
+  a.G2 = d.G2;
+  a.nsg = d.nsg;
   if (tck::launch_delta_memory(a, s->D, s->dtype == TC_BF16, (hipStream_t)stream) != hipSuccess) return TC_ERR_HIP;
   // y = y_local + sigma(g) m, rounded once (the window-only forward adds the read)
   return launch_fwd(*s, d.fp, q, k, v, lambda, eta, gate, y, nullptr, lse, ws, true, 0, a.yadd, (hipStream_t)stream,

@@ -386,6 +386,26 @@ struct AffineStep {
 
 constexpr int kDeltaWaves = 8;  // waves of the group, walk and expand kernels
 
+// One level of the scan over affine maps X <- M X + B, per head bh: n maps
+// (M row-major at M + (bh n + i) D^2, B^T likewise), taken in groups of gs.
+// The group kernel composes each group into Mo, BoT ([BH][ceil(n/gs)]); the
+// walk runs the n maps from zero, storing the state before each map and after
+// the last at AoT ([BH][n+1], transposed) and the last also at A_final; the
+// expand kernel starts group g from A0T[bh][g] (a0_stride states per head)
+// and stores the state before each of its maps at AoT[bh][i] (ao_stride).
+struct ScanLevel {
+  const float* M;
+  const float* BT;
+  int n, gs;
+  float* Mo;
+  float* BoT;
+  const float* A0T;
+  int a0_stride;
+  float* AoT;
+  int ao_stride;
+  float* A_final;
+};
+
 // Steps s = 0 .. n-1 of a walk whose step operands come three steps ahead:
 // fetch(o, s) loads step s into the operand set o, apply(o, s) runs step s
 // from it.  Three sets rotate (the loop is unrolled by three so that each is
@@ -408,25 +428,26 @@ __device__ __forceinline__ void walk3(Ops (&o)[3], int n, Fetch fetch, Apply app
   }
 }
 
-// Per group g of head bh: the composed map of its chunks, M_g (row-major)
-// and B_g^T.  grid = BH * ng, 512 threads.
+// Per group g of head bh: the composed map of its maps (row-major) and its
+// offset (transposed).  grid = BH * ceil(n / gs), 512 threads.
 template <int D>
-__global__ void __launch_bounds__(64 * kDeltaWaves) delta_group_kernel(DeltaArgs a) {
+__global__ void __launch_bounds__(64 * kDeltaWaves) delta_group_kernel(ScanLevel L) {
   constexpr int LDA = D + 4;
   __shared__ __attribute__((aligned(16))) float PT[D * LDA];  // product of the maps so far (transposed)
   __shared__ __attribute__((aligned(16))) float QT[D * LDA];  // offset so far (transposed)
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
-  const int bh = blockIdx.x / a.ng, g = blockIdx.x - bh * a.ng;
+  const int ngo = (L.n + L.gs - 1) / L.gs;
+  const int bh = blockIdx.x / ngo, g = blockIdx.x - bh * ngo;
   for (int x = tid; x < D * LDA; x += 64 * kDeltaWaves) {
     const int row = x / LDA, col = x - row * LDA;
     PT[x] = row == col ? 1.0f : 0.0f;
     QT[x] = 0.0f;
   }
   __syncthreads();
-  const int c0 = g * a.G, c1 = min(a.nch, c0 + a.G);
+  const int c0 = g * L.gs, c1 = min(L.n, c0 + L.gs);
   AffineStep<D, kDeltaWaves> st;  // (the two products one after the other: half the registers)
-  auto mc = [&](int c) { return a.Mc + ((size_t)bh * a.nch + c) * D * D; };
-  auto bc = [&](int c) { return a.BcT + ((size_t)bh * a.nch + c) * D * D; };
+  auto mc = [&](int c) { return L.M + ((size_t)bh * L.n + c) * D * D; };
+  auto bc = [&](int c) { return L.BT + ((size_t)bh * L.n + c) * D * D; };
   if constexpr (AffineStep<D, kDeltaWaves>::kFetch) {
     // (one set of operands, the next chunk's loaded during this one's second
     // product: here, unlike the walk, the registers of more sets would cost
@@ -454,8 +475,8 @@ __global__ void __launch_bounds__(64 * kDeltaWaves) delta_group_kernel(DeltaArgs
       __syncthreads();
     }
   }
-  float* Mg = a.Mg + ((size_t)bh * a.ng + g) * D * D;
-  float* Bg = a.BgT + ((size_t)bh * a.ng + g) * D * D;
+  float* Mg = L.Mo + ((size_t)bh * ngo + g) * D * D;
+  float* Bg = L.BoT + ((size_t)bh * ngo + g) * D * D;
   for (int x = tid; x < D * D; x += 64 * kDeltaWaves) {
     const int row = x / D, col = x - row * D;
     Mg[x] = PT[col * LDA + row];
@@ -463,47 +484,47 @@ __global__ void __launch_bounds__(64 * kDeltaWaves) delta_group_kernel(DeltaArgs
   }
 }
 
-// Per head: the walk over the groups, A^T at every group start, and the
-// final memory.  grid = BH, 512 threads.
+// Per head: the walk over the level's maps from zero, A^T before every map
+// (and after the last), and the final memory.  grid = BH, 512 threads.
 template <int D>
-__global__ void __launch_bounds__(64 * kDeltaWaves) delta_walk_kernel(DeltaArgs a) {
+__global__ void __launch_bounds__(64 * kDeltaWaves) delta_walk_kernel(ScanLevel L) {
   constexpr int LDA = D + 4;
   __shared__ __attribute__((aligned(16))) float AT[D * LDA];
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int bh = blockIdx.x;
-  float* Ag = a.AgT + (size_t)bh * (a.ng + 1) * D * D;
+  float* Ag = L.AoT + (size_t)bh * (L.n + 1) * D * D;
   for (int x = tid; x < D * LDA; x += 64 * kDeltaWaves) AT[x] = 0.0f;
   for (int x = tid; x < D * D; x += 64 * kDeltaWaves) Ag[x] = 0.0f;
   __syncthreads();
   AffineStep<D, kDeltaWaves> st;
-  auto mg = [&](int g) { return a.Mg + ((size_t)bh * a.ng + g) * D * D; };
-  auto bg = [&](int g) { return a.BgT + ((size_t)bh * a.ng + g) * D * D; };
+  auto mg = [&](int g) { return L.M + ((size_t)bh * L.n + g) * D * D; };
+  auto bg = [&](int g) { return L.BT + ((size_t)bh * L.n + g) * D * D; };
   if constexpr (AffineStep<D, kDeltaWaves>::kFetch) {
     // (each step's state goes to global memory one step late, after the next
     // step's products: see hold())
     using Ops = typename AffineStep<D, kDeltaWaves>::Operands;
     Ops ops[3];
     walk3(
-        ops, a.ng, [&](Ops& o, int g) { o.fetch(mg(g), bg(g), wid, l16, lg); },
+        ops, L.n, [&](Ops& o, int g) { o.fetch(mg(g), bg(g), wid, l16, lg); },
         [&](Ops& o, int g) {
           st.run_fetched(o, AT, LDA, true, wid, l16, lg);
           if (g > 0) st.store_held(Ag + (size_t)g * D * D, wid, l16, lg);
           __syncthreads();
           st.put(AT, LDA, nullptr, wid, l16, lg);
           st.hold();
-          if (g + 1 == a.ng) st.store_held(Ag + (size_t)a.ng * D * D, wid, l16, lg);
+          if (g + 1 == L.n) st.store_held(Ag + (size_t)L.n * D * D, wid, l16, lg);
           __syncthreads();
         });
   } else {
-    for (int g = 0; g < a.ng; ++g) {
+    for (int g = 0; g < L.n; ++g) {
       st.run(mg(g), AT, LDA, bg(g), wid, l16, lg);
       __syncthreads();
       st.put(AT, LDA, Ag + (size_t)(g + 1) * D * D, wid, l16, lg);
       __syncthreads();
     }
   }
-  if (a.A_final) {
-    float* Af = a.A_final + (size_t)bh * D * D;
+  if (L.A_final) {
+    float* Af = L.A_final + (size_t)bh * D * D;
     for (int x = tid; x < D * D; x += 64 * kDeltaWaves) {
       const int ar = x / D, col = x - ar * D;
       Af[x] = AT[col * LDA + ar];
@@ -511,17 +532,19 @@ __global__ void __launch_bounds__(64 * kDeltaWaves) delta_walk_kernel(DeltaArgs 
   }
 }
 
-// Per group: from its start state, the walk over its chunks, A^T at every
-// chunk start.  grid = BH * ng, 512 threads.
+// Per group: from its start state, the walk over its maps, A^T before each.
+// grid = BH * ceil(n / gs), 512 threads.
 template <int D>
-__global__ void __launch_bounds__(64 * kDeltaWaves) delta_expand_kernel(DeltaArgs a) {
+__global__ void __launch_bounds__(64 * kDeltaWaves) delta_expand_kernel(ScanLevel L) {
   constexpr int LDA = D + 4;
   __shared__ __attribute__((aligned(16))) float AT[D * LDA];
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
-  const int bh = blockIdx.x / a.ng, g = blockIdx.x - bh * a.ng;
-  const float* Ag = a.AgT + ((size_t)bh * (a.ng + 1) + g) * D * D;
-  const int c0 = g * a.G, c1 = min(a.nch, c0 + a.G);
-  float* Ac0 = a.AcT + ((size_t)bh * a.nch + c0) * D * D;
+  const int ngo = (L.n + L.gs - 1) / L.gs;
+  const int bh = blockIdx.x / ngo, g = blockIdx.x - bh * ngo;
+  const float* Ag = L.A0T + ((size_t)bh * L.a0_stride + g) * D * D;
+  const int c0 = g * L.gs, c1 = min(L.n, c0 + L.gs);
+  auto aout = [&](int c) { return L.AoT + ((size_t)bh * L.ao_stride + c) * D * D; };
+  float* Ac0 = aout(c0);
   {
     // the group's start state: every load in flight before the first store
     constexpr int NV = D * D / 4, PER = (NV + 64 * kDeltaWaves - 1) / (64 * kDeltaWaves);
@@ -543,8 +566,8 @@ __global__ void __launch_bounds__(64 * kDeltaWaves) delta_expand_kernel(DeltaArg
   }
   __syncthreads();
   AffineStep<D, kDeltaWaves> st;
-  auto mc = [&](int c) { return a.Mc + ((size_t)bh * a.nch + c) * D * D; };
-  auto bc = [&](int c) { return a.BcT + ((size_t)bh * a.nch + c) * D * D; };
+  auto mc = [&](int c) { return L.M + ((size_t)bh * L.n + c) * D * D; };
+  auto bc = [&](int c) { return L.BT + ((size_t)bh * L.n + c) * D * D; };
   if constexpr (AffineStep<D, kDeltaWaves>::kFetch) {
     // (one set of operands, as in the group kernel; each state goes to
     // global memory one step late, as in the walk)
@@ -552,19 +575,19 @@ __global__ void __launch_bounds__(64 * kDeltaWaves) delta_expand_kernel(DeltaArg
     if (c0 + 1 < c1) o.fetch(mc(c0), bc(c0), wid, l16, lg);
     for (int c = c0; c + 1 < c1; ++c) {
       st.run_fetched(o, AT, LDA, true, wid, l16, lg);
-      if (c > c0) st.store_held(a.AcT + ((size_t)bh * a.nch + c) * D * D, wid, l16, lg);
+      if (c > c0) st.store_held(aout(c), wid, l16, lg);
       __syncthreads();
       st.put(AT, LDA, nullptr, wid, l16, lg);
       st.hold();
       if (c + 2 < c1) o.fetch(mc(c + 1), bc(c + 1), wid, l16, lg);
       __syncthreads();
     }
-    if (c0 + 1 < c1) st.store_held(a.AcT + ((size_t)bh * a.nch + c1 - 1) * D * D, wid, l16, lg);
+    if (c0 + 1 < c1) st.store_held(aout(c1 - 1), wid, l16, lg);
   } else {
     for (int c = c0; c + 1 < c1; ++c) {
       st.run(mc(c), AT, LDA, bc(c), wid, l16, lg);
       __syncthreads();
-      st.put(AT, LDA, a.AcT + ((size_t)bh * a.nch + c + 1) * D * D, wid, l16, lg);
+      st.put(AT, LDA, aout(c + 1), wid, l16, lg);
       __syncthreads();
     }
   }
@@ -733,12 +756,24 @@ template <class E, int D>
 hipError_t launch_delta_impl(const DeltaArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
   const dim3 wide(64 * kDeltaWaves);
+  // levels: chunk maps -> groups of G (-> supergroups of G2 groups when nsg > 0)
+  const ScanLevel chunks{a.Mc, a.BcT, a.nch, a.G, a.Mg, a.BgT, a.AgT, a.ng + 1, a.AcT, a.nch, nullptr};
+  const ScanLevel groups{a.Mg, a.BgT, a.ng, a.G2, a.Ms, a.BsT, a.AsT, a.nsg + 1, a.AgT, a.ng + 1, nullptr};
   if (a.nch > 0) {
     hipLaunchKernelGGL((delta_chunk_kernel<E, D>), dim3(BH * a.nch), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((delta_group_kernel<D>), dim3(BH * a.ng), wide, 0, s, a);
+    hipLaunchKernelGGL((delta_group_kernel<D>), dim3(BH * a.ng), wide, 0, s, chunks);
+    if (a.nsg > 0) hipLaunchKernelGGL((delta_group_kernel<D>), dim3(BH * a.nsg), wide, 0, s, groups);
   }
-  hipLaunchKernelGGL((delta_walk_kernel<D>), dim3(BH), wide, 0, s, a);
-  if (a.nch > 0) hipLaunchKernelGGL((delta_expand_kernel<D>), dim3(BH * a.ng), wide, 0, s, a);
+  // the walk over the top level's maps (none when there are no evictions)
+  const ScanLevel top = a.nsg > 0 ? ScanLevel{a.Ms, a.BsT, a.nsg, 1, nullptr, nullptr, nullptr, 0, a.AsT, a.nsg + 1,
+                                              a.A_final}
+                                  : ScanLevel{a.Mg, a.BgT, a.ng, 1, nullptr, nullptr, nullptr, 0, a.AgT, a.ng + 1,
+                                              a.A_final};
+  hipLaunchKernelGGL((delta_walk_kernel<D>), dim3(BH), wide, 0, s, top);
+  if (a.nch > 0) {
+    if (a.nsg > 0) hipLaunchKernelGGL((delta_expand_kernel<D>), dim3(BH * a.nsg), wide, 0, s, groups);
+    hipLaunchKernelGGL((delta_expand_kernel<D>), dim3(BH * a.ng), wide, 0, s, chunks);
+  }
   hipLaunchKernelGGL((delta_read_kernel<E, D>), dim3(BH * (a.nch > 0 ? a.nch : 1)), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -167,6 +167,9 @@ struct DeltaArgs {
   float* BgT;      // [B*H][ng][D][D] its offset, transposed
   float* AgT;      // [B*H][ng+1][D][D] A^T at every group start (and after the last)
   float* AcT;      // [B*H][nch][D][D] A^T at every chunk start
+  float* Ms;       // [B*H][nsg][D][D] composed map of each supergroup of G2 groups (when nsg > 0)
+  float* BsT;      // [B*H][nsg][D][D] its offset, transposed
+  float* AsT;      // [B*H][nsg+1][D][D] A^T at every supergroup start (and after the last)
   float* yadd;     // [B*H][T][D] sigma(g) m_t
   float* A_final;  // [B*H][D][D] (nullable)
   int B, H, T, W;
@@ -174,6 +177,8 @@ struct DeltaArgs {
   int nch;  // chunks, ceil(E / 64)
   int G;    // chunks per group
   int ng;   // groups, ceil(nch / G)
+  int G2;   // groups per supergroup
+  int nsg;  // supergroups, ceil(ng / G2); 0: two levels (the walk runs over the groups)
 };
 hipError_t launch_delta_memory(const DeltaArgs& a, int D, bool is_bf16, hipStream_t s);
 

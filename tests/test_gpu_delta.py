@@ -52,9 +52,10 @@ CASES = [
     (2, 2, 300, 16, 64, "bf16"),   # D = 16
     (1, 2, 200, 64, 256, "bf16"),  # T < W: no write, the window alone
     (1, 1, 64 + 64, 64, 64, "bf16"),  # exactly one full chunk
-    (1, 2, 64 * 100 + 300, 64, 256, "bf16"),  # 101 chunks: groups of 7, the last of 3
+    (1, 2, 64 * 100 + 300, 64, 256, "bf16"),  # 101 chunks: 34 groups of 3 (the last of 2) in 12 supergroups of 3 (the last of 1)
     (1, 1, 64 * 40 + 100, 128, 128, "bf16"),  # D = 128, 40 chunks in groups of 4
-    (1, 1, 64 * 20 + 30, 32, 64, "f32"),      # float32, 20 chunks in groups of 3
+    (1, 1, 64 * 20 + 30, 32, 64, "f32"),      # float32, 20 chunks in groups of 2
+    (1, 1, 64 * 169 + 20 + 128, 64, 128, "f32"),  # float32, 170 chunks: 43 groups of 4 (the last of 2) in 11 supergroups of 4 (the last of 3)
 ]
 
 
