@@ -667,6 +667,12 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
     if (PUB) {
       State<E, D> acc;  // S(e0)
       state_zero(acc);
+      if (a.A_in) {
+        // a continuation's carried memory: S(0) = A_in / eta (m_lo = 0 then),
+        // decayed by the gather below with the earlier segments' states
+        state_load(acc, a.A_in + (size_t)bh * D * D, wid, l16, lg);
+        state_scale(acc, 1.0f / a.eta[h]);
+      }
       if (seg > m_lo) {
         // wait for the earlier segments' flags (bounded, so that every wave
         // ends; the workgroups waited for were dispatched earlier and wait for
@@ -681,6 +687,8 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
         state_gather_all(acc, pw[BM], slots, m_lo + 1, seg + 1, wid, lane);
         if (ran_out) state_fill(acc, __uint_as_float(0x7fc00000u));  // quiet NaN (bit pattern: no NaN literal here)
         timed_out = ran_out;
+      }
+      if (seg > m_lo || a.A_in) {
 #pragma unroll
         for (int o = 0; o < State<E, D>::NOWN; ++o)
           if (wid + 4 * o < NT)
@@ -839,6 +847,9 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdA
 // workgroup reads at most this many D x D states, L2-resident) instead of a
 // separate chain kernel.
 constexpr int kDirectPrefixMaxSeg = 16;
+// Segments up to which the workgroups exchange their local states through
+// flags (each gathers at most this many states after its window).
+constexpr int kPublishMaxSeg = 32;
 // Waves per workgroup of the bf16 kernel: 4 waves x 32 rows = 128-row blocks,
 // two workgroups per compute unit.  (Eight waves and 256-row blocks halve the
 // key/value tile traffic but run all eight waves in barrier lockstep at one
@@ -879,12 +890,12 @@ static hipError_t launch_rows_impl(const FwdArgs& a0, hipStream_t s) {
   // workgroups dispatched before it, so the waits end in any case.)
   // Not under graph capture: a replayed launch repeats this call's flag value,
   // so flags left by the previous replay would read as current.  Not for the
-  // chunk-mean shortcut, which always takes the state pass, nor for a scan
-  // that starts from a carried memory (A_in: the state pass adds it).
+  // chunk-mean shortcut, which always takes the state pass.  A scan that
+  // starts from a carried memory (A_in) seeds each gather with it.
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   const bool capturing = hipStreamIsCapturing(s, &capture) != hipSuccess || capture != hipStreamCaptureStatusNone;
-  a.publish = (MEANC == 0 && a.G == 1 && a.R == 0 && a.nseg > 1 && a.prefix_direct && a.flags != nullptr &&
-               !a.A_in && !a.window_only && !capturing && (long long)BH * a.nseg <= rows_resident_capacity<E, D, NW>())
+  a.publish = (MEANC == 0 && a.G == 1 && a.R == 0 && a.nseg > 1 && a.nseg <= kPublishMaxSeg && a.flags != nullptr &&
+               !a.window_only && !capturing && (long long)BH * a.nseg <= rows_resident_capacity<E, D, NW>())
                   ? 1
                   : 0;
   // otherwise the state pass also forms the last block's local state (final
