@@ -234,8 +234,9 @@ def continue_leg(steps, warmup, chunk=4096):
                 ms_per_sequence=ms, tokens_per_s=B * T / (ms * 1e-3), flops=fl,
                 roofline=dict(bound="mfma", achieved=tflops, peak=PEAK_BF16, unit="TFLOP/s", frac=tflops / PEAK_BF16,
                               traffic=measured_traffic().get("continue"),
-                              kernel="%d tc_forward_continue calls (gather + initial-state read + forward over "
-                                     "ring prefix and chunk + state/ring update)" % n))
+                              kernel="%d tc_forward_continue calls (each: the forward over the ring prefix and "
+                                     "the chunk, its segments exchanging states seeded from the carried memory, "
+                                     "then the ring and memory update)" % n))
 
 
 def chunk_mean_leg(steps, warmup, exact_ms):
