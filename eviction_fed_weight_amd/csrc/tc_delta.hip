@@ -112,17 +112,18 @@ struct RawFrag4<float> {
 // Per chunk c of head bh: U'^T and Wm^T ([D][64]), M_c (row-major) and
 // B_c^T.  grid = BH * nch, 256 threads.
 template <class E, int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) delta_chunk_kernel(DeltaArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) delta_chunk_kernel(DeltaArgs a) {
   using M = Mfma<float>;
-  constexpr int C = kDeltaC, LDX = 2 * D + 4, LDN = C + 4, LDT = C + 4, NT = D / 16;
-  constexpr int XN = C * LDX + C * LDN, XT_ = 2 * D * LDT;
+  constexpr int C = kDeltaC, LDN = C + 4, LDT = C + 4, NT = D / 16;
+  constexpr int XN = D * LDT + C * LDN, XT_ = 2 * D * LDT;
+  // (about 52 KB at D = 64: three workgroups per compute unit)
   __shared__ __attribute__((aligned(16))) float KT[D * LDT];         // keys, rows d
   __shared__ __attribute__((aligned(16))) float big[XN > XT_ ? XN : XT_];
   __shared__ float pw[C + 1];  // lambda^n
   __shared__ float wv[C];      // eta lambda^(n-1-i), zero for i >= n
-  float* const X = big;             // [V | lambda^i K] (rows i), solved in place into registers
-  float* const Nt = big + C * LDX;  // N^T: N_ij at j * LDN + i, zero for j >= i
-  float* const XT = big;            // after the solve: [U'^T ; Wm^T] (rows = columns of X)
+  float* const VT = big;            // values, rows d (the right-hand sides V; the others are lambda^i K, from KT)
+  float* const Nt = big + D * LDT;  // N^T: N_ij at j * LDN + i, zero for j >= i
+  float* const XT = big;            // after the solve: [U'^T ; Wm^T] (rows = columns of the solution)
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int bh = blockIdx.x / a.nch, c = blockIdx.x - bh * a.nch, h = bh % a.H;
   const int e0 = C * c, n = min(C, a.E - e0);
@@ -153,10 +154,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
         const E* ve = (const E*)&vr[p];
 #pragma unroll
         for (int jj = 0; jj < VE; ++jj) {
-          const float kv = (float)ke[jj];
-          KT[(d + jj) * LDT + i] = kv;
-          X[i * LDX + d + jj] = (float)ve[jj];
-          X[i * LDX + D + d + jj] = pw[i] * kv;
+          KT[(d + jj) * LDT + i] = (float)ke[jj];
+          VT[(d + jj) * LDT + i] = (float)ve[jj];
         }
       }
     }
@@ -211,24 +210,31 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
   float x[C];
   const bool solver = tid < 2 * D;
   if (solver) {
+    // column tid of [V | lambda^i K]
+    const bool isv = tid < D;
+    const float* col0 = isv ? VT + tid * LDT : KT + (tid - D) * LDT;
 #pragma unroll
-    for (int i = 0; i < C; ++i) x[i] = X[i * LDX + tid];
-    // (column j + 1 is loaded while column j is applied)
-    f32x4 col[2][C / 4];
+    for (int i4 = 0; i4 < C; i4 += 4) {
+      const f32x4 c4 = *(const f32x4*)(col0 + i4);
 #pragma unroll
-    for (int i4 = 0; i4 < C; i4 += 4) col[0][i4 / 4] = *(const f32x4*)(Nt + i4);
+      for (int ii = 0; ii < 4; ++ii) x[i4 + ii] = isv ? c4[ii] : pw[i4 + ii] * c4[ii];
+    }
+    // (each 4-row slot of column j + 1 is loaded into the registers of the
+    // same slot of column j as soon as that slot has been applied: one
+    // column's registers instead of two, so that three workgroups fit a
+    // compute unit, whose other waves cover the shorter lead)
+    f32x4 col[C / 4];
+#pragma unroll
+    for (int i4 = 0; i4 < C; i4 += 4) col[i4 / 4] = *(const f32x4*)(Nt + i4);
 #pragma unroll
     for (int j = 0; j < C - 1; ++j) {
-      const int b = j & 1;
-      if (j + 2 < C) {
 #pragma unroll
-        for (int i4 = (j + 2) & ~3; i4 < C; i4 += 4) col[b ^ 1][i4 / 4] = *(const f32x4*)(Nt + (j + 1) * LDN + i4);
-      }
-#pragma unroll
-      for (int i4 = (j + 1) & ~3; i4 < C; i4 += 4)
+      for (int i4 = (j + 1) & ~3; i4 < C; i4 += 4) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-          if (i4 + ii > j) x[i4 + ii] -= col[b][i4 / 4][ii] * x[j];
+          if (i4 + ii > j) x[i4 + ii] -= col[i4 / 4][ii] * x[j];
+        if (j + 2 < C && i4 + 3 > j + 1) col[i4 / 4] = *(const f32x4*)(Nt + (j + 1) * LDN + i4);
+      }
     }
   }
   __syncthreads();  // X and N are read; XT reuses their space
