@@ -444,23 +444,29 @@ __global__ void __launch_bounds__(64 * kDeltaWaves) delta_group_kernel(ScanLevel
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int ngo = (L.n + L.gs - 1) / L.gs;
   const int bh = blockIdx.x / ngo, g = blockIdx.x - bh * ngo;
-  for (int x = tid; x < D * LDA; x += 64 * kDeltaWaves) {
-    const int row = x / LDA, col = x - row * LDA;
-    PT[x] = row == col ? 1.0f : 0.0f;
-    QT[x] = 0.0f;
-  }
-  __syncthreads();
-  const int c0 = g * L.gs, c1 = min(L.n, c0 + L.gs);
-  AffineStep<D, kDeltaWaves> st;  // (the two products one after the other: half the registers)
+  const int c0 = g * L.gs, c1 = min(L.n, c0 + L.gs);  // (c0 < c1: no group is empty)
   auto mc = [&](int c) { return L.M + ((size_t)bh * L.n + c) * D * D; };
   auto bc = [&](int c) { return L.BT + ((size_t)bh * L.n + c) * D * D; };
+  {
+    // the group's first map as it is (its product with the identity and the
+    // zero offset would give the same values exactly)
+    const float* m0 = mc(c0);
+    const float* b0 = bc(c0);
+    for (int x = tid; x < D * D; x += 64 * kDeltaWaves) {
+      const int row = x / D, col = x - row * D;
+      PT[col * LDA + row] = m0[x];
+      QT[row * LDA + col] = b0[x];
+    }
+  }
+  __syncthreads();
+  AffineStep<D, kDeltaWaves> st;  // (the two products one after the other: half the registers)
   if constexpr (AffineStep<D, kDeltaWaves>::kFetch) {
     // (one set of operands, the next chunk's loaded during this one's second
     // product: here, unlike the walk, the registers of more sets would cost
     // resident workgroups)
     typename AffineStep<D, kDeltaWaves>::Operands o;
-    if (c0 < c1) o.fetch(mc(c0), bc(c0), wid, l16, lg);
-    for (int c = c0; c < c1; ++c) {
+    if (c0 + 1 < c1) o.fetch(mc(c0 + 1), bc(c0 + 1), wid, l16, lg);
+    for (int c = c0 + 1; c < c1; ++c) {
       st.run_fetched(o, PT, LDA, false, wid, l16, lg);
       __syncthreads();
       st.put(PT, LDA, nullptr, wid, l16, lg);
@@ -471,7 +477,7 @@ __global__ void __launch_bounds__(64 * kDeltaWaves) delta_group_kernel(ScanLevel
       __syncthreads();
     }
   } else {
-    for (int c = c0; c < c1; ++c) {
+    for (int c = c0 + 1; c < c1; ++c) {
       st.run(mc(c), PT, LDA, nullptr, wid, l16, lg);
       __syncthreads();
       st.put(PT, LDA, nullptr, wid, l16, lg);
@@ -499,22 +505,29 @@ __global__ void __launch_bounds__(64 * kDeltaWaves) delta_walk_kernel(ScanLevel 
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int bh = blockIdx.x;
   float* Ag = L.AoT + (size_t)bh * (L.n + 1) * D * D;
-  for (int x = tid; x < D * LDA; x += 64 * kDeltaWaves) AT[x] = 0.0f;
-  for (int x = tid; x < D * D; x += 64 * kDeltaWaves) Ag[x] = 0.0f;
-  __syncthreads();
-  AffineStep<D, kDeltaWaves> st;
   auto mg = [&](int g) { return L.M + ((size_t)bh * L.n + g) * D * D; };
   auto bg = [&](int g) { return L.BT + ((size_t)bh * L.n + g) * D * D; };
+  // A_0 = 0 and A_1 = M_0 A_0 + B_0 = B_0: the first map applied as it is
+  for (int x = tid; x < D * D; x += 64 * kDeltaWaves) {
+    const int q = x / D, p = x - q * D;  // (B_0^T row-major: B_0[p][q] at q D + p)
+    const float b = L.n > 0 ? bg(0)[x] : 0.0f;
+    AT[q * LDA + p] = b;
+    Ag[x] = 0.0f;
+    if (L.n > 0) Ag[(size_t)D * D + x] = b;
+  }
+  __syncthreads();
+  AffineStep<D, kDeltaWaves> st;
   if constexpr (AffineStep<D, kDeltaWaves>::kFetch) {
     // (each step's state goes to global memory one step late, after the next
-    // step's products: see hold())
+    // step's products: see hold(); step s applies map s + 1)
     using Ops = typename AffineStep<D, kDeltaWaves>::Operands;
     Ops ops[3];
     walk3(
-        ops, L.n, [&](Ops& o, int g) { o.fetch(mg(g), bg(g), wid, l16, lg); },
-        [&](Ops& o, int g) {
+        ops, L.n > 0 ? L.n - 1 : 0, [&](Ops& o, int s) { o.fetch(mg(s + 1), bg(s + 1), wid, l16, lg); },
+        [&](Ops& o, int s) {
+          const int g = s + 1;
           st.run_fetched(o, AT, LDA, true, wid, l16, lg);
-          if (g > 0) st.store_held(Ag + (size_t)g * D * D, wid, l16, lg);
+          if (s > 0) st.store_held(Ag + (size_t)g * D * D, wid, l16, lg);
           __syncthreads();
           st.put(AT, LDA, nullptr, wid, l16, lg);
           st.hold();
@@ -522,7 +535,7 @@ __global__ void __launch_bounds__(64 * kDeltaWaves) delta_walk_kernel(ScanLevel 
           __syncthreads();
         });
   } else {
-    for (int g = 0; g < L.n; ++g) {
+    for (int g = 1; g < L.n; ++g) {
       st.run(mg(g), AT, LDA, bg(g), wid, l16, lg);
       __syncthreads();
       st.put(AT, LDA, Ag + (size_t)(g + 1) * D * D, wid, l16, lg);
