@@ -380,8 +380,9 @@ tc_status_t tc_forward_noalloc(const tc_shape_t* s, const void* q, const void* k
 
 // Delta-rule workspace: the window-only forward's, then (float32) per chunk
 // U'^T and Wm^T [D][64], M_c and B_c^T [D][D]; per group M_g and B_g^T; the
-// group-start and chunk-start states; the memory read [BH][T][D]; with three
-// levels also per supergroup its map, offset and start state.
+// group-start states and (D = 128) the chunk-start states; the memory read
+// [BH][T][D]; with three levels also per supergroup its map, offset and start
+// state.
 //
 // Level sizes.  A scan level of n maps in groups of g costs g steps in its
 // group kernel (two products a step) and g in its expand kernel (one), each
@@ -429,7 +430,8 @@ DeltaPlan delta_plan_for(const tc_shape_t& s) {
   d.off_bg = d.off_mg + align256(BH * d.ng * DD);
   d.off_ag = d.off_bg + align256(BH * d.ng * DD);
   d.off_ac = d.off_ag + align256(BH * (d.ng + 1) * DD);
-  d.off_ms = d.off_ac + align256(BH * d.nch * DD);
+  // (D <= 64: the last expansion and the read run fused, A_c is never stored)
+  d.off_ms = d.off_ac + (s.D <= 64 ? 0 : align256(BH * d.nch * DD));
   d.off_bs = d.off_ms + align256(BH * d.nsg * DD);
   d.off_as = d.off_bs + align256(BH * d.nsg * DD);
   d.off_yadd = d.off_as + (d.nsg > 0 ? align256(BH * (d.nsg + 1) * DD) : 0);

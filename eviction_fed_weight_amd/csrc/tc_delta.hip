@@ -620,8 +620,10 @@ __global__ void __launch_bounds__(64 * kDeltaWaves) delta_expand_kernel(ScanLeve
 // The contraction slots of a fragment pair up two 16-wide tiles of the
 // product before (index 32 kc + 4 lg + ii, then 32 kc + 16 + 4 lg + ii), and
 // the other operand is read in the same order.
+// The read of chunk c of head bh by four waves (256 threads): A_c^T at AcT,
+// row stride lda (global memory, or the expanding kernel's LDS copy).
 template <class E, int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) delta_read_kernel(DeltaArgs a) {
+__device__ __forceinline__ void delta_read_chunk(const DeltaArgs& a, int bh, int c, const float* AcT, int lda) {
   using M = Mfma<float>;
   constexpr int C = kDeltaC, NT = D / 16, NKC = (D + 31) / 32;
   // The operands arrive in three rounds of loads, each issued as a whole
@@ -632,20 +634,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))
   constexpr bool EARLY = D <= 64;
   constexpr int CTB = NT >= 2 ? 2 : 1;  // column tiles per round of A_c / U' loads
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
-  const int nb = a.nch > 0 ? a.nch : 1;
-  const int bh = blockIdx.x / nb, c = blockIdx.x - bh * nb, h = bh % a.H;
+  (void)tid;
+  const int h = bh % a.H;
   float* yb = a.yadd + (size_t)bh * a.T * D;
-  if (c == 0) {
-    const int nz = min(a.W, a.T) * D;
-    for (int x = tid; x < nz; x += 256) yb[x] = 0.0f;
-  }
-  if (c >= a.nch) return;
   const float lam = a.lam[h], eta = a.eta[h], sg = sigmoidf(a.gate[h]);
   const int e0 = C * c, n = min(C, a.E - e0);
   const int r = 16 * wid + l16;  // this lane's row of the chunk (query t = W + e0 + r)
   const E* qg = (const E*)a.q + ((size_t)bh * a.T + a.W + e0) * D;
   const E* kg = (const E*)a.k + ((size_t)bh * a.T + e0) * D;
-  const float* AcT = a.AcT + ((size_t)bh * a.nch + c) * D * D;
   const float* UpT = a.UpT + ((size_t)bh * a.nch + c) * D * C;
   const float* WmT = a.WmT + ((size_t)bh * a.nch + c) * D * C;
 
@@ -731,7 +727,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))
       const int col = 16 * (cb + u) + l16;
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
-        const float* ar = AcT + (size_t)col * D + 32 * kc + 4 * lg;
+        const float* ar = AcT + (size_t)col * lda + 32 * kc + 4 * lg;
         av[u][kc][0] = *(const f32x4*)ar;
         // (D = 16: one tile of Qt, the other half of the slots empty)
         av[u][kc][1] = 32 * kc + 16 < D ? *(const f32x4*)(ar + 16) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -770,6 +766,58 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))
   }
 }
 
+template <class E, int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))) delta_read_kernel(DeltaArgs a) {
+  const int nb = a.nch > 0 ? a.nch : 1;
+  const int bh = blockIdx.x / nb, c = blockIdx.x - bh * nb;
+  if (c == 0) {
+    float* yb = a.yadd + (size_t)bh * a.T * D;
+    const int nz = min(a.W, a.T) * D;
+    for (int x = threadIdx.x; x < nz; x += 256) yb[x] = 0.0f;
+  }
+  if (c >= a.nch) return;
+  delta_read_chunk<E, D>(a, bh, c, a.AcT + ((size_t)bh * a.nch + c) * D * D, D);
+}
+
+// The last expansion fused with the read (D <= 64): per group of chunks,
+// from the group's start state, the read of each chunk from A_c in LDS and
+// the step to A_{c+1}; A_c never goes to global memory.  The four waves run
+// the read of chunk c, then the step (both read A_c^T; a barrier before the
+// new state replaces it).  grid = BH * ceil(nch / gs), 256 threads.
+template <class E, int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3)))
+    delta_expand_read_kernel(DeltaArgs a, ScanLevel L) {
+  constexpr int LDA = D + 4;
+  __shared__ __attribute__((aligned(16))) float AT[D * LDA];
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  const int ngo = (L.n + L.gs - 1) / L.gs;
+  const int bh = blockIdx.x / ngo, g = blockIdx.x - bh * ngo;
+  const int c0 = g * L.gs, c1 = min(L.n, c0 + L.gs);
+  if (g == 0) {  // rows t < W read no memory
+    float* yb = a.yadd + (size_t)bh * a.T * D;
+    const int nz = min(a.W, a.T) * D;
+    for (int x = tid; x < nz; x += 256) yb[x] = 0.0f;
+  }
+  {
+    const float* A0 = L.A0T + ((size_t)bh * L.a0_stride + g) * D * D;
+    for (int x4 = 4 * tid; x4 < D * D; x4 += 4 * 256) {
+      const int q = x4 / D, p = x4 - q * D;
+      *(f32x4*)(AT + q * LDA + p) = *(const f32x4*)(A0 + x4);
+    }
+  }
+  __syncthreads();
+  AffineStep<D, 4> st;
+  for (int c = c0; c < c1; ++c) {
+    delta_read_chunk<E, D>(a, bh, c, AT, LDA);
+    if (c + 1 < c1) {
+      st.run(L.M + ((size_t)bh * L.n + c) * D * D, AT, LDA, L.BT + ((size_t)bh * L.n + c) * D * D, wid, l16, lg);
+      __syncthreads();
+      st.put(AT, LDA, nullptr, wid, l16, lg);
+      __syncthreads();
+    }
+  }
+}
+
 namespace {
 template <class E, int D>
 hipError_t launch_delta_impl(const DeltaArgs& a, hipStream_t s) {
@@ -791,6 +839,11 @@ hipError_t launch_delta_impl(const DeltaArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((delta_walk_kernel<D>), dim3(BH), wide, 0, s, top);
   if (a.nch > 0) {
     if (a.nsg > 0) hipLaunchKernelGGL((delta_expand_kernel<D>), dim3(BH * a.nsg), wide, 0, s, groups);
+    if constexpr (D <= 64) {
+      // the expansion over the chunks and the read in one kernel (no A_c in global memory)
+      hipLaunchKernelGGL((delta_expand_read_kernel<E, D>), dim3(BH * a.ng), dim3(256), 0, s, a, chunks);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL((delta_expand_kernel<D>), dim3(BH * a.ng), wide, 0, s, chunks);
   }
   hipLaunchKernelGGL((delta_read_kernel<E, D>), dim3(BH * (a.nch > 0 ? a.nch : 1)), dim3(256), 0, s, a);

@@ -166,7 +166,7 @@ struct DeltaArgs {
   float* Mg;       // [B*H][ng][D][D] composed map of each group of G chunks (row-major)
   float* BgT;      // [B*H][ng][D][D] its offset, transposed
   float* AgT;      // [B*H][ng+1][D][D] A^T at every group start (and after the last)
-  float* AcT;      // [B*H][nch][D][D] A^T at every chunk start
+  float* AcT;      // [B*H][nch][D][D] A^T at every chunk start (D = 128 only: with D <= 64 the read is fused)
   float* Ms;       // [B*H][nsg][D][D] composed map of each supergroup of G2 groups (when nsg > 0)
   float* BsT;      // [B*H][nsg][D][D] its offset, transposed
   float* AsT;      // [B*H][nsg+1][D][D] A^T at every supergroup start (and after the last)
