@@ -317,7 +317,8 @@ def delta_leg(steps, warmup, exact_ms):
             rel_gap_y_vs_exact=float((y.float() - ye.float()).norm() / ye.float().norm()),
             rel_gap_A_final_vs_exact=float((A - Ae).norm() / Ae.norm()),
             kernel="one tc_forward_delta call (delta_chunk_kernel [per chunk of 64 evictions] + delta_group_kernel "
-                   "+ delta_walk_kernel [one workgroup per head] + delta_expand_kernel + delta_read_kernel + the "
+                   "[per level] + delta_walk_kernel [one workgroup per head] + delta_expand_kernel [upper levels] + "
+                   "delta_expand_read_kernel [per group of chunks: the last expansion and the read] + the "
                    "window-only forward)"))
     return out
 
