@@ -293,21 +293,22 @@ template <int D, int NWV>
 struct AffineStep {
   static constexpr int NT = D / 16, NKC = (D + 31) / 32, TPW = (NT * NT + NWV - 1) / NWV;
   f32x4 out[TPW];
+  // (ldm, ldb: row strides of M and B^T, D in global memory)
   __device__ __forceinline__ void run(const float* Mrow, const float* XT, int lda, const float* BT, int wid, int l16,
-                                      int lg) {
+                                      int lg, int ldm = D, int ldb = D) {
     using M = Mfma<float>;
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
       const int t = wid + NWV * m;
       if (t < NT * NT) {
         const int pt = t / NT, qt = t - pt * NT;
-        f32x4 acc = BT ? *(const f32x4*)(BT + (size_t)(16 * qt + l16) * D + 16 * pt + 4 * lg)
+        f32x4 acc = BT ? *(const f32x4*)(BT + (size_t)(16 * qt + l16) * ldb + 16 * pt + 4 * lg)
                        : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
           const int d0 = 32 * kc + 8 * lg;
           if (d0 < D)
-            acc = M::mma(ld8f(Mrow + (size_t)(16 * pt + l16) * D + d0), ld8f(XT + (16 * qt + l16) * lda + d0), acc);
+            acc = M::mma(ld8f(Mrow + (size_t)(16 * pt + l16) * ldm + d0), ld8f(XT + (16 * qt + l16) * lda + d0), acc);
         }
         out[m] = acc;
       }
@@ -783,12 +784,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))
 // from the group's start state, the read of each chunk from A_c in LDS and
 // the step to A_{c+1}; A_c never goes to global memory.  The four waves run
 // the read of chunk c, then the step (both read A_c^T; a barrier before the
-// new state replaces it).  grid = BH * ceil(nch / gs), 256 threads.
+// new state replaces it).  The step's M_c and B_c^T are loaded before the
+// read, which covers their latency, and parked in LDS after it.
+// grid = BH * ceil(nch / gs), 256 threads.
 template <class E, int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 3)))
     delta_expand_read_kernel(DeltaArgs a, ScanLevel L) {
   constexpr int LDA = D + 4;
   __shared__ __attribute__((aligned(16))) float AT[D * LDA];
+  __shared__ __attribute__((aligned(16))) float MS[D * LDA];  // M_c, row stride LDA
+  __shared__ __attribute__((aligned(16))) float BS[D * LDA];  // B_c^T, row stride LDA
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int ngo = (L.n + L.gs - 1) / L.gs;
   const int bh = blockIdx.x / ngo, g = blockIdx.x - bh * ngo;
@@ -807,10 +812,32 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 3))
   }
   __syncthreads();
   AffineStep<D, 4> st;
+  constexpr int NV4 = D * D / 4, PER = (NV4 + 255) / 256;  // float4 vectors of one matrix; per thread
   for (int c = c0; c < c1; ++c) {
+    const bool step = c + 1 < c1;
+    f32x4 mreg[PER], breg[PER];
+    if (step) {
+      const f32x4* Mc = (const f32x4*)(L.M + ((size_t)bh * L.n + c) * D * D);
+      const f32x4* Bc = (const f32x4*)(L.BT + ((size_t)bh * L.n + c) * D * D);
+#pragma unroll
+      for (int v = 0; v < PER; ++v) {
+        const int x = tid + 256 * v;
+        mreg[v] = (NV4 % 256 == 0 || x < NV4) ? Mc[x] : f32x4{0.f, 0.f, 0.f, 0.f};
+        breg[v] = (NV4 % 256 == 0 || x < NV4) ? Bc[x] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
     delta_read_chunk<E, D>(a, bh, c, AT, LDA);
-    if (c + 1 < c1) {
-      st.run(L.M + ((size_t)bh * L.n + c) * D * D, AT, LDA, L.BT + ((size_t)bh * L.n + c) * D * D, wid, l16, lg);
+    if (step) {
+#pragma unroll
+      for (int v = 0; v < PER; ++v) {
+        const int x = tid + 256 * v, row = 4 * x / D, col = 4 * x - row * D;
+        if (NV4 % 256 == 0 || x < NV4) {
+          *(f32x4*)(MS + row * LDA + col) = mreg[v];
+          *(f32x4*)(BS + row * LDA + col) = breg[v];
+        }
+      }
+      __syncthreads();
+      st.run(MS, AT, LDA, BS, wid, l16, lg, LDA, LDA);
       __syncthreads();
       st.put(AT, LDA, nullptr, wid, l16, lg);
       __syncthreads();
