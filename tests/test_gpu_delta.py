@@ -56,6 +56,9 @@ CASES = [
     (1, 1, 64 * 40 + 100, 128, 128, "bf16"),  # D = 128, 40 chunks in groups of 4
     (1, 1, 64 * 20 + 30, 32, 64, "f32"),      # float32, 20 chunks in groups of 2
     (1, 1, 64 * 169 + 20 + 128, 64, 128, "f32"),  # float32, 170 chunks: 43 groups of 4 (the last of 2) in 11 supergroups of 4 (the last of 3)
+    (1, 1, 64 * 256 + 10 + 128, 64, 128, "f32"),  # float32, 257 chunks: 65 groups of 4 (the last of 1) in 13 supergroups of 5
+    (1, 2, 64 * 96 + 1 + 64, 32, 64, "bf16"),     # D = 32, 97 chunks: 33 groups of 3 (the last of 1) in 11 supergroups of 3
+    (1, 3, 64 * 149 + 33 + 100, 16, 100, "f32"),  # D = 16, 150 chunks: 50 groups of 3 in 13 supergroups of 4 (the last of 2)
 ]
 
 
