@@ -303,12 +303,13 @@ struct TileRegs {
 };
 
 
-// Tile load from a sequence: RING = false for a sequence that starts at
-// token 0 (no prefix: the plain single-resource load, nothing else in the
-// kernel's code), RING = true for a continuation that re-reads the ring.
-template <bool RING, class TR>
+// Tile load from a sequence: RING = 0 for a sequence that starts at token 0
+// (no prefix: the plain single-resource load, nothing else in the kernel's
+// code), RING = 1 or 2 for a continuation that re-reads the ring (2: the
+// prefix length p is a multiple of the tile rows).
+template <int RING, class TR>
 __device__ __forceinline__ void load_seq(TR& t, const SeqRows& s, int r0) {
-  if constexpr (RING)
+  if constexpr (RING != 0)
     t.load(s, r0);
   else
     t.load(s.cur, r0);
@@ -351,10 +352,62 @@ struct SeqTileRegs {
   }
 };
 
-// Staging registers of a key/value tile: plain for a sequence from token 0,
-// SeqTileRegs for a continuation that re-reads the ring.
-template <bool RING, class E, int D, int NR, int NTH = 256>
-using KVRegs = typename std::conditional<RING, SeqTileRegs<E, D, NR, NTH>, TileRegs<E, D, NR, NTH>>::type;
+// TileRegs for rows of a continued sequence whose prefix length p is a
+// multiple of NR and tiles that start at multiples of NR: a tile then lies
+// wholly in the ring or wholly in the current tokens, so one load per vector
+// from a resource chosen once per tile (the same for every lane) serves it.
+// Ring rows wrap at most once within a tile (slot (s0 + r) mod W).
+template <class E, int D, int NR, int NTH = 256>
+struct AlignedSeqTileRegs {
+  using Base = TileRegs<E, D, NR, NTH>;
+  static constexpr int VE = Base::VE, VPR = Base::VPR, NV = Base::NV, PER = Base::PER;
+  uint4 v[PER];
+  __device__ __forceinline__ void load(const SeqRows& s, int r0) {
+    // (r0 is the same in every lane: the branch is uniform and each side
+    // loads through a scalar resource)
+    if (__builtin_amdgcn_readfirstlane(r0) >= s.p) {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int x = (int)threadIdx.x + NTH * p;
+        const int row = x / VPR;
+        const int col = (x - row * VPR) * VE;
+        int off = ((r0 + row - s.p) * D + col) * (int)sizeof(E);
+        if (NV % NTH != 0 && x >= NV) off = -16;  // out of range: reads zero
+        v[p] = buf_load16(s.cur, off);
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int x = (int)threadIdx.x + NTH * p;
+        const int row = x / VPR;
+        const int col = (x - row * VPR) * VE;
+        const int rr = r0 + row;
+        int slot = s.s0 + rr;  // (s0 < W and rr < p <= W)
+        if (slot >= s.W) slot -= s.W;
+        int off = (slot * D + col) * (int)sizeof(E);
+        if ((NV % NTH != 0 && x >= NV) || rr < 0) off = -16;  // out of range: reads zero
+        v[p] = buf_load16(s.ring, off);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(E* lds, int ld) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int x = (int)threadIdx.x + NTH * p;
+      const int row = x / VPR;
+      const int col = (x - row * VPR) * VE;
+      if (NV % NTH == 0 || x < NV) *(uint4*)(lds + row * ld + col) = v[p];
+    }
+  }
+};
+
+// Staging registers of a key/value tile: plain for a sequence from token 0
+// (RING = 0), SeqTileRegs for a continuation that re-reads the ring (1), and
+// AlignedSeqTileRegs when its prefix is a multiple of the tile rows (2).
+template <int RING, class E, int D, int NR, int NTH = 256>
+using KVRegs = typename std::conditional<
+    RING == 0, TileRegs<E, D, NR, NTH>,
+    typename std::conditional<RING == 1, SeqTileRegs<E, D, NR, NTH>, AlignedSeqTileRegs<E, D, NR, NTH>>::type>::type;
 
 // Workgroup b of a grid of n runs on XCD b % 8 (the eight chiplets take
 // workgroups in turn, each with its own L2).  Renumber so that each XCD gets

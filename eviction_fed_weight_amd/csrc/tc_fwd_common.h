@@ -395,7 +395,7 @@ __device__ __forceinline__ void store4(float* dst, f32x4 x) { *(f32x4*)dst = x; 
 //
 // RING: a continuation (row0 > 0) whose first row0 keys and values are read
 // from the ring.
-template <class E, int D, int BM, int MEANC = 0, bool RING = false>
+template <class E, int D, int BM, int MEANC = 0, int RING = 0>
 __global__ void __launch_bounds__(256, 2) seg_state_kernel(FwdArgs a) {
   constexpr int LDK = D + 16 / (int)sizeof(E);
   constexpr int TILE = 64 * LDK * (int)sizeof(E);

@@ -163,8 +163,9 @@ __device__ __forceinline__ void own_state_update(OwnS<D, NW>& so, const E* Ks, i
 // carry is BM / MEANC such writes.  No intra-chunk triangle.
 //
 // RING: a continuation (row0 > 0) whose first row0 keys and values are read
-// from the ring.
-template <class E, int D, int NW, bool PUB, int MEANC = 0, bool RING = false>
+// from the ring (1; 2 when row0 and W are multiples of 64, so that every tile
+// lies wholly in the ring or wholly in the new tokens: one load per vector).
+template <class E, int D, int NW, bool PUB, int MEANC = 0, int RING = 0>
 __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd_kernel_rows(FwdArgs a) {
   using M = Mfma<E>;
   using frag = typename M::frag;
@@ -906,9 +907,13 @@ static hipError_t launch_rows_impl(const FwdArgs& a0, hipStream_t s) {
   const char* polls = getenv("TC_FORWARD_MAX_POLLS");
   a.max_polls = polls ? atoi(polls) : kPublishPolls;
   const bool ring = a.row0 > 0;
+  const bool aligned = a.row0 % 64 == 0 && a.W % 64 == 0;  // (tiles never straddle the ring's end)
   if (a.nseg > 1 && !a.publish && !a.window_only) {
-    if (ring)
-      hipLaunchKernelGGL((seg_state_kernel<E, D, BM, MEANC, true>), dim3(BH * (a.nseg - 1 + a.final_slot)),
+    if (ring && aligned)
+      hipLaunchKernelGGL((seg_state_kernel<E, D, BM, MEANC, 2>), dim3(BH * (a.nseg - 1 + a.final_slot)),
+                         dim3(256), 0, s, a);
+    else if (ring)
+      hipLaunchKernelGGL((seg_state_kernel<E, D, BM, MEANC, 1>), dim3(BH * (a.nseg - 1 + a.final_slot)),
                          dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((seg_state_kernel<E, D, BM, MEANC>), dim3(BH * (a.nseg - 1 + a.final_slot)), dim3(256), 0,
@@ -919,10 +924,14 @@ static hipError_t launch_rows_impl(const FwdArgs& a0, hipStream_t s) {
   }
   const dim3 grid(BH * a.nseg), block(64 * NW);
   if (MEANC == 0 && ring) {  // (continuations run the exact scan)
-    if (a.publish)
-      hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, true, 0, true>), grid, block, 0, s, a);
+    if (a.publish && aligned)
+      hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, true, 0, 2>), grid, block, 0, s, a);
+    else if (a.publish)
+      hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, true, 0, 1>), grid, block, 0, s, a);
+    else if (aligned)
+      hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, false, 0, 2>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, false, 0, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, false, 0, 1>), grid, block, 0, s, a);
   } else if (a.publish) {
     hipLaunchKernelGGL((fwd_kernel_rows<E, D, NW, true>), grid, block, 0, s, a);
   } else {
